@@ -1,0 +1,354 @@
+/*
+ * qmm_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU reference for the quantized-weight
+ * matmul with inline block dequantization.  Only the tests, the smoke check
+ * and the benchmark's CPU-baseline leg may load this library; the product
+ * path (the HIP library) never links, loads or calls it, and it shares no
+ * code, header or table with that path.
+ *
+ * What it computes (plain definitions, no blocking, fusion or reordering):
+ *   - dequant:  every weight w = f(block fields), computed exactly in fp64 and
+ *               rounded once to fp32 (the exact value is always representable
+ *               or, for Q4_K with extreme scales, rounded to nearest-even);
+ *   - gemv:     y[b][n] = sum_k w[n][k] * x[b][k], fp64, k in ascending order,
+ *               plus a[b][n] = sum_k |w[n][k] * x[b][k]| for the tolerance;
+ *   - gemm:     Y[m][n] = sum_k X[m][k] * w[n][k] with X given as IEEE fp16
+ *               bits, w the exact fp32 dequant (not rounded to fp16), fp64
+ *               accumulation in ascending k, plus the same |.| sum.
+ *
+ * Sources (page / section):
+ *   - shimmy "Airframe GPU pipeline", per-layer ops: dequantization happens
+ *     inline inside each matmul (the operation being checked).
+ *   - shimmy "Architecture", Quantization table: the GGUF block types the GPU
+ *     shaders decode (Q4_0 32-element 4-bit, Q8_0 32-element 8-bit, K-quant
+ *     super-blocks, Q6_K 6-bit) and "fp16 unpack" for the scales.
+ *   - dotLLM "GPU Inference", Quantization on GPU table and Weight Strategy:
+ *     weights stay in their original quantized bytes; Q4_K is about
+ *     4.5 bits per parameter.
+ *   - Field layouts the pages do not print are taken from the workload
+ *     definitions that accompany them (Q8_0: fp16 d then 32 int8; Q4_0: fp16 d
+ *     then 16 bytes of nibbles, low nibbles = elements 0-15; Q4_K: fp16 d,
+ *     fp16 dmin, 12 bytes of 6-bit scale/min pairs, 128 bytes of nibbles;
+ *     Q6_K: 128 bytes ql, 64 bytes qh, 16 int8 scales, fp16 d).
+ *   - Where neither says how codes map to elements (the Q4_K nibble order and
+ *     the Q6_K ql/qh bit planes) this follows the public GGUF convention; that
+ *     mapping is "parity unpinned" against real files (none are available) and
+ *     is pinned only by encoder/decoder self-consistency tests.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
+ * Parallelism is an OpenMP loop over independent output rows only; it does not
+ * change any result.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Type ids, mirrored by value (not by header) from the public ABI. */
+enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3 };
+
+/* Return codes: 0 = ok, -1 = bad type, -2 = bad shape, -3 = out of memory. */
+
+int oracle_block_elems(int t)
+{
+    switch (t) {
+    case OR_Q4_0: return 32;
+    case OR_Q8_0: return 32;
+    case OR_Q4_K: return 256;
+    case OR_Q6_K: return 256;
+    default: return 0;
+    }
+}
+
+int oracle_block_bytes(int t)
+{
+    switch (t) {
+    case OR_Q4_0: return 2 + 16;            /* d, 16 bytes of nibbles        */
+    case OR_Q8_0: return 2 + 32;            /* d, 32 int8 codes              */
+    case OR_Q4_K: return 2 + 2 + 12 + 128;  /* d, dmin, scales, nibbles      */
+    case OR_Q6_K: return 128 + 64 + 16 + 2; /* ql, qh, int8 scales, d        */
+    default: return 0;
+    }
+}
+
+/*
+ * IEEE 754 binary16 -> value, written from the format definition
+ * (1 sign bit, 5 exponent bits with bias 15, 10 fraction bits):
+ *   e == 0       : (-1)^s * f * 2^-24          (zero / subnormal)
+ *   e == 31      : +-Inf if f == 0, else NaN
+ *   otherwise    : (-1)^s * (1024 + f) * 2^(e - 25)
+ * Every binary16 value is exactly representable in fp32 and fp64.
+ * (shimmy "Architecture", Quantization table: "fp16 unpack".)
+ */
+double oracle_half_to_double(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return s ? -v : v;
+}
+
+float oracle_half_to_float(uint16_t h)
+{
+    return (float)oracle_half_to_double(h);
+}
+
+void oracle_half_to_float_array(const uint16_t *h, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_half_to_float(h[i]);
+}
+
+static uint16_t rd16(const uint8_t *p)
+{
+    return (uint16_t)(p[0] | (p[1] << 8)); /* little-endian */
+}
+
+/*
+ * Q4_K 6-bit scale / min of sub-block j (0..7) from the 12 packed bytes s[].
+ * Rule, as given with the Llama-3-8B Q4_K workload:
+ *   sub-blocks 0-3: scale = low 6 bits of byte j, min = low 6 bits of byte j+4;
+ *   sub-blocks 4-7: scale = low nibble of byte j+4 with the top 2 bits of
+ *                   byte j-4 as bits 4-5; min = high nibble of byte j+4 with
+ *                   the top 2 bits of byte j as bits 4-5.
+ */
+void oracle_q4k_scale_min(const uint8_t *s, int j, int *sc, int *m)
+{
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 15) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+}
+
+/* Exact value of element e (0 <= e < block_elems) of one block, in fp64. */
+static double elem_value(int t, const uint8_t *blk, int e)
+{
+    switch (t) {
+    case OR_Q8_0: {
+        /* w = d * q, q the int8 at byte 2+e. */
+        double d = oracle_half_to_double(rd16(blk));
+        int q = (int)(int8_t)blk[2 + e];
+        return d * (double)q;
+    }
+    case OR_Q4_0: {
+        /* 16 bytes of nibbles: low nibbles are elements 0-15, high nibbles
+         * elements 16-31; w = d * (q - 8). */
+        double d = oracle_half_to_double(rd16(blk));
+        const uint8_t *qs = blk + 2;
+        int q = (e < 16) ? (qs[e] & 15) : (qs[e - 16] >> 4);
+        return d * (double)(q - 8);
+    }
+    case OR_Q4_K: {
+        /* w = d * sc_j * q - dmin * m_j, sub-block j = e / 32.
+         * Code placement (GGUF convention, parity unpinned): the 128 code
+         * bytes form 4 groups of 32; group p holds sub-block 2p in its low
+         * nibbles and sub-block 2p+1 in its high nibbles, element l of the
+         * sub-block sitting in byte l of the group. */
+        double d = oracle_half_to_double(rd16(blk));
+        double dmin = oracle_half_to_double(rd16(blk + 2));
+        const uint8_t *s = blk + 4;
+        const uint8_t *qs = blk + 16;
+        int j = e / 32, l = e % 32, sc, m;
+        oracle_q4k_scale_min(s, j, &sc, &m);
+        uint8_t byte = qs[32 * (j / 2) + l];
+        int q = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
+        return d * (double)sc * (double)q - dmin * (double)m;
+    }
+    case OR_Q6_K: {
+        /* w = d * scale[e/16] * (q - 32), q a 6-bit code split into a low
+         * nibble (ql) and 2 high bits (qh).  Bit placement (GGUF convention,
+         * parity unpinned): the block is two halves h of 128 elements; within
+         * a half, r = e % 128, g = r / 32, l = r % 32; the low nibble is in
+         * ql[64h + 32(g%2) + l] (low nibble for g < 2, high nibble for
+         * g >= 2) and the high bits are bits 2g..2g+1 of qh[32h + l]. */
+        const uint8_t *ql = blk;
+        const uint8_t *qh = blk + 128;
+        const int8_t *sc = (const int8_t *)(blk + 192);
+        double d = oracle_half_to_double(rd16(blk + 208));
+        int h = e / 128, r = e % 128, g = r / 32, l = r % 32;
+        uint8_t lb = ql[64 * h + 32 * (g % 2) + l];
+        int lo = (g < 2) ? (lb & 15) : (lb >> 4);
+        int hi = (qh[32 * h + l] >> (2 * g)) & 3;
+        int q = lo | (hi << 4);
+        return d * (double)sc[e / 16] * (double)(q - 32);
+    }
+    default:
+        return NAN;
+    }
+}
+
+static int check(int t, int64_t n, int64_t k)
+{
+    int be = oracle_block_elems(t);
+    if (be == 0)
+        return -1;
+    if (n < 0 || k < 0 || k % be != 0)
+        return -2;
+    return 0;
+}
+
+size_t oracle_row_bytes(int t, int64_t k)
+{
+    int be = oracle_block_elems(t);
+    if (be == 0 || k < 0 || k % be != 0)
+        return 0;
+    return (size_t)(k / be) * (size_t)oracle_block_bytes(t);
+}
+
+/* One row of k weights -> fp32 (exact value rounded once). */
+static void dequant_row(int t, const uint8_t *row, int64_t k, float *out)
+{
+    int be = oracle_block_elems(t), bb = oracle_block_bytes(t);
+    for (int64_t i = 0; i < k; i++)
+        out[i] = (float)elem_value(t, row + (i / be) * bb, (int)(i % be));
+}
+
+/* out[n][k] = dequantized weights, row-major fp32. */
+int oracle_dequant(int t, const uint8_t *w, int64_t n, int64_t k, float *out)
+{
+    int rc = check(t, n, k);
+    if (rc)
+        return rc;
+    size_t rb = oracle_row_bytes(t, k);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++)
+        dequant_row(t, w + (size_t)r * rb, k, out + (size_t)r * k);
+    return 0;
+}
+
+/* fp64 value of each weight (no fp32 rounding), for exact-arithmetic pins. */
+int oracle_dequant_f64(int t, const uint8_t *w, int64_t n, int64_t k, double *out)
+{
+    int rc = check(t, n, k);
+    if (rc)
+        return rc;
+    size_t rb = oracle_row_bytes(t, k);
+    int be = oracle_block_elems(t), bb = oracle_block_bytes(t);
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t i = 0; i < k; i++)
+            out[r * k + i] = elem_value(t, w + r * rb + (i / be) * bb, (int)(i % be));
+    return 0;
+}
+
+/*
+ * y[b][n] = sum_k w[n][k] * x[b][k];  a[b][n] = sum_k |w[n][k] * x[b][k]|.
+ * x is fp32 [batch][k].  Products of two fp32 values are exact in fp64, so
+ * only the ascending-k summation rounds (relative error <= k * 2^-53).
+ */
+int oracle_gemv(int t, const uint8_t *w, int64_t n, int64_t k,
+                const float *x, int64_t batch, double *y, double *a)
+{
+    int rc = check(t, n, k);
+    if (rc)
+        return rc;
+    if (batch < 0)
+        return -2;
+    size_t rb = oracle_row_bytes(t, k);
+    int fail = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++) {
+        /* one fp32 dequant pass over the row, then fp64 dot products */
+        float *wrow = (float *)malloc((size_t)(k > 0 ? k : 1) * sizeof(float));
+        if (!wrow) {
+#pragma omp atomic write
+            fail = 1;
+            continue;
+        }
+        dequant_row(t, w + (size_t)r * rb, k, wrow);
+        for (int64_t b = 0; b < batch; b++) {
+            double acc = 0.0, aac = 0.0;
+            for (int64_t i = 0; i < k; i++) {
+                double p = (double)wrow[i] * (double)x[b * k + i];
+                acc += p;
+                aac += fabs(p);
+            }
+            y[b * n + r] = acc;
+            a[b * n + r] = aac;
+        }
+        free(wrow);
+    }
+    if (fail)
+        return -3;
+    return 0;
+}
+
+/*
+ * Y[m][n] = sum_k X[m][k] * w[n][k];  A[m][n] = sum_k |X[m][k] * w[n][k]|.
+ * X is IEEE fp16 bits [m][k], converted exactly; w is the exact fp32 dequant.
+ * rows (optional, may be NULL): compute only output rows rows[0..nrows) of
+ * Y/A, stored compactly as [nrows][n]; with rows == NULL, nrows must equal m.
+ */
+int oracle_gemm(int t, const uint8_t *w, int64_t n, int64_t k,
+                const uint16_t *x, int64_t m, const int64_t *rows, int64_t nrows,
+                double *y, double *a)
+{
+    int rc = check(t, n, k);
+    if (rc)
+        return rc;
+    if (m < 0 || nrows < 0 || (rows == NULL && nrows != m))
+        return -2;
+    for (int64_t i = 0; rows && i < nrows; i++)
+        if (rows[i] < 0 || rows[i] >= m)
+            return -2;
+    size_t rb = oracle_row_bytes(t, k);
+    int fail = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; r++) {
+        float *wrow = (float *)malloc((size_t)(k > 0 ? k : 1) * sizeof(float));
+        if (!wrow) {
+#pragma omp atomic write
+            fail = 1;
+            continue;
+        }
+        dequant_row(t, w + (size_t)r * rb, k, wrow);
+        for (int64_t ii = 0; ii < nrows; ii++) {
+            int64_t mm = rows ? rows[ii] : ii;
+            double acc = 0.0, aac = 0.0;
+            for (int64_t i = 0; i < k; i++) {
+                double p = oracle_half_to_double(x[mm * k + i]) * (double)wrow[i];
+                acc += p;
+                aac += fabs(p);
+            }
+            y[ii * n + r] = acc;
+            a[ii * n + r] = aac;
+        }
+        free(wrow);
+    }
+    if (fail)
+        return -3;
+    return 0;
+}
+
+void oracle_set_threads(int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the quantized-weight matmul.
+
+This module only *draws* random field values and writes them into the byte
+layout of each GGUF block type; it contains none of the method's arithmetic
+(no decoding, no products).  Both the oracle-side tests and the GPU-side
+tests/benchmark draw their inputs from here, so that the two paths see the
+same bytes.
+
+Block layouts written here (byte offsets inside one block, little-endian fp16):
+  Q8_0  (32 elements, 34 B):  [0:2] d, [2:34] 32 x int8 codes
+  Q4_0  (32 elements, 18 B):  [0:2] d, [2:18] 16 bytes of 4-bit codes
+  Q4_K  (256 elements, 144 B): [0:2] d, [2:4] dmin, [4:16] 12 packed bytes of
+                               6-bit scale/min fields, [16:144] 4-bit codes
+  Q6_K  (256 elements, 210 B): [0:128] ql, [128:192] qh, [192:208] 16 x int8
+                               scales, [208:210] d
+
+Distributions (the workload definitions that go with the pages):
+  Q8_0: d ~ U[1e-3, 1e-2] rounded to fp16 (RNE), q ~ U{-127..127}
+  Q4_0: d ~ U[1e-3, 1e-2], code bytes uniform (each nibble ~ U{0..15})
+  Q4_K: d, dmin ~ U[1e-4, 1e-3]; the 12 scale bytes uniform (the packing is a
+        bijection between 96 bits and 16 six-bit fields, so every field is
+        ~ U{0..63}); code bytes uniform
+  Q6_K: ql, qh uniform (so q ~ U{0..63}); scales ~ U{-64..63}; d ~ U[1e-4,1e-3]
+  activations: fp32 (decode) or fp16 (prefill) ~ N(0, 1)
+
+Seeds: matrix i of workload c uses seed 1000*c + i; its activation uses
+1000*c + 500 + i.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
+NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210}
+
+DEFAULT_D_RANGE = {Q8_0: (1e-3, 1e-2), Q4_0: (1e-3, 1e-2), Q4_K: (1e-4, 1e-3), Q6_K: (1e-4, 1e-3)}
+
+
+def row_bytes(qtype: int, k: int) -> int:
+    be = BLOCK_ELEMS[qtype]
+    if k % be:
+        raise ValueError("k=%d is not a multiple of the %s block size %d" % (k, NAMES[qtype], be))
+    return (k // be) * BLOCK_BYTES[qtype]
+
+
+def _f16_bytes(v: np.ndarray) -> np.ndarray:
+    """fp64 draws -> fp16 (round to nearest even) -> little-endian bytes [..., 2]."""
+    return v.astype("<f2").view(np.uint8).reshape(v.shape + (2,))
+
+
+def gen_weights(qtype: int, n: int, k: int, seed: int, d_range=None) -> np.ndarray:
+    """Random quantized weight matrix as raw bytes, shape [n, row_bytes]."""
+    rng = np.random.default_rng(seed)
+    nb = k // BLOCK_ELEMS[qtype]
+    rb = row_bytes(qtype, k)
+    lo, hi = d_range if d_range is not None else DEFAULT_D_RANGE[qtype]
+    blk = np.empty((n, nb, BLOCK_BYTES[qtype]), dtype=np.uint8)
+    if qtype == Q8_0:
+        blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
+        blk[:, :, 2:34] = rng.integers(-127, 128, size=(n, nb, 32), dtype=np.int8).view(np.uint8)
+    elif qtype == Q4_0:
+        blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
+        blk[:, :, 2:18] = rng.integers(0, 256, size=(n, nb, 16), dtype=np.uint8)
+    elif qtype == Q4_K:
+        blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
+        blk[:, :, 2:4] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
+        blk[:, :, 4:16] = rng.integers(0, 256, size=(n, nb, 12), dtype=np.uint8)
+        blk[:, :, 16:144] = rng.integers(0, 256, size=(n, nb, 128), dtype=np.uint8)
+    elif qtype == Q6_K:
+        blk[:, :, 0:192] = rng.integers(0, 256, size=(n, nb, 192), dtype=np.uint8)
+        blk[:, :, 192:208] = rng.integers(-64, 64, size=(n, nb, 16), dtype=np.int8).view(np.uint8)
+        blk[:, :, 208:210] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
+    else:
+        raise ValueError("unknown type %r" % (qtype,))
+    return blk.reshape(n, rb)
+
+
+def gen_x(k: int, batch: int, seed: int) -> np.ndarray:
+    """fp32 activations [batch, k] ~ N(0, 1)."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((batch, k), dtype=np.float32)
+
+
+def gen_x_f16(m: int, k: int, seed: int) -> np.ndarray:
+    """fp16 activations [m, k] ~ N(0, 1) (drawn in fp32, rounded RNE)."""
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((m, k), dtype=np.float32).astype(np.float16)
+
+
+# --------------------------------------------------------------------------
+# Workloads (shapes, block types and seeds).  Each entry: (name, qtype, n, k).
+# --------------------------------------------------------------------------
+
+def _llama_layer(hidden, ffn, kv, t_default, t_v=None, t_down=None):
+    t_v = t_default if t_v is None else t_v
+    t_down = t_default if t_down is None else t_down
+    return [("q", t_default, hidden, hidden), ("k", t_default, kv, hidden),
+            ("v", t_v, kv, hidden), ("o", t_default, hidden, hidden),
+            ("gate", t_default, ffn, hidden), ("up", t_default, ffn, hidden),
+            ("down", t_down, hidden, ffn)]
+
+
+def workload(cfg: int):
+    """Matrix list of one workload: [(name, qtype, n, k, seed)], plus extras."""
+    mats = []
+    if cfg == 1:
+        # single Q8_0 2048 x 2048 GEMV
+        mats = [("w", Q8_0, 2048, 2048)]
+    elif cfg == 2:
+        # TinyLlama-shaped Q4_0 decode stream: 22 layers x 7 projections
+        for layer in range(22):
+            mats += [("l%d.%s" % (layer, nm), t, n, k)
+                     for nm, t, n, k in _llama_layer(2048, 5632, 256, Q4_0)]
+    elif cfg == 3:
+        # Llama-3-8B-shaped Q4_K decode set: 32 layers x 7 projections
+        for layer in range(32):
+            mats += [("l%d.%s" % (layer, nm), t, n, k)
+                     for nm, t, n, k in _llama_layer(4096, 14336, 1024, Q4_K)]
+    elif cfg == 4:
+        # prefill chunk GEMMs: N in {14336, 4096}, K = 4096, Q8_0 and Q4_K
+        mats = [("gate_q8_0", Q8_0, 14336, 4096), ("q_q8_0", Q8_0, 4096, 4096),
+                ("gate_q4_k", Q4_K, 14336, 4096), ("q_q4_k", Q4_K, 4096, 4096)]
+    elif cfg == 5:
+        # Q4_K_M-style mix: v and down in Q6_K, plus a Q6_K LM head
+        for layer in range(32):
+            mats += [("l%d.%s" % (layer, nm), t, n, k)
+                     for nm, t, n, k in _llama_layer(4096, 14336, 1024, Q4_K, t_v=Q6_K, t_down=Q6_K)]
+        mats.append(("lm_head", Q6_K, 128256, 4096))
+    else:
+        raise ValueError("unknown workload %r" % (cfg,))
+    return [(nm, t, n, k, 1000 * cfg + i) for i, (nm, t, n, k) in enumerate(mats)]
+
+
+def x_seed(cfg: int, i: int) -> int:
+    return 1000 * cfg + 500 + i
+
+
+PREFILL_M = 512
+PREFILL_CHUNKS = 4
