@@ -1,0 +1,148 @@
+"""dequant_matmul_amd -- quantized-weight matmul on AMD MI355X (gfx950).
+
+Python binding of ``libqmm.so`` (C ABI declared in ``include/qmm.h``).  This
+module only marshals arguments: it checks tensor dtypes/devices, allocates the
+output with torch, and passes raw device pointers plus torch's current HIP
+stream to the library, where every step of the computation runs.  There is no
+CPU fallback: if the library is missing, importing this package fails.
+
+    import dequant_matmul_amd as qmm
+    y = qmm.gemv(w_bytes, qmm.Q4_K, n, k, x)          # x fp32 [B, k] -> y fp32 [B, n]
+    Y = qmm.gemm_prefill(w_bytes, qmm.Q4_K, n, k, X)  # X fp16 [m, k] -> Y fp32 [m, n]
+    W = qmm.dequant(w_bytes, qmm.Q4_K, n, k)          # -> fp32 [n, k]
+
+Block types and layouts follow shimmy "Architecture" (Quantization table) and
+dotLLM "GPU Inference" (Quantization on GPU table); see include/qmm.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmm.so")
+
+Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
+TYPE_NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_ALIGN, ERR_HIP = range(6)
+
+# C-ABI entry points and their ctypes signatures (mirrors include/qmm.h).
+_P, _I, _I64, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "qmm_block_elems": (_I, [_I]),
+    "qmm_block_bytes": (_I, [_I]),
+    "qmm_row_bytes": (_SZ, [_I, _I64]),
+    "qmm_dequant": (_I, [_I, _P, _I64, _I64, _P, _P]),
+    "qmm_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "qmm_gemm_prefill": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "qmm_status_str": (ctypes.c_char_p, [_I]),
+    "qmm_version": (ctypes.c_char_p, []),
+}
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_str(status), status))
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libqmm.so not built: run `python -m dequant_matmul_amd.build` "
+                          "(expected at %s)" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return L
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.qmm_status_str(int(status)).decode()
+
+
+def version() -> str:
+    return lib.qmm_version().decode()
+
+
+def block_elems(qtype: int) -> int:
+    return lib.qmm_block_elems(qtype)
+
+
+def block_bytes(qtype: int) -> int:
+    return lib.qmm_block_bytes(qtype)
+
+
+def row_bytes(qtype: int, k: int) -> int:
+    return lib.qmm_row_bytes(qtype, k)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_w(w, qtype: int, n: int, k: int):
+    torch = _torch()
+    if w.dtype != torch.uint8 or not w.is_cuda:
+        raise TypeError("weights must be a uint8 tensor on a HIP device")
+    if not w.is_contiguous():
+        raise ValueError("weights must be contiguous")
+    rb = row_bytes(qtype, k)
+    if (n > 0 and k > 0) and w.numel() != n * rb:
+        raise ValueError("weight tensor has %d bytes, expected n * row_bytes = %d" % (w.numel(), n * rb))
+
+
+def _call(status: int, what: str) -> None:
+    if status != OK:
+        raise QmmError(status, what)
+
+
+def dequant(w, qtype: int, n: int, k: int, out=None):
+    """fp32 [n, k] dequantized weights (bit-exact)."""
+    torch = _torch()
+    _check_w(w, qtype, n, k)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    _call(lib.qmm_dequant(qtype, w.data_ptr(), n, k, out.data_ptr(), _stream_ptr(w.device)), "qmm_dequant")
+    return out
+
+
+def gemv(w, qtype: int, n: int, k: int, x, out=None):
+    """y[b, j] = sum_i W[j, i] x[b, i]; x fp32 [B, k] (or [k]), 1 <= B <= 8."""
+    torch = _torch()
+    _check_w(w, qtype, n, k)
+    squeeze = x.dim() == 1
+    if squeeze:
+        x = x.unsqueeze(0)
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or x.shape[1] != k:
+        raise ValueError("x must be a contiguous fp32 device tensor [B, k]")
+    B = x.shape[0]
+    if out is None:
+        out = torch.empty((B, n), dtype=torch.float32, device=w.device)
+    _call(lib.qmm_gemv(qtype, w.data_ptr(), n, k, x.data_ptr(), B, out.data_ptr(), _stream_ptr(w.device)),
+          "qmm_gemv")
+    return out[0] if squeeze else out
+
+
+def gemm_prefill(w, qtype: int, n: int, k: int, x, out=None):
+    """Y[r, j] = sum_i X[r, i] W[j, i]; X fp16 [m, k] -> Y fp32 [m, n]."""
+    torch = _torch()
+    _check_w(w, qtype, n, k)
+    if x.dtype != torch.float16 or not x.is_cuda or not x.is_contiguous() or x.shape[1] != k:
+        raise ValueError("X must be a contiguous fp16 device tensor [m, k]")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    _call(lib.qmm_gemm_prefill(qtype, w.data_ptr(), n, k, x.data_ptr(), m, out.data_ptr(),
+                               _stream_ptr(w.device)), "qmm_gemm_prefill")
+    return out

@@ -1,0 +1,142 @@
+// qmm_api.cpp -- the C ABI of libqmm.so (declared in include/qmm.h): argument
+// validation on the host, then one kernel launch on the caller's stream.
+// Nothing here allocates, synchronizes or keeps state.
+#include <hip/hip_runtime.h>
+
+#include "../../include/qmm.h"
+#include "qmm_launch.h"
+
+namespace {
+
+int block_elems(int t)
+{
+    switch (t) {
+    case QMM_Q4_0: case QMM_Q8_0: return 32;
+    case QMM_Q4_K: case QMM_Q6_K: return 256;
+    default: return 0;
+    }
+}
+
+int block_bytes(int t)
+{
+    switch (t) {
+    case QMM_Q4_0: return 18;
+    case QMM_Q8_0: return 34;
+    case QMM_Q4_K: return 144;
+    case QMM_Q6_K: return 210;
+    default: return 0;
+    }
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shared checks; on success *rb holds the row size in bytes.
+int check_common(int type, const void *w, int64_t n, int64_t k, size_t *rb)
+{
+    const int be = block_elems(type);
+    if (be == 0)
+        return QMM_ERR_TYPE;
+    if (n < 0 || k < 0 || k % be != 0)
+        return QMM_ERR_SHAPE;
+    // keep every index the kernels form inside int32 element counts per row
+    if (n > 0x7fffffff || k > 0x7fffffff)
+        return QMM_ERR_SHAPE;
+    *rb = (size_t)(k / be) * (size_t)block_bytes(type);
+    if (n > 0 && k > 0) {
+        if (w == nullptr)
+            return QMM_ERR_NULL;
+        if (!aligned16(w))
+            return QMM_ERR_ALIGN;
+    }
+    return QMM_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int qmm_block_elems(int type) { return block_elems(type); }
+
+int qmm_block_bytes(int type) { return block_bytes(type); }
+
+size_t qmm_row_bytes(int type, int64_t k)
+{
+    const int be = block_elems(type);
+    if (be == 0 || k < 0 || k % be != 0)
+        return 0;
+    return (size_t)(k / be) * (size_t)block_bytes(type);
+}
+
+int qmm_dequant(int type, const void *w, int64_t n, int64_t k, float *out, void *stream)
+{
+    size_t rb = 0;
+    int st = check_common(type, w, n, k, &rb);
+    if (st != QMM_OK)
+        return st;
+    if (n == 0 || k == 0)
+        return QMM_OK;
+    if (out == nullptr)
+        return QMM_ERR_NULL;
+    if (!aligned16(out))
+        return QMM_ERR_ALIGN;
+    return hip_status(qmm::launch_dequant(type, w, n, k, rb, out, (hipStream_t)stream));
+}
+
+int qmm_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch, float *y,
+             void *stream)
+{
+    size_t rb = 0;
+    int st = check_common(type, w, n, k, &rb);
+    if (st != QMM_OK)
+        return st;
+    if (batch < 0 || batch > 8)
+        return QMM_ERR_SHAPE;
+    if (n == 0 || batch == 0)
+        return QMM_OK;
+    if (y == nullptr || (k > 0 && x == nullptr))
+        return QMM_ERR_NULL;
+    if (!aligned16(y) || (k > 0 && !aligned16(x)))
+        return QMM_ERR_ALIGN;
+    if (k == 0)
+        return hip_status(qmm::launch_fill_zero(y, batch * n, (hipStream_t)stream));
+    return hip_status(qmm::launch_gemv(type, w, n, k, rb, x, (int)batch, y, (hipStream_t)stream));
+}
+
+int qmm_gemm_prefill(int type, const void *w, int64_t n, int64_t k, const uint16_t *x, int64_t m, float *y,
+                     void *stream)
+{
+    size_t rb = 0;
+    int st = check_common(type, w, n, k, &rb);
+    if (st != QMM_OK)
+        return st;
+    if (m < 0 || m > 0x7fffffff)
+        return QMM_ERR_SHAPE;
+    if (n == 0 || m == 0)
+        return QMM_OK;
+    if (y == nullptr || (k > 0 && x == nullptr))
+        return QMM_ERR_NULL;
+    if (!aligned16(y) || (k > 0 && !aligned16(x)))
+        return QMM_ERR_ALIGN;
+    if (k == 0)
+        return hip_status(qmm::launch_fill_zero(y, m * n, (hipStream_t)stream));
+    return hip_status(qmm::launch_gemm(type, w, n, k, rb, x, m, y, (hipStream_t)stream));
+}
+
+const char *qmm_status_str(int status)
+{
+    switch (status) {
+    case QMM_OK: return "ok";
+    case QMM_ERR_NULL: return "null pointer";
+    case QMM_ERR_TYPE: return "unknown block type";
+    case QMM_ERR_SHAPE: return "invalid shape";
+    case QMM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QMM_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+const char *qmm_version(void) { return "qmm 0.1.0 gfx950"; }
+
+}  // extern "C"

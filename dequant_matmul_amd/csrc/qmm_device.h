@@ -1,0 +1,95 @@
+// qmm_device.h -- device-side helpers shared by the gfx950 kernels of libqmm.
+//
+// Block formats decoded here (shimmy "Architecture", Quantization table;
+// dotLLM "GPU Inference", Quantization on GPU table):
+//   Q4_0  32 el / 18 B : fp16 d | 16 B codes (el i<16 low nibble of byte i,
+//                        el i>=16 high nibble of byte i-16)   w = d (q - 8)
+//   Q8_0  32 el / 34 B : fp16 d | 32 int8                      w = d q
+//   Q4_K 256 el / 144 B: fp16 d | fp16 dmin | 12 B 6-bit scale/min |
+//                        128 B codes; w = d sc_j q - dmin m_j, j = e / 32
+//   Q6_K 256 el / 210 B: 128 B ql | 64 B qh | 16 int8 scales | fp16 d;
+//                        w = d scale[e/16] (q - 32)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+enum : int { T_Q4_0 = 0, T_Q8_0 = 1, T_Q4_K = 2, T_Q6_K = 3 };
+
+template <int T> struct Fmt;
+template <> struct Fmt<T_Q4_0> { static constexpr int BE = 32, BB = 18; };
+template <> struct Fmt<T_Q8_0> { static constexpr int BE = 32, BB = 34; };
+template <> struct Fmt<T_Q4_K> { static constexpr int BE = 256, BB = 144; };
+template <> struct Fmt<T_Q6_K> { static constexpr int BE = 256, BB = 210; };
+
+// IEEE binary16 bits -> fp32 (exact; v_cvt_f32_f16).
+__device__ __forceinline__ float h2f(uint32_t bits16)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// Hide a value from the optimizer so that a whole-dword mask stays one
+// v_and_b32 followed by per-byte converts (v_cvt_f32_ubyteN), instead of being
+// folded into one bit-field extract per element.
+__device__ __forceinline__ uint32_t opaque(uint32_t v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Bytes [s, s+4) of the 8-byte value (hi:lo), s in 0..3 (v_alignbyte_b32).
+__device__ __forceinline__ uint32_t align_bytes(uint32_t hi, uint32_t lo, uint32_t s)
+{
+    return __builtin_amdgcn_alignbyte(hi, lo, s);
+}
+
+__device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xffu); }
+__device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xffu); }
+__device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xffu); }
+__device__ __forceinline__ float ub3(uint32_t v) { return (float)(v >> 24); }
+__device__ __forceinline__ float sb0(uint32_t v) { return (float)(int8_t)(v); }
+__device__ __forceinline__ float sb1(uint32_t v) { return (float)(int8_t)(v >> 8); }
+__device__ __forceinline__ float sb2(uint32_t v) { return (float)(int8_t)(v >> 16); }
+__device__ __forceinline__ float sb3(uint32_t v) { return (float)(int8_t)(v >> 24); }
+
+// Make this wave's LDS writes visible to the other lanes of the same wave.
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Sum over the 64 lanes of a wavefront; every lane receives the total.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Q4_K: 6-bit scale and min of sub-block j from the 3 dwords holding the 12
+// packed bytes (byte i of the 12 is byte i%4 of dword i/4).  For j < 4 the
+// scale / min are the low 6 bits of bytes j and j+4; for j >= 4 they are the
+// low / high nibble of byte j+4 with the top two bits of byte j-4 / j as bits
+// 4-5 (packing given with the Llama-3-8B Q4_K workload).
+__device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t s2, int j,
+                                              uint32_t &sc, uint32_t &m)
+{
+    const uint32_t sh = 8u * (uint32_t)(j & 3);
+    const uint32_t a = (s0 >> sh) & 0xffu;  // byte j   (j<4) or j-4 (j>=4)
+    const uint32_t b = (s1 >> sh) & 0xffu;  // byte j+4 (j<4) or j   (j>=4)
+    const uint32_t c = (s2 >> sh) & 0xffu;  // byte j+4 for j>=4
+    if (j < 4) {
+        sc = a & 63u;
+        m = b & 63u;
+    } else {
+        sc = (c & 15u) | ((a >> 6) << 4);
+        m = (c >> 4) | ((b >> 6) << 4);
+    }
+}
+
+}  // namespace qmm

@@ -1,0 +1,25 @@
+// qmm_launch.h -- internal launchers of libqmm (host side).  Arguments are
+// already validated by the C-ABI layer (qmm_api.cpp): known type, k a
+// multiple of the block size, n, k, m/batch > 0, pointers non-null and
+// 16-byte aligned.  Each launcher only enqueues on stream s and returns the
+// HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmm {
+
+hipError_t launch_dequant(int type, const void *w, int64_t n, int64_t k, size_t rb, float *out,
+                          hipStream_t s);
+
+hipError_t launch_gemv(int type, const void *w, int64_t n, int64_t k, size_t rb, const float *x,
+                       int batch, float *y, hipStream_t s);
+
+hipError_t launch_gemm(int type, const void *w, int64_t n, int64_t k, size_t rb, const uint16_t *x,
+                       int64_t m, float *y, hipStream_t s);
+
+hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s);
+
+}  // namespace qmm

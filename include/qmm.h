@@ -1,0 +1,135 @@
+/*
+ * qmm.h -- C ABI of libqmm.so: matrix products whose weights are stored as
+ * GGUF quantized blocks and decoded on the fly on an AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (shimmy "Airframe GPU pipeline", per-layer ops): every matmul
+ * decodes the quantized weight blocks inline and multiplies them by the
+ * activations; there is no separate dequantize-then-multiply pass.  dotLLM
+ * "GPU Inference" (Forward Pass, step 4a) splits the same projections by
+ * sequence length: one token (decode) uses a quantized GEMV straight from the
+ * blocks, many tokens (prefill) a dense FP16 GEMM; its kernel table lists
+ * dequant-to-FP16 kernels and quantized GEMV kernels with one block per
+ * output row.  Weights stay resident in their original quantized bytes
+ * (dotLLM "GPU Inference", Weight Loading Pipeline).
+ *
+ * Block types (shimmy "Architecture", Quantization table; dotLLM "GPU
+ * Inference", Quantization on GPU table).  Byte layout of one block,
+ * little-endian fp16 fields:
+ *   QMM_Q4_0  32 elements, 18 B:  d | 16 B codes        w = d (q - 8)
+ *             element i < 16: low nibble of code byte i; i >= 16: high
+ *             nibble of code byte i - 16
+ *   QMM_Q8_0  32 elements, 34 B:  d | 32 int8 codes     w = d q
+ *   QMM_Q4_K  256 elements, 144 B: d | dmin | 12 B scales | 128 B codes
+ *             w = d sc_j q - dmin m_j, j = e / 32 (6-bit sc_j, m_j packed in
+ *             the 12 bytes: j < 4 low 6 bits of bytes j and j+4; j >= 4 the
+ *             nibbles of byte j+4 plus the top 2 bits of bytes j-4 and j);
+ *             element (j, l) is nibble (j % 2) of code byte 32 (j / 2) + l
+ *   QMM_Q6_K  256 elements, 210 B: 128 B ql | 64 B qh | 16 int8 scales | d
+ *             w = d scale[e / 16] (q - 32); element e = 128 h + 32 g + l has
+ *             its low 4 bits in nibble (g / 2) of ql[64 h + 32 (g % 2) + l]
+ *             and its high 2 bits at bit 2 g of qh[32 h + l]
+ *
+ * Common conventions
+ *   - Weight matrix w: n rows (output features) of qmm_row_bytes(t, k)
+ *     bytes each, packed back to back; a row holds the k inputs in block
+ *     order.  Row-major outputs (dotLLM "GPU Inference", cuBLAS GEMM/GEMV:
+ *     row-major C = A x B).
+ *   - All pointers are device pointers (HIP device memory, or memory the
+ *     device can access) and must be 16-byte aligned.  The caller owns every
+ *     buffer; the library allocates nothing, keeps no state between calls,
+ *     and is safe to call from several host threads.
+ *   - stream: a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on that stream and never synchronizes
+ *     (dotLLM "GPU Inference", Synchronization Model: one stream, all
+ *     launches asynchronous).  Outputs are overwritten, never accumulated.
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     the call then returns the error and touches no memory.  A launch error
+ *     reported by the HIP runtime returns QMM_ERR_HIP.  Errors of earlier,
+ *     unrelated work on the stream are not reported here.
+ *   - Empty problems (n == 0, or batch / m == 0) return QMM_OK and enqueue
+ *     nothing; k == 0 with n > 0 writes zeros to the output (empty sums).
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef QMM_API
+#define QMM_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qmm_type {
+    QMM_Q4_0 = 0,
+    QMM_Q8_0 = 1,
+    QMM_Q4_K = 2,
+    QMM_Q6_K = 3
+} qmm_type;
+
+typedef enum qmm_status {
+    QMM_OK = 0,
+    QMM_ERR_NULL = 1,  /* a required pointer is NULL                     */
+    QMM_ERR_TYPE = 2,  /* unknown block type                             */
+    QMM_ERR_SHAPE = 3, /* negative size, k not a block multiple, batch>8 */
+    QMM_ERR_ALIGN = 4, /* a pointer is not 16-byte aligned               */
+    QMM_ERR_HIP = 5    /* the HIP runtime rejected a launch              */
+} qmm_status;
+
+/* Elements per block (32 or 256); 0 for an unknown type. */
+QMM_API int qmm_block_elems(int type);
+
+/* Bytes per block (18, 34, 144, 210); 0 for an unknown type. */
+QMM_API int qmm_block_bytes(int type);
+
+/* Bytes of one row of k weights; 0 if the type is unknown, k < 0 or k is not
+ * a multiple of the block size. */
+QMM_API size_t qmm_row_bytes(int type, int64_t k);
+
+/*
+ * Dequantize: out[n][k] (fp32, row-major) = the weights of w.
+ * Each value is the exact weight rounded once to fp32; no division,
+ * reciprocal or fp16 intermediate is used, so the result is bit-identical to
+ * any exact decoder.  (dotLLM "GPU Inference", Custom Kernels table: the
+ * dequant_* kernels; here the output is fp32 so it can be exact.)
+ */
+QMM_API int qmm_dequant(int type, const void *w, int64_t n, int64_t k, float *out, void *stream);
+
+/*
+ * Decode GEMV: y[b][j] = sum_i w[j][i] * x[b][i] for b < batch, j < n.
+ * x: fp32 [batch][k], y: fp32 [batch][n], 1 <= batch <= 8 (batch 0 = empty).
+ * Weights are read once from the quantized bytes and decoded in registers;
+ * products and sums are fp32.  (dotLLM "GPU Inference", Custom Kernels
+ * table: quantized_gemv_* operating directly on quantized weights; the
+ * decode path is memory-bandwidth bound.)
+ */
+QMM_API int qmm_gemv(int type, const void *w, int64_t n, int64_t k,
+             const float *x, int64_t batch, float *y, void *stream);
+
+/*
+ * Prefill GEMM: y[r][j] = sum_i x[r][i] * w[j][i] for r < m, j < n.
+ * x: IEEE fp16 bit patterns [m][k], y: fp32 [m][n].  Weight tiles are decoded
+ * to fp16 (round to nearest even) in on-chip memory and fed to fp16 matrix
+ * cores with fp32 accumulation.  (dotLLM "GPU Inference", Future Work: a
+ * fused quantized GEMM replacing dequant-to-scratch + FP16 GEMM for
+ * prefill; shimmy "Airframe GPU pipeline": prompts are prefilled in
+ * 512-token chunks.)
+ */
+QMM_API int qmm_gemm_prefill(int type, const void *w, int64_t n, int64_t k,
+                     const uint16_t *x, int64_t m, float *y, void *stream);
+
+/* Static text for a status code (never NULL). */
+QMM_API const char *qmm_status_str(int status);
+
+/* Library version string, e.g. "qmm 0.1.0 gfx950". */
+QMM_API const char *qmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

@@ -1,0 +1,247 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bars:
+  dequant   bit-exact fp32 (+0 == -0);
+  gemv      |y - ref| <= 2e-5 * sum|w x| per output element (exact 0 when the
+            sum is 0);
+  gemm      |Y - ref| <= 1e-3 * sum|w x| per output element, and X = one-hot
+            rows reproduce fp16_RNE(w) exactly.
+Sizes span several tiles / segments and ragged tails; the full workload shapes
+are checked too (GEMM on sampled rows of M).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import qmm_inputs as G
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import dequant_matmul_amd as q  # noqa: E402
+
+DEV = "cuda:0"
+TYPES = [G.Q4_0, G.Q8_0, G.Q4_K, G.Q6_K]
+GEMV_TOL = 2e-5
+GEMM_TOL = 1e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def upload(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def check_tol(got, ref, absum, tol, what):
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref)
+    bound = tol * absum
+    zero = absum == 0
+    assert np.all(got[zero] == 0), what + ": nonzero output where sum|w x| = 0"
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / np.where(bound > 0, bound, 1)), err.shape)
+        raise AssertionError("%s: %d elements over tolerance, worst at %s: got %r ref %r bound %r"
+                             % (what, int(bad.sum()), i, got[i], ref[i], bound[i]))
+    return float((err[~zero] / absum[~zero]).max()) if (~zero).any() else 0.0
+
+
+# ---------------------------------------------------------------- dequant ---
+
+DEQ_SHAPES = [(1, None), (37, None), (130, 3), (64, 16)]   # (n, blocks per row; None = 1)
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("shape", DEQ_SHAPES)
+def test_dequant_bit_exact_small(t, shape):
+    n, nb = shape
+    k = G.BLOCK_ELEMS[t] * (nb or 1)
+    say("dequant", G.NAMES[t], n, k)
+    w = G.gen_weights(t, n, k, seed=100 + n + t)
+    ref = oracle.dequant(t, w, n, k)
+    got = q.dequant(upload(w), t, n, k).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("t,n,k", [(G.Q8_0, 2048, 2048), (G.Q4_0, 5632, 2048), (G.Q4_K, 14336, 4096),
+                                   (G.Q6_K, 4096, 14336)])
+def test_dequant_bit_exact_workload_shapes(t, n, k):
+    say("dequant full", G.NAMES[t], n, k)
+    w = G.gen_weights(t, n, k, seed=7)
+    ref = oracle.dequant(t, w, n, k)
+    got = q.dequant(upload(w), t, n, k).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_dequant_extreme_scales():
+    """fp16 scales over the whole finite range (incl. subnormals and negative
+    values) still give bit-identical fp32 weights."""
+    for t in TYPES:
+        n, k = 16, 4 * G.BLOCK_ELEMS[t]
+        w = G.gen_weights(t, n, k, seed=3, d_range=(-6e4, 6e4))
+        w2 = G.gen_weights(t, n, k, seed=4, d_range=(-1e-6, 1e-6))   # fp16 subnormals
+        for ww in (w, w2):
+            ref = oracle.dequant(t, ww, n, k)
+            got = q.dequant(upload(ww), t, n, k).cpu().numpy()
+            assert np.array_equal(got, ref), G.NAMES[t]
+
+
+# ------------------------------------------------------------------- gemv ---
+
+GEMV_SHAPES = [(1, 1), (37, 3), (130, 9), (259, 17), (64, 40)]   # (n, blocks per row)
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 8])
+def test_gemv_small_and_ragged(t, batch):
+    worst = 0.0
+    for n, nb in GEMV_SHAPES:
+        k = G.BLOCK_ELEMS[t] * nb
+        say("gemv", G.NAMES[t], "n", n, "k", k, "batch", batch)
+        w = G.gen_weights(t, n, k, seed=200 + nb)
+        x = G.gen_x(k, batch, seed=300 + nb)
+        ref, absum = oracle.gemv(t, w, n, k, x)
+        got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+        worst = max(worst, check_tol(got, ref, absum, GEMV_TOL, "gemv %s n=%d k=%d B=%d" % (G.NAMES[t], n, k, batch)))
+    say("  worst relative error", worst)
+
+
+@pytest.mark.parametrize("t,n,k", [(G.Q8_0, 2048, 2048), (G.Q4_0, 2048, 5632), (G.Q4_0, 256, 2048),
+                                   (G.Q4_K, 14336, 4096), (G.Q4_K, 4096, 14336), (G.Q6_K, 4096, 14336),
+                                   (G.Q6_K, 1024, 4096)])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_gemv_workload_shapes(t, n, k, batch):
+    say("gemv full", G.NAMES[t], n, k, batch)
+    w = G.gen_weights(t, n, k, seed=11)
+    x = G.gen_x(k, batch, seed=12)
+    ref, absum = oracle.gemv(t, w, n, k, x)
+    got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+    say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "gemv %s %dx%d" % (G.NAMES[t], n, k)))
+
+
+@pytest.mark.parametrize("t", TYPES)
+def test_gemv_special_inputs(t):
+    n, k = 70, 8 * G.BLOCK_ELEMS[t]
+    w = G.gen_weights(t, n, k, seed=5)
+    W = oracle.dequant(t, w, n, k)
+    wd = upload(w)
+    # one-hot x selects a column (exactly: a single nonzero product)
+    for col in (0, 17, k // 2 + 3, k - 1):
+        x = np.zeros((1, k), np.float32)
+        x[0, col] = 1.0
+        got = q.gemv(wd, t, n, k, upload(x)).cpu().numpy()[0]
+        assert np.array_equal(got, W[:, col]), col
+    # zero x -> exactly zero
+    got = q.gemv(wd, t, n, k, upload(np.zeros((3, k), np.float32))).cpu().numpy()
+    assert not got.any()
+    # each batch column equals the batch-1 call
+    x = G.gen_x(k, 8, seed=6)
+    y8 = q.gemv(wd, t, n, k, upload(x)).cpu().numpy()
+    for b in (0, 3, 7):
+        y1 = q.gemv(wd, t, n, k, upload(x[b:b + 1])).cpu().numpy()
+        ref, absum = oracle.gemv(t, w, n, k, x[b:b + 1])
+        check_tol(y1, ref, absum, GEMV_TOL, "batch-1")
+        check_tol(y8[b:b + 1], ref, absum, GEMV_TOL, "batch-8 column")
+
+
+def test_gemv_unaligned_rows():
+    """Row sizes that are not a multiple of 16 bytes take the 2-byte staging
+    path."""
+    for t, nb in ((G.Q8_0, 3), (G.Q4_0, 5), (G.Q6_K, 3)):
+        k = G.BLOCK_ELEMS[t] * nb
+        assert G.row_bytes(t, k) % 16 != 0
+        for batch in (1, 5):
+            w = G.gen_weights(t, 45, k, seed=9)
+            x = G.gen_x(k, batch, seed=10)
+            ref, absum = oracle.gemv(t, w, 45, k, x)
+            got = q.gemv(upload(w), t, 45, k, upload(x)).cpu().numpy()
+            check_tol(got, ref, absum, GEMV_TOL, "unaligned %s" % G.NAMES[t])
+
+
+def test_gemv_empty_and_k0():
+    w = upload(np.zeros(16, np.uint8))
+    y = q.gemv(w[:0], G.Q8_0, 0, 32, upload(np.zeros((1, 32), np.float32)))
+    assert y.shape == (1, 0)
+    y = torch.full((2, 5), 7.0, device=DEV)
+    q.gemv(w[:0], G.Q8_0, 5, 0, torch.zeros((2, 0), device=DEV), out=y)
+    assert not y.cpu().numpy().any()
+
+
+# ------------------------------------------------------------------- gemm ---
+
+GEMM_SHAPES = [(1, 1, 1), (7, 50, 3), (130, 200, 9), (257, 129, 5)]   # (m, n, blocks per row)
+
+
+@pytest.mark.parametrize("t", TYPES)
+def test_gemm_small_and_ragged(t):
+    worst = 0.0
+    for m, n, nb in GEMM_SHAPES:
+        k = G.BLOCK_ELEMS[t] * nb
+        say("gemm", G.NAMES[t], m, n, k)
+        w = G.gen_weights(t, n, k, seed=400 + nb)
+        X = G.gen_x_f16(m, k, seed=500 + nb)
+        ref, absum = oracle.gemm(t, w, n, k, X)
+        got = q.gemm_prefill(upload(w), t, n, k, upload(X)).cpu().numpy()
+        worst = max(worst, check_tol(got, ref, absum, GEMM_TOL, "gemm %s %dx%dx%d" % (G.NAMES[t], m, n, k)))
+    say("  worst relative error", worst)
+
+
+@pytest.mark.parametrize("t", TYPES)
+def test_gemm_one_hot_rows_give_fp16_weights(t):
+    """Row r of X = e_{c_r} makes row r of Y equal to column c_r of W rounded
+    to fp16 (round to nearest even), exactly: pins the rounding mode and the
+    operand orientation."""
+    n, k = 150, 5 * G.BLOCK_ELEMS[t]
+    w = G.gen_weights(t, n, k, seed=8)
+    W16 = oracle.dequant(t, w, n, k).astype(np.float16).astype(np.float32)
+    cols = [0, 1, 31, 32, k // 2, k - 1, 129 % k]
+    X = np.zeros((len(cols), k), np.float16)
+    for r, c in enumerate(cols):
+        X[r, c] = 1.0
+    got = q.gemm_prefill(upload(w), t, n, k, upload(X)).cpu().numpy()
+    for r, c in enumerate(cols):
+        assert np.array_equal(got[r], W16[:, c]), (r, c)
+
+
+@pytest.mark.parametrize("t,n", [(G.Q8_0, 14336), (G.Q8_0, 4096), (G.Q4_K, 14336), (G.Q4_K, 4096),
+                                 (G.Q4_0, 4096), (G.Q6_K, 4096)])
+def test_gemm_prefill_workload_shapes(t, n):
+    m, k = G.PREFILL_M, 4096
+    say("gemm full", G.NAMES[t], m, n, k)
+    w = G.gen_weights(t, n, k, seed=13)
+    X = G.gen_x_f16(m, k, seed=14)
+    got = q.gemm_prefill(upload(w), t, n, k, upload(X)).cpu().numpy()
+    rows = [0, 1, 127, 128, 255, 300, 510, 511]
+    ref, absum = oracle.gemm(t, w, n, k, X, rows=rows)
+    say("  worst relative error", check_tol(got[rows], ref, absum, GEMM_TOL, "gemm full"))
+
+
+@pytest.mark.parametrize("t", [G.Q4_K, G.Q6_K])
+@pytest.mark.parametrize("mb", [1, 4, 8])
+def test_gemm_skinny_matches_oracle(t, mb):
+    """M = batch (the skinny-GEMM side of the decode crossover)."""
+    n, k = 1000, 4096
+    w = G.gen_weights(t, n, k, seed=15)
+    X = G.gen_x_f16(mb, k, seed=16)
+    ref, absum = oracle.gemm(t, w, n, k, X)
+    got = q.gemm_prefill(upload(w), t, n, k, upload(X)).cpu().numpy()
+    check_tol(got, ref, absum, GEMM_TOL, "skinny")
+
+
+def test_gemm_k0_writes_zeros():
+    y = torch.full((3, 4), 5.0, device=DEV)
+    w = upload(np.zeros(16, np.uint8))
+    q.gemm_prefill(w[:0], G.Q4_K, 4, 0, torch.zeros((3, 0), dtype=torch.float16, device=DEV), out=y)
+    assert not y.cpu().numpy().any()
+
+
+def test_native_library_loaded():
+    import os
+    maps = open("/proc/self/maps").read()
+    assert os.path.realpath(q.LIB_PATH) in maps
