@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-weight matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none]
+
+A step is one decode pass over the TinyLlama-shaped Q4_0 weight stream:
+22 layers x (q, k, v, o, gate, up, down) = 154 GEMVs at batch 1 on one
+stream, each with a fresh fp32 activation, as one captured HIP graph (one
+submission per token, no host synchronization inside the pass).  Inputs are
+resident in HBM before timing starts.  The 545 MB stream is larger than the
+256 MB last-level cache, so every pass reads the weights from HBM.
+
+Printed: one JSON line with the whole-pass HBM throughput (GB/s), its fraction
+of the 8 TB/s peak, the decode-equivalent tokens/s, the roofline of the
+dominant kernel (the Q4_0 GEMV) from per-launch HIP-event timings, the CPU
+oracle timed on a bounded sample of the same workload, and secondary figures
+for the other workloads (Q8_0 single matrix, Llama-3-8B Q4_K set, 512-token
+prefill GEMMs, Q4_K_M-style mix with a Q6_K LM head at batch 1/4/8).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import qmm_inputs as G  # noqa: E402
+
+METRIC = "quantized GEMV HBM GB/s (% of peak) + decode tok/s equiv; prefill GEMM TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--secondary", choices=["all", "none"], default="all")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU oracle sample")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------- helpers --
+
+class Problem:
+    """One GEMV (or GEMM) with its device buffers and byte/flop counts."""
+
+    def __init__(self, torch, name, t, n, k, w_dev, x_dev, y_dev, kind="gemv"):
+        self.name, self.t, self.n, self.k, self.kind = name, t, n, k, kind
+        self.w, self.x, self.y = w_dev, x_dev, y_dev
+        self.batch = x_dev.shape[0]
+        wbytes = n * G.row_bytes(t, k)
+        if kind == "gemv":
+            # algorithmic bytes: weights + x + y (x re-reads from cache not counted)
+            self.bytes = wbytes + 4 * self.batch * k + 4 * self.batch * n
+            self.flops = 2 * self.batch * n * k
+        else:
+            self.bytes = wbytes + 2 * self.batch * k + 4 * self.batch * n
+            self.flops = 2 * self.batch * n * k
+        self.wbytes = wbytes
+
+    def launch(self, q, stream):
+        if self.kind == "gemv":
+            st = q.lib.qmm_gemv(self.t, self.w.data_ptr(), self.n, self.k, self.x.data_ptr(), self.batch,
+                                self.y.data_ptr(), stream)
+        else:
+            st = q.lib.qmm_gemm_prefill(self.t, self.w.data_ptr(), self.n, self.k, self.x.data_ptr(),
+                                        self.batch, self.y.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError("%s %s: %s" % (self.kind, self.name, q.status_str(st)))
+
+
+def build_weights(torch, cfg, dev="cuda:0"):
+    return [(name, t, n, k, torch.from_numpy(G.gen_weights(t, n, k, seed)).to(dev))
+            for (name, t, n, k, seed) in G.workload(cfg)]
+
+
+def make_gemvs(torch, cfg, weights, batch, dev="cuda:0"):
+    probs = []
+    for i, (name, t, n, k, w) in enumerate(weights):
+        x = torch.from_numpy(G.gen_x(k, batch, G.x_seed(cfg, i))).to(dev)
+        y = torch.empty((batch, n), dtype=torch.float32, device=dev)
+        probs.append(Problem(torch, name, t, n, k, w, x, y))
+    return probs
+
+
+def run_pass(q, probs, stream):
+    for p in probs:
+        p.launch(q, stream)
+
+
+def capture(torch, q, probs):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run_pass(q, probs, torch.cuda.current_stream().cuda_stream)   # warm (outside capture)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run_pass(q, probs, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, steps, warmup):
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_eager(torch, q, probs, steps, warmup):
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        run_pass(q, probs, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run_pass(q, probs, stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def per_launch_times(torch, q, probs, reps):
+    """Kernel durations from HIP events recorded right before and after each
+    launch, on the stream the kernels run on (torch's current stream, which
+    the library launches on).  Returns the summed duration of one pass (s),
+    averaged over reps passes."""
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in probs]
+    total = 0.0
+    for _ in range(reps):
+        for p, (a, b) in zip(probs, ev):
+            a.record()
+            p.launch(q, stream)
+            b.record()
+        torch.cuda.synchronize()
+        total += sum(a.elapsed_time(b) for a, b in ev) * 1e-3
+    return total / reps
+
+
+def cpu_baseline(cfg_probs_host, target_s):
+    """The oracle (plain C, fp64, OpenMP over rows) on a bounded sample of the
+    same workload: whole layers of the decode stream, as many as fit in
+    about target_s seconds."""
+    import oracle
+    nthreads = oracle.max_threads()
+    done_bytes, t_used, layers = 0, 0.0, 0
+    per_layer = 7
+    i = 0
+    while i < len(cfg_probs_host) and (t_used < target_s or layers == 0):
+        chunk = cfg_probs_host[i:i + per_layer]
+        t0 = time.perf_counter()
+        for (t, n, k, w, x) in chunk:
+            oracle.gemv(t, w, n, k, x)
+        t_used += time.perf_counter() - t0
+        done_bytes += sum(n * G.row_bytes(t, k) + 4 * k + 4 * n for (t, n, k, w, x) in chunk)
+        layers += 1
+        i += per_layer
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
+            "sample": "%d of 22 layers (%d GEMVs, %.1f MB of weights) of the same Q4_0 stream, %.1f s"
+                      % (layers, layers * per_layer, done_bytes / 1e6, t_used)}
+
+
+# ------------------------------------------------------------- secondaries --
+
+def sec_cfg1(torch, q, steps, warmup, dev):
+    """Q8_0 2048x2048: rotate over 256 copies (1.14 GB) so caches cannot serve
+    it; also the cache-resident single-call time."""
+    n = k = 2048
+    w0 = torch.from_numpy(G.gen_weights(G.Q8_0, n, k, 1000)).to(dev)
+    x = torch.from_numpy(G.gen_x(k, 1, G.x_seed(1, 0))).to(dev)
+    copies = [w0.clone() for _ in range(256)]
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)
+    probs = [Problem(torch, "w%d" % i, G.Q8_0, n, k, c, x, y) for i, c in enumerate(copies)]
+    g = capture(torch, q, probs)
+    t = time_graph(torch, g, max(2, steps // 4), 2) / len(probs)
+    hot = [Problem(torch, "hot", G.Q8_0, n, k, w0, x, y)] * 256
+    gh = capture(torch, q, hot)
+    th = time_graph(torch, gh, max(2, steps // 4), 2) / 256
+    kt = per_launch_times(torch, q, probs, 1) / len(probs)
+    b = probs[0].bytes
+    del copies, probs, g, gh
+    return {"workload": "Q8_0 2048x2048 GEMV, batch 1, over 256 rotating copies",
+            "us_per_gemv": t * 1e6, "GB_s": b / t / 1e9, "pct_hbm_peak": 100 * b / t / 1e9 / HBM_PEAK_GBS,
+            "kernel_us_event": kt * 1e6,
+            "hot_us_per_gemv_cache_resident": th * 1e6}
+
+
+def sec_stream(torch, q, cfg, weights, batch, steps, warmup, dev, label, with_gemm=False):
+    probs = make_gemvs(torch, cfg, weights, batch, dev)
+    wbytes = sum(p.wbytes for p in probs)
+    tbytes = sum(p.bytes for p in probs)
+    g = capture(torch, q, probs)
+    tg = time_graph(torch, g, steps, warmup)
+    kt = per_launch_times(torch, q, probs, 2)
+    out = {"workload": label, "gemvs": len(probs), "batch": batch, "weight_bytes": wbytes,
+           "ms_per_pass": tg * 1e3, "GB_s": tbytes / tg / 1e9, "pct_hbm_peak": 100 * tbytes / tg / 1e9 / HBM_PEAK_GBS,
+           "decode_tok_s": batch / tg, "kernel_sum_ms": kt * 1e3, "GB_s_kernel_sum": tbytes / kt / 1e9}
+    del g
+    if with_gemm:
+        # the same pass as a skinny GEMM (fp16 activations, M = batch)
+        gp = []
+        for p in probs:
+            X = torch.from_numpy(G.gen_x_f16(batch, p.k, 77)).to(dev)
+            gp.append(Problem(torch, p.name, p.t, p.n, p.k, p.w, X, p.y, kind="gemm"))
+        gg = capture(torch, q, gp)
+        tgg = time_graph(torch, gg, steps, warmup)
+        out["skinny_gemm_ms_per_pass"] = tgg * 1e3
+        out["skinny_gemm_tok_s"] = batch / tgg
+        del gg, gp
+    del probs
+    torch.cuda.empty_cache()
+    return out
+
+
+def sec_prefill(torch, q, steps, warmup, dev):
+    res = {}
+    m = G.PREFILL_M
+    for name, t, n, k, seed in G.workload(4):
+        w = torch.from_numpy(G.gen_weights(t, n, k, seed)).to(dev)
+        probs = []
+        for c in range(G.PREFILL_CHUNKS):
+            X = torch.from_numpy(G.gen_x_f16(m, k, G.x_seed(4, 10 * c + len(res)))).to(dev)
+            Y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            probs.append(Problem(torch, "%s.c%d" % (name, c), t, n, k, w, X, Y, kind="gemm"))
+        g = capture(torch, q, probs)
+        tg = time_graph(torch, g, steps, warmup)
+        kt = per_launch_times(torch, q, probs, 2)
+        flops = sum(p.flops for p in probs)
+        res[name] = {"shape": "4 x (%d x %d x %d)" % (m, n, k), "ms_4_chunks": tg * 1e3,
+                     "TFLOP_s": flops / tg / 1e12, "pct_fp16_peak": 100 * flops / tg / 1e12 / FP16_PEAK_TFLOPS,
+                     "kernel_us_per_chunk": kt / len(probs) * 1e6,
+                     "TFLOP_s_kernel": flops / kt / 1e12}
+        del g, probs, w
+    torch.cuda.empty_cache()
+    return res
+
+
+# -------------------------------------------------------------------- main --
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(GEMV rows / GEMM columns would shard across GPUs; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dequant_matmul_amd as q
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log("device:", torch.cuda.get_device_name(0), "| lib:", q.version())
+
+    # primary: TinyLlama-shaped Q4_0 decode stream, batch 1
+    log("generating the Q4_0 decode stream (154 GEMVs)")
+    host = []
+    probs = []
+    for i, (name, t, n, k, seed) in enumerate(G.workload(2)):
+        w = G.gen_weights(t, n, k, seed)
+        x = G.gen_x(k, 1, G.x_seed(2, i))
+        host.append((t, n, k, w, x))
+        probs.append(Problem(torch, name, t, n, k, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev),
+                             torch.empty((1, n), dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+    tot_bytes = sum(p.bytes for p in probs)
+    w_bytes = sum(p.wbytes for p in probs)
+    g = capture(torch, q, probs)
+    log("timing %d graph replays after %d warmup" % (args.steps, args.warmup))
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / args.steps
+    value = tot_bytes / step_s / 1e9
+
+    # dominant kernel: per-launch event durations over the same pass
+    kt = per_launch_times(torch, q, probs, max(3, args.steps // 4))
+    achieved = tot_bytes / kt / 1e9
+    eager_s = time_eager(torch, q, probs, max(3, args.steps // 2), 2)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "TinyLlama-shaped Q4_0 decode weight stream: 22 layers x "
+                               "(q 2048x2048, k/v 256x2048, o 2048x2048, gate/up 5632x2048, down 2048x5632) "
+                               "= 154 GEMVs, batch 1, one HIP graph per pass",
+                   "gemvs": len(probs), "batch": 1, "weight_bytes": w_bytes, "algorithmic_bytes": tot_bytes},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "decode_tok_s": round(1.0 / step_s, 1),
+        "eager_ms_per_step": round(eager_s * 1e3, 4),
+        "kernel_sum_ms_per_step": round(kt * 1e3, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_kernel<Q4_0, batch 1, 2 rows/wave>",
+                     "avg_launch_us": round(kt / len(probs) * 1e6, 3),
+                     "bytes_per_launch": tot_bytes / len(probs)},
+    }
+    del g
+
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline (~%.0f s)" % args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(host, args.cpu_seconds)
+    del host
+
+    if args.secondary == "all":
+        sec = {}
+        log("secondary: Q8_0 single matrix")
+        sec["q8_0_2048"] = sec_cfg1(torch, q, args.steps, args.warmup, dev)
+        del probs
+        torch.cuda.empty_cache()
+        log("secondary: Llama-3-8B Q4_K set")
+        wts = build_weights(torch, 3, dev)
+        sec["llama3_8b_q4_k"] = sec_stream(torch, q, 3, wts, 1, args.steps, args.warmup, dev,
+                                           "Llama-3-8B-shaped Q4_K, 224 GEMVs, batch 1")
+        del wts
+        torch.cuda.empty_cache()
+        log("secondary: prefill GEMMs")
+        sec["prefill_512"] = sec_prefill(torch, q, args.steps, args.warmup, dev)
+        log("secondary: Q4_K_M-style mix weights")
+        wts = build_weights(torch, 5, dev)
+        for b in (1, 4, 8):
+            log("secondary: Q4_K_M-style mix, batch", b)
+            sec["q4_k_m_mix_b%d" % b] = sec_stream(
+                torch, q, 5, wts, b, max(3, args.steps // 2), 2, dev,
+                "Q4_K_M-style mix (v, down, LM head 128256x4096 in Q6_K), 225 GEMVs, batch %d" % b,
+                with_gemm=True)
+        del wts
+        line["secondary"] = sec
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,6 +18,11 @@ namespace qmm {
 
 enum : int { T_Q4_0 = 0, T_Q8_0 = 1, T_Q4_K = 2, T_Q6_K = 3 };
 
+// Native 128-bit vectors.  (HIP's uint4 / float4 are structs whose copies
+// lower to memcpy, which can keep arrays of them in scratch memory.)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int T> struct Fmt;
 template <> struct Fmt<T_Q4_0> { static constexpr int BE = 32, BB = 18; };
 template <> struct Fmt<T_Q8_0> { static constexpr int BE = 32, BB = 34; };
@@ -63,12 +68,28 @@ __device__ __forceinline__ void wave_lds_sync()
 }
 
 // Sum over the 64 lanes of a wavefront; every lane receives the total.
+// Within each 16-lane row: DPP swaps (quad_perm [1,0,3,2], [2,3,0,1],
+// row_half_mirror, row_mirror) -- register-to-register, no LDS round trip;
+// then the four row sums are read with v_readlane and added.
+__device__ __forceinline__ float dpp_f(float v, int ctrl)
+{
+    return __builtin_bit_cast(float, ctrl == 0xB1 ? __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)
+                                 : ctrl == 0x4E ? __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)
+                                 : ctrl == 0x141 ? __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)
+                                                 : __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f(v, 0xB1);    // lanes 1,0,3,2 of each quad
+    v += dpp_f(v, 0x4E);    // lanes 2,3,0,1 of each quad
+    v += dpp_f(v, 0x141);   // mirror within each half-row of 8
+    v += dpp_f(v, 0x140);   // mirror within the row of 16
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Q4_K: 6-bit scale and min of sub-block j from the 3 dwords holding the 12

@@ -74,9 +74,9 @@ __device__ __forceinline__ void gload_group(const uint8_t *row, int g, GRaw<T> &
     } else if constexpr (T == T_Q4_K) {
         const uint8_t *blk = row + (int64_t)(g >> 3) * F::BB;   // 16-byte aligned
         const int j = g & 7;
-        const uint4 h = *(const uint4 *)blk;
-        const uint4 c0 = *(const uint4 *)(blk + 16 + 32 * (j >> 1));
-        const uint4 c1 = *(const uint4 *)(blk + 32 + 32 * (j >> 1));
+        const u32x4 h = *(const u32x4 *)blk;
+        const u32x4 c0 = *(const u32x4 *)(blk + 16 + 32 * (j >> 1));
+        const u32x4 c1 = *(const u32x4 *)(blk + 32 + 32 * (j >> 1));
         r.hd[0] = h.x; r.hd[1] = h.y; r.hd[2] = h.z; r.hd[3] = h.w;
         r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
         r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
@@ -171,10 +171,10 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
     // per-thread load assignment
     // X tile: 128 rows x 16 chunks of 8 halves -> 8 chunks per thread
     // W tile: 128 rows x 4 groups -> 2 items per thread (row = tid/2 + 0/64... )
-    uint4 xa[8];
+    u32x4 xa[8];
     GRaw<T> wr[GITEMS];
 
-    auto load_step = [&](int kt) {
+    auto load_step = [&](int kt) __attribute__((always_inline)) {
         const int kb = kt * GBK;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -182,9 +182,9 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
             const int r = c >> 4, ch = c & 15;
             const int gm = m0 + r, gk = kb + 8 * ch;
             if (gm < m && gk < k)
-                xa[i] = *(const uint4 *)(x + (int64_t)gm * k + gk);
+                xa[i] = *(const u32x4 *)(x + (int64_t)gm * k + gk);
             else
-                xa[i] = make_uint4(0, 0, 0, 0);
+                xa[i] = u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int it = 0; it < GITEMS; ++it) {
@@ -196,13 +196,13 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
         }
     };
 
-    auto store_step = [&](int kt) {
+    auto store_step = [&](int kt) __attribute__((always_inline)) {
         const int kb = kt * GBK;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int c = tid + 256 * i;
             const int r = c >> 4, ch = c & 15;
-            *(uint4 *)(As + r * GLD + 8 * ch) = xa[i];
+            *(u32x4 *)(As + r * GLD + 8 * ch) = xa[i];
         }
 #pragma unroll
         for (int it = 0; it < GITEMS; ++it) {
@@ -216,11 +216,11 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
 #pragma unroll
                 for (int i = 0; i < 16; ++i) o[i] = 0u;
             }
-            uint4 *dst = (uint4 *)(Bs + r * GLD + 32 * gl);
-            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-            dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-            dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
+            u32x4 *dst = (u32x4 *)(Bs + r * GLD + 32 * gl);
+            dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+            dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+            dst[2] = u32x4{o[8], o[9], o[10], o[11]};
+            dst[3] = u32x4{o[12], o[13], o[14], o[15]};
         }
     };
 

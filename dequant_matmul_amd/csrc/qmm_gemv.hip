@@ -6,39 +6,87 @@
 // pipeline" (decode) says the same: reading the weight tensors dominates.
 //
 // gfx950 design
-//   - A workgroup is 4 wavefronts; each wavefront owns R consecutive rows
-//     and walks the whole K range in segments of 64 lane-units.
-//   - Weights: for each segment and row the wave copies the row's bytes with
-//     fully coalesced 16-byte loads (64 lanes x 16 B contiguous) into a
-//     wave-private LDS buffer; each lane then reads its own unit (one Q8_0 /
-//     Q4_0 block, or a 64-element quarter of a Q4_K / Q6_K super-block) from
-//     LDS.  Blocks of 34, 18 and 210 bytes are only 2-byte aligned, so lanes
-//     read aligned dwords and realign them with v_alignbyte_b32.
-//   - Activations: the segment of x (all batches) is staged once per
-//     workgroup in LDS, padded by 4 floats per unit so that the 64 lanes'
-//     128-bit reads do not collide on banks.  A lane reads each x value once
-//     per segment and applies it to all R rows of its wavefront.
-//   - Codes are converted with one mask per dword plus v_cvt_f32_ubyteN (or
-//     the sign-extending SDWA convert for Q8_0) and accumulated in fp32 per
-//     block / sub-block; the scale is applied once per (sub-)block.  Constant
-//     code offsets (-8, -32, -dmin*m) are applied through the per-sub-block
-//     sum of x, which every row of the wave shares.
-//   - The per-lane partial sums are reduced across the wavefront with
-//     cross-lane shuffles; lane 0 writes y.
+//   - Work is split into lane-units: one Q8_0 / Q4_0 block (32 elements) or a
+//     64-element quarter of a Q4_K / Q6_K super-block.  A segment is 64
+//     consecutive units of a row, i.e. one unit per lane of a wavefront.
+//   - Weights are read with 16-byte loads.  Q4_K blocks (144 B) keep 16-byte
+//     alignment, so each lane loads its unit straight into registers.  Blocks
+//     of 34, 18 and 210 bytes are only 2-byte aligned: the wavefront copies the
+//     row segment into LDS with fully coalesced loads (64 lanes x 16 B
+//     contiguous) and each lane reads its unit back with aligned dword reads,
+//     realigned in registers with v_alignbyte_b32.
+//   - Codes are converted with one mask per dword plus v_cvt_f32_ubyteN (the
+//     sign-extending SDWA convert for Q8_0) and accumulated in fp32 per block
+//     or sub-block; the scale is applied once per (sub-)block.  Constant code
+//     offsets (-8, -32, -dmin m) go through the per-sub-block sum of x, which
+//     all rows share.
+//   - Per-lane partial sums are reduced across the wavefront with cross-lane
+//     shuffles; lane 0 writes y.
+//   - Loads are issued without branches (out-of-range lanes read a valid
+//     address and discard it): the compiler otherwise sinks a predicated load
+//     into its branch and waits for it at once, serializing the memory
+//     round trips.
+//
+// Kernels
+//   gemv2_kernel  batch 1, k <= one segment (every projection except the
+//                 wide-k down projections): each lane holds its slice of x in
+//                 registers, waves are independent and persistent, and the
+//                 weight bytes of the next row group are in flight while the
+//                 current one is decoded.
+//   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
+//                 once per workgroup; otherwise as gemv2.
+//   gemv_kernel   batch 2..8 (and unaligned rows): x segment and weight
+//                 segments staged in LDS per workgroup.
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
 namespace qmm {
 
-template <int T> struct GemvUnit;
-// UE: elements per lane-unit; a segment is 64 units.
-template <> struct GemvUnit<T_Q4_0> { static constexpr int UE = 32; };
-template <> struct GemvUnit<T_Q8_0> { static constexpr int UE = 32; };
-template <> struct GemvUnit<T_Q4_K> { static constexpr int UE = 64; };
-template <> struct GemvUnit<T_Q6_K> { static constexpr int UE = 64; };
+// ------------------------------------------------------------ unit layout --
 
-// Read NDW dwords starting at an arbitrary even byte offset of an LDS byte
-// buffer (given as dwords), realigning in registers.
+template <int T> struct GemvUnit;
+// UE: elements per lane-unit; NRUN: runs of 4 consecutive elements per unit.
+template <> struct GemvUnit<T_Q4_0> { static constexpr int UE = 32, NRUN = 8; };
+template <> struct GemvUnit<T_Q8_0> { static constexpr int UE = 32, NRUN = 8; };
+template <> struct GemvUnit<T_Q4_K> { static constexpr int UE = 64, NRUN = 16; };
+template <> struct GemvUnit<T_Q6_K> { static constexpr int UE = 64, NRUN = 16; };
+
+// Element (relative to the segment start) of the first element of run j of
+// lane-unit u.  The run order is the order in which unit_dot consumes x.
+template <int T>
+__device__ __forceinline__ int run_elem(int u, int j)
+{
+    if constexpr (T == T_Q8_0) {
+        return 32 * u + 4 * j;                                // codes 4j..4j+3
+    } else if constexpr (T == T_Q4_0) {
+        return 32 * u + (j < 4 ? 4 * j : 16 + 4 * (j - 4));   // low nibbles, then high
+    } else if constexpr (T == T_Q4_K) {
+        return 64 * u + (j < 8 ? 4 * j : 32 + 4 * (j - 8));   // sub-block 2p, then 2p+1
+    } else {
+        // u = 4 sb + 2 h + hf: elements 128h + 32g + 16hf + i of super-block sb,
+        // run j = 4g + i/4
+        const int sb = u >> 2, h = (u >> 1) & 1, hf = u & 1;
+        return 256 * sb + 128 * h + 16 * hf + 32 * (j >> 2) + 4 * (j & 3);
+    }
+}
+
+// Padded LDS index of element e of an x segment: 4 floats of padding per
+// lane-unit, so the 64 lanes' 128-bit reads do not collide on banks.
+template <int UE>
+__device__ __forceinline__ int xpad(int e)
+{
+    return e + (e / UE) * 4;
+}
+
+// Raw bytes of one lane-unit of one row.
+template <int T> struct URaw;
+template <> struct URaw<T_Q8_0> { uint32_t d; uint32_t c[8]; };
+template <> struct URaw<T_Q4_0> { uint32_t d; uint32_t c[4]; };
+template <> struct URaw<T_Q4_K> { u32x4 hd; uint32_t c[8]; };
+template <> struct URaw<T_Q6_K> { uint32_t qa[4], qb[4], qh[4], sc[2], d; };
+
+// Read NDW dwords starting at an even byte offset of an LDS byte buffer
+// (addressed as dwords), realigning in registers.
 template <int NDW>
 __device__ __forceinline__ void lds_read_bytes(const uint32_t *lds, uint32_t byte_off, uint32_t *out)
 {
@@ -57,23 +105,52 @@ __device__ __forceinline__ uint32_t lds_read_u16(const uint32_t *lds, uint32_t b
     return (lds[byte_off >> 2] >> (8u * (byte_off & 2u))) & 0xffffu;
 }
 
-// Padded LDS index of element e of the x segment (4 floats of padding per
-// lane-unit of UE elements).
-template <int UE>
-__device__ __forceinline__ int xpad(int e)
+// Unit u of a row segment staged in LDS (raw bytes from offset 0).
+template <int T>
+__device__ __forceinline__ void raw_from_lds(const uint32_t *seg, int u, URaw<T> &r)
 {
-    return e + (e / UE) * 4;
+    if constexpr (T == T_Q8_0) {
+        const uint32_t off = 34u * u;               // fp16 d, then 32 int8 codes
+        r.d = lds_read_u16(seg, off);
+        lds_read_bytes<8>(seg, off + 2, r.c);
+    } else if constexpr (T == T_Q4_0) {
+        const uint32_t off = 18u * u;               // fp16 d, then 16 code bytes
+        r.d = lds_read_u16(seg, off);
+        lds_read_bytes<4>(seg, off + 2, r.c);
+    } else if constexpr (T == T_Q4_K) {
+        const int p = u & 3;
+        const uint32_t *blk = seg + 36 * (u >> 2);  // 144 B = 36 dwords
+        r.hd = *(const u32x4 *)blk;
+        const u32x4 c0 = *(const u32x4 *)(blk + 4 + 8 * p);
+        const u32x4 c1 = *(const u32x4 *)(blk + 8 + 8 * p);
+        r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
+        r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
+    } else {
+        const int sb = u >> 2, h = (u >> 1) & 1, hf = u & 1, l0 = 16 * hf;
+        const uint32_t off = 210u * sb;
+        lds_read_bytes<4>(seg, off + 64 * h + l0, r.qa);        // ql, g = 0 (low) / 2 (high)
+        lds_read_bytes<4>(seg, off + 64 * h + 32 + l0, r.qb);   // ql, g = 1 (low) / 3 (high)
+        lds_read_bytes<4>(seg, off + 128 + 32 * h + l0, r.qh);  // qh, bits 2g
+        lds_read_bytes<2>(seg, off + 192 + 8 * h, r.sc);        // scales 8h .. 8h+7
+        r.d = lds_read_u16(seg, off + 208);
+    }
 }
 
-template <int B>
-__device__ __forceinline__ void load_x4(const float *xs, int stride, int idx, float4 *v)
+// Q4_K unit u straight from global memory (super-blocks are 16-byte aligned).
+__device__ __forceinline__ void raw_from_global_q4k(const uint8_t *seg, int u, URaw<T_Q4_K> &r)
 {
-#pragma unroll
-    for (int b = 0; b < B; ++b)
-        v[b] = *(const float4 *)(xs + b * stride + idx);
+    const uint8_t *blk = seg + 144 * (u >> 2);
+    const int p = u & 3;
+    r.hd = *(const u32x4 *)blk;
+    const u32x4 c0 = *(const u32x4 *)(blk + 16 + 32 * p);
+    const u32x4 c1 = *(const u32x4 *)(blk + 32 + 32 * p);
+    r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
+    r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
 }
 
-__device__ __forceinline__ float dot4_u(uint32_t q, const float4 &x, float acc)
+// ------------------------------------------------------------- unit dot --
+
+__device__ __forceinline__ float dot4_u(uint32_t q, const f32x4 &x, float acc)
 {
     acc = __builtin_fmaf(ub0(q), x.x, acc);
     acc = __builtin_fmaf(ub1(q), x.y, acc);
@@ -82,7 +159,7 @@ __device__ __forceinline__ float dot4_u(uint32_t q, const float4 &x, float acc)
     return acc;
 }
 
-__device__ __forceinline__ float dot4_s(uint32_t q, const float4 &x, float acc)
+__device__ __forceinline__ float dot4_s(uint32_t q, const f32x4 &x, float acc)
 {
     acc = __builtin_fmaf(sb0(q), x.x, acc);
     acc = __builtin_fmaf(sb1(q), x.y, acc);
@@ -91,55 +168,53 @@ __device__ __forceinline__ float dot4_s(uint32_t q, const float4 &x, float acc)
     return acc;
 }
 
-__device__ __forceinline__ float sum4(const float4 &v) { return (v.x + v.y) + (v.z + v.w); }
+__device__ __forceinline__ float sum4(const f32x4 &v) { return (v.x + v.y) + (v.z + v.w); }
 
-// One lane-unit for R rows and B batches.  wst: this wave's staged row
-// segments (R of them, each SEGB bytes).  xs: staged x segment.  Adds each
-// (row, batch) contribution to acc.
-template <int T, int B, int R, int SEGB, int XS>
-__device__ __forceinline__ void gemv_unit(const uint32_t *wst, const float *xs, int lane, float (&acc)[R][B])
+// x of run j for batch b, from LDS (padded layout) ...
+template <int T, int XS>
+struct XFromLds {
+    const float *xs;
+    int u;
+    __device__ __forceinline__ f32x4 operator()(int j, int b) const
+    {
+        return *(const f32x4 *)(xs + b * XS + xpad<GemvUnit<T>::UE>(run_elem<T>(u, j)));
+    }
+};
+
+// ... or from registers (batch 1).
+template <int T>
+struct XFromRegs {
+    const f32x4 *xr;
+    __device__ __forceinline__ f32x4 operator()(int j, int) const { return xr[j]; }
+};
+
+// Contribution of lane-unit u of R rows to acc[r][b].
+template <int T, int B, int R, class XG>
+__device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const XG &xg, float (&acc)[R][B])
 {
-    constexpr int UE = GemvUnit<T>::UE;
-    const int xb = xpad<UE>(lane * UE);   // padded start of this lane's elements
     if constexpr (T == T_Q8_0) {
-        // unit = one block: fp16 d at byte 34*lane, 32 int8 codes after it
-        float d[R];
-        uint32_t c[R][8];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint32_t off = 34u * lane;
-            d[r] = h2f(lds_read_u16(wst + r * (SEGB / 4), off));
-            lds_read_bytes<8>(wst + r * (SEGB / 4), off + 2, c[r]);
-        }
         float s[R][B];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int b = 0; b < B; ++b) s[r][b] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float4 xv[B];
-            load_x4<B>(xs, XS, xb + 4 * i, xv);
+        for (int j = 0; j < 8; ++j) {
+            f32x4 xv[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) xv[b] = xg(j, b);
 #pragma unroll
             for (int r = 0; r < R; ++r)
 #pragma unroll
-                for (int b = 0; b < B; ++b) s[r][b] = dot4_s(c[r][i], xv[b], s[r][b]);
+                for (int b = 0; b < B; ++b) s[r][b] = dot4_s(raw[r].c[j], xv[b], s[r][b]);
         }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d[r], s[r][b], acc[r][b]);
-    } else if constexpr (T == T_Q4_0) {
-        // unit = one block: fp16 d at byte 18*lane, 16 code bytes after it;
-        // low nibble of byte i = element i, high nibble = element 16+i
-        float d[R];
-        uint32_t c[R][4];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const uint32_t off = 18u * lane;
-            d[r] = h2f(lds_read_u16(wst + r * (SEGB / 4), off));
-            lds_read_bytes<4>(wst + r * (SEGB / 4), off + 2, c[r]);
+            const float d = h2f(raw[r].d);
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d, s[r][b], acc[r][b]);
         }
+    } else if constexpr (T == T_Q4_0) {
         float slo[R][B], shi[R][B], xsum[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -149,15 +224,17 @@ __device__ __forceinline__ void gemv_unit(const uint32_t *wst, const float *xs, 
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float4 xl[B], xh[B];
-            load_x4<B>(xs, XS, xb + 4 * i, xl);
-            load_x4<B>(xs, XS, xb + 16 + 4 * i, xh);
+            f32x4 xl[B], xh[B];
 #pragma unroll
-            for (int b = 0; b < B; ++b) xsum[b] += sum4(xl[b]) + sum4(xh[b]);
+            for (int b = 0; b < B; ++b) {
+                xl[b] = xg(i, b);
+                xh[b] = xg(4 + i, b);
+                xsum[b] += sum4(xl[b]) + sum4(xh[b]);
+            }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t lo = opaque(c[r][i] & 0x0f0f0f0fu);
-                const uint32_t hi = opaque(c[r][i] & 0xf0f0f0f0u);  // 16 * code
+                const uint32_t lo = opaque(raw[r].c[i] & 0x0f0f0f0fu);
+                const uint32_t hi = opaque(raw[r].c[i] & 0xf0f0f0f0u);   // 16 * code
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     slo[r][b] = dot4_u(lo, xl[b], slo[r][b]);
@@ -165,34 +242,29 @@ __device__ __forceinline__ void gemv_unit(const uint32_t *wst, const float *xs, 
                 }
             }
         }
-        // d * sum (q - 8) x = d * (slo + shi/16 - 8 * sum x)
+        // d * sum (q - 8) x = d * (slo + shi/16 - 8 sum x)
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int r = 0; r < R; ++r) {
+            const float d = h2f(raw[r].d);
 #pragma unroll
             for (int b = 0; b < B; ++b) {
                 const float t = __builtin_fmaf(shi[r][b], 0.0625f, slo[r][b]);
-                acc[r][b] = __builtin_fmaf(d[r], __builtin_fmaf(-8.f, xsum[b], t), acc[r][b]);
+                acc[r][b] = __builtin_fmaf(d, __builtin_fmaf(-8.f, xsum[b], t), acc[r][b]);
             }
+        }
     } else if constexpr (T == T_Q4_K) {
-        // unit = (super-block sb = lane/4, code group p = lane%4): sub-blocks
-        // 2p (low nibbles) and 2p+1 (high nibbles) of 32 elements each
-        const int sb = lane >> 2, p = lane & 3;
+        // unit = (super-block, code group p = u % 4): sub-block 2p in the low
+        // nibbles, 2p+1 in the high nibbles
+        const int p = u & 3;
         float dsc0[R], dsc1[R], dm0[R], dm1[R];
-        uint32_t c[R][8];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const uint32_t *blk = wst + r * (SEGB / 4) + sb * 36;   // 144 B = 36 dwords
-            const uint4 hd = *(const uint4 *)blk;
-            const uint4 c0 = *(const uint4 *)(blk + 4 + 8 * p);
-            const uint4 c1 = *(const uint4 *)(blk + 8 + 8 * p);
-            c[r][0] = c0.x; c[r][1] = c0.y; c[r][2] = c0.z; c[r][3] = c0.w;
-            c[r][4] = c1.x; c[r][5] = c1.y; c[r][6] = c1.z; c[r][7] = c1.w;
             uint32_t sc0, m0, sc1, m1;
-            q4k_scale_min(hd.y, hd.z, hd.w, 2 * p, sc0, m0);
-            q4k_scale_min(hd.y, hd.z, hd.w, 2 * p + 1, sc1, m1);
-            const float d = h2f(hd.x & 0xffffu), dmin = h2f(hd.x >> 16);
+            q4k_scale_min(raw[r].hd.y, raw[r].hd.z, raw[r].hd.w, 2 * p, sc0, m0);
+            q4k_scale_min(raw[r].hd.y, raw[r].hd.z, raw[r].hd.w, 2 * p + 1, sc1, m1);
+            const float d = h2f(raw[r].hd.x & 0xffffu), dmin = h2f(raw[r].hd.x >> 16);
             dsc0[r] = d * (float)sc0;
-            dsc1[r] = d * (float)sc1 * 0.0625f;  // high nibbles convert as 16 q
+            dsc1[r] = d * (float)sc1 * 0.0625f;   // high nibbles convert as 16 q
             dm0[r] = dmin * (float)m0;
             dm1[r] = dmin * (float)m1;
         }
@@ -205,18 +277,18 @@ __device__ __forceinline__ void gemv_unit(const uint32_t *wst, const float *xs, 
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float4 xl[B], xh[B];
-            load_x4<B>(xs, XS, xb + 4 * i, xl);
-            load_x4<B>(xs, XS, xb + 32 + 4 * i, xh);
+            f32x4 xl[B], xh[B];
 #pragma unroll
             for (int b = 0; b < B; ++b) {
+                xl[b] = xg(i, b);
+                xh[b] = xg(8 + i, b);
                 x0[b] += sum4(xl[b]);
                 x1[b] += sum4(xh[b]);
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t lo = opaque(c[r][i] & 0x0f0f0f0fu);
-                const uint32_t hi = opaque(c[r][i] & 0xf0f0f0f0u);
+                const uint32_t lo = opaque(raw[r].c[i] & 0x0f0f0f0fu);
+                const uint32_t hi = opaque(raw[r].c[i] & 0xf0f0f0f0u);
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     s0[r][b] = dot4_u(lo, xl[b], s0[r][b]);
@@ -235,40 +307,27 @@ __device__ __forceinline__ void gemv_unit(const uint32_t *wst, const float *xs, 
                 acc[r][b] += t;
             }
     } else {  // Q6_K
-        // unit = (super-block sb = lane/4, half h, l-range l0..l0+15): for
-        // g = 0..3 the 16 elements 128h + 32g + l0 + i, i.e. sub-block
-        // 8h + 2g + (l0/16); their low nibbles sit in ql[64h + l0 + i]
-        // (g = 0 low, g = 2 high) and ql[64h + 32 + l0 + i] (g = 1 low,
-        // g = 3 high), their high bits at bit 2g of qh[32h + l0 + i].
-        const int sb = lane >> 2, u = lane & 3, h = u >> 1, hf = u & 1, l0 = 16 * hf;
+        // unit = (super-block, half h, l-range 16 hf .. 16 hf + 15): for each
+        // g the 16 elements 128h + 32g + 16hf + i belong to sub-block
+        // 8h + 2g + hf; low nibble in ql (g = 0/2 in qa, 1/3 in qb), high bits
+        // at bit 2g of qh
+        const int hf = u & 1;
         float dsc[R][4];
-        uint32_t qa[R][4], qb[R][4], qh[R][4];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const uint32_t *rw = wst + r * (SEGB / 4);
-            const uint32_t off = 210u * sb;
-            lds_read_bytes<4>(rw, off + 64 * h + l0, qa[r]);
-            lds_read_bytes<4>(rw, off + 64 * h + 32 + l0, qb[r]);
-            lds_read_bytes<4>(rw, off + 128 + 32 * h + l0, qh[r]);
-            uint32_t sc[2];
-            lds_read_bytes<2>(rw, off + 192 + 8 * h, sc);
-            const float d = h2f(lds_read_u16(rw, off + 208));
+            const float d = h2f(raw[r].d);
             const uint32_t sh = 8u * hf;
-            dsc[r][0] = d * (float)(int8_t)(sc[0] >> sh);          // scale 8h + hf
-            dsc[r][1] = d * (float)(int8_t)(sc[0] >> (16 + sh));   // scale 8h + 2 + hf
-            dsc[r][2] = d * (float)(int8_t)(sc[1] >> sh);          // scale 8h + 4 + hf
-            dsc[r][3] = d * (float)(int8_t)(sc[1] >> (16 + sh));   // scale 8h + 6 + hf
+            dsc[r][0] = d * (float)(int8_t)(raw[r].sc[0] >> sh);          // scale 8h + hf
+            dsc[r][1] = d * (float)(int8_t)(raw[r].sc[0] >> (16 + sh));   // scale 8h + 2 + hf
+            dsc[r][2] = d * (float)(int8_t)(raw[r].sc[1] >> sh);          // scale 8h + 4 + hf
+            dsc[r][3] = d * (float)(int8_t)(raw[r].sc[1] >> (16 + sh));   // scale 8h + 6 + hf
         }
-        // element offset of (g, i) inside this lane's unit in the padded x
-        // layout: the unit's elements are the 4 runs 128h + 32g + l0 + i of
-        // super-block sb, i.e. segment elements 256 sb + 128 h + 32 g + l0 + i
-        const int ebase = 256 * sb + 128 * h + l0;
-        float s[R][B][4], xg[B][4];
+        float s[R][B][4], xgs[B][4];
 #pragma unroll
         for (int b = 0; b < B; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                xg[b][g] = 0.f;
+                xgs[b][g] = 0.f;
 #pragma unroll
                 for (int r = 0; r < R; ++r) s[r][b][g] = 0.f;
             }
@@ -276,13 +335,15 @@ __device__ __forceinline__ void gemv_unit(const uint32_t *wst, const float *xs, 
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                float4 xv[B];
-                load_x4<B>(xs, XS, xpad<64>(ebase + 32 * g + 4 * i), xv);
+                f32x4 xv[B];
 #pragma unroll
-                for (int b = 0; b < B; ++b) xg[b][g] += sum4(xv[b]);
+                for (int b = 0; b < B; ++b) {
+                    xv[b] = xg(4 * g + i, b);
+                    xgs[b][g] += sum4(xv[b]);
+                }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint32_t a = qa[r][i], bq = qb[r][i], hb = qh[r][i];
+                    const uint32_t a = raw[r].qa[i], bq = raw[r].qb[i], hb = raw[r].qh[i];
                     uint32_t q;
                     if (g == 0) q = (a & 0x0f0f0f0fu) | ((hb & 0x03030303u) << 4);
                     else if (g == 1) q = (bq & 0x0f0f0f0fu) | ((hb & 0x0c0c0c0cu) << 2);
@@ -301,12 +362,214 @@ __device__ __forceinline__ void gemv_unit(const uint32_t *wst, const float *xs, 
                 float t = 0.f;
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    t = __builtin_fmaf(dsc[r][g], __builtin_fmaf(-32.f, xg[b][g], s[r][b][g]), t);
+                    t = __builtin_fmaf(dsc[r][g], __builtin_fmaf(-32.f, xgs[b][g], s[r][b][g]), t);
                 acc[r][b] += t;
             }
     }
 }
 
+// ------------------------------------------------- row-segment staging --
+
+// Prefetch of R row segments into registers (16-byte chunks, unconditional:
+// chunks past the data read offset 0 of w instead) and their store to LDS.
+template <int T, int R>
+struct SegStage {
+    static constexpr int UE = GemvUnit<T>::UE;
+    static constexpr int SEGE = 64 * UE;
+    static constexpr int SEGB = SEGE / Fmt<T>::BE * Fmt<T>::BB;
+    static constexpr int CPR = SEGB / 16;                  // chunks per full row segment
+    static constexpr int RS = SEGB / 4 + 4;                // LDS row stride (dwords)
+    static constexpr int NCH = (R * CPR + 63) / 64;        // chunks per lane
+    static constexpr int LDS_DW = R * RS + 256;            // + 64 dummy 16-byte slots
+    u32x4 pf[NCH];
+
+    __device__ __forceinline__ void load(const uint8_t *w, int64_t rb, int n, int row0, int seg, int cpr, int lane)
+    {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = lane + 64 * i;
+            const int jr = c / CPR, off = c - jr * CPR;
+            const int row = row0 + jr;
+            const bool ok = jr < R && off < cpr && row < n;
+            const int64_t o = ok ? (int64_t)row * rb + (int64_t)seg * SEGB + 16 * off : 0;
+            pf[i] = *(const u32x4 *)(w + o);
+        }
+    }
+    __device__ __forceinline__ void store(uint32_t *ws, int lane) const
+    {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const int c = lane + 64 * i;
+            const int jr = c / CPR, off = c - jr * CPR;
+            const int idx = jr < R ? jr * RS + 4 * off : R * RS + 4 * lane;
+            *(u32x4 *)(ws + idx) = pf[i];
+        }
+    }
+};
+
+template <int R>
+__device__ __forceinline__ void reduce_store(float (&acc)[R][1], int row0, int n, int lane, float *y)
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const float v = wave_sum(acc[r][0]);
+        const int row = row0 + r;
+        if (lane == 0 && row < n)
+            y[row] = v;
+        acc[r][0] = 0.f;
+    }
+}
+
+// --------------------------------------------------------------- gemv2 --
+// Batch 1, k <= one segment, x in registers, independent persistent waves.
+template <int T, int R>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
+gemv2_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
+             float *__restrict__ y)
+{
+    constexpr int UE = GemvUnit<T>::UE, NRUN = GemvUnit<T>::NRUN;
+    using S = SegStage<T, R>;
+    constexpr bool DIRECT = (T == T_Q4_K);
+    __shared__ __attribute__((aligned(16))) uint32_t ws[DIRECT ? 4 : 4 * S::LDS_DW];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gw = blockIdx.x * 4 + wave, tw = gridDim.x * 4;
+    const int nrg = (n + R - 1) / R;
+    const int nit = gw < nrg ? (nrg - gw + tw - 1) / tw : 0;
+    const bool active = lane < k / UE;
+    const int cpr = k / Fmt<T>::BE * Fmt<T>::BB / 16;
+
+    // this lane's slice of x
+    f32x4 xr[NRUN];
+#pragma unroll
+    for (int j = 0; j < NRUN; ++j)
+        xr[j] = *(const f32x4 *)(x + (active ? run_elem<T>(lane, j) : 0));
+    const XFromRegs<T> xg{xr};
+
+    float acc[R][1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = 0.f;
+
+    if constexpr (DIRECT) {
+        URaw<T> pr[R];
+        auto load = [&](int it) __attribute__((always_inline)) {
+            it = min(it, max(nit - 1, 0));
+            const int row0 = (gw + tw * it) * R;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const bool ok = active && row0 + r < n;
+                raw_from_global_q4k(w + (ok ? (int64_t)(row0 + r) * rb : 0), ok ? lane : 0, pr[r]);
+            }
+        };
+        load(0);
+        for (int it = 0; it < nit; ++it) {
+            URaw<T> cur[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) cur[r] = pr[r];
+            load(it + 1);
+            if (active)
+                unit_dot<T, 1, R>(cur, lane, xg, acc);
+            reduce_store<R>(acc, (gw + tw * it) * R, n, lane, y);
+        }
+    } else {
+        uint32_t *mw = ws + wave * S::LDS_DW;
+        S st;
+        auto load = [&](int it) __attribute__((always_inline)) {
+            it = min(it, max(nit - 1, 0));
+            st.load(w, rb, n, (gw + tw * it) * R, 0, cpr, lane);
+        };
+        load(0);
+        for (int it = 0; it < nit; ++it) {
+            st.store(mw, lane);
+            wave_lds_sync();
+            load(it + 1);
+            if (active) {
+                URaw<T> cur[R];
+#pragma unroll
+                for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
+                unit_dot<T, 1, R>(cur, lane, xg, acc);
+            }
+            reduce_store<R>(acc, (gw + tw * it) * R, n, lane, y);
+            wave_lds_sync();
+        }
+    }
+}
+
+// --------------------------------------------------------------- gemv1 --
+// Batch 1, k spanning several segments: x staged in LDS once per workgroup;
+// each wave walks items (R rows x one segment) with the next item's weight
+// bytes in flight.
+template <int T, int R, int NW, int XK>
+__global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 4)))
+gemv1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
+             float *__restrict__ y)
+{
+    using F = Fmt<T>;
+    constexpr int UE = GemvUnit<T>::UE;
+    using S = SegStage<T, R>;
+    constexpr int SEGE = S::SEGE;
+    constexpr int XS = XK + (XK / UE) * 4;
+    constexpr int XV = XK / (4 * 64 * NW);          // 4-float vectors per thread for x
+    __shared__ __attribute__((aligned(16))) float xs[XS];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[NW * S::LDS_DW];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int gw = blockIdx.x * NW + wave, tw = gridDim.x * NW;
+    const int nrg = (n + R - 1) / R;
+    const int nseg = (k + SEGE - 1) / SEGE;
+    const int my_rg = gw < nrg ? (nrg - gw + tw - 1) / tw : 0;
+    const int nitems = my_rg * nseg;
+    uint32_t *mw = ws + wave * S::LDS_DW;
+
+    S st;
+    auto load = [&](int it) __attribute__((always_inline)) {
+        it = min(it, max(nitems - 1, 0));   // past the end: reload the last item
+        const int rg = gw + tw * (it / nseg), seg = it % nseg;
+        const int segE = min(SEGE, k - seg * SEGE);
+        st.load(w, rb, n, rg * R, seg, segE / F::BE * F::BB / 16, lane);
+    };
+
+    load(0);
+    {   // stage x; positions >= k hold copies of x[0..3], which no active lane reads
+        f32x4 xv[XV];
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            const int e = 4 * (threadIdx.x + 64 * NW * i);
+            xv[i] = *(const f32x4 *)(x + (e < k ? e : 0));
+        }
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            const int e = 4 * (threadIdx.x + 64 * NW * i);
+            *(f32x4 *)(xs + xpad<UE>(e)) = xv[i];
+        }
+    }
+    __syncthreads();
+
+    float acc[R][1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r][0] = 0.f;
+    for (int it = 0; it < nitems; ++it) {
+        st.store(mw, lane);
+        wave_lds_sync();
+        load(it + 1);
+        const int rg = gw + tw * (it / nseg), seg = it % nseg;
+        const int segE = min(SEGE, k - seg * SEGE);
+        if (lane < segE / UE) {
+            URaw<T> cur[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
+            const XFromLds<T, XS> xg{xs + xpad<UE>(seg * SEGE), lane};
+            unit_dot<T, 1, R>(cur, lane, xg, acc);
+        }
+        if (seg == nseg - 1)
+            reduce_store<R>(acc, rg * R, n, lane, y);
+        wave_lds_sync();
+    }
+}
+
+// ---------------------------------------------------------------- gemv --
+// Batch 1..8, any row alignment: per segment, the workgroup stages x (all
+// batches) and each wave its R row segments in LDS.
 template <int T, int B, int R, bool A16>
 __global__ void __launch_bounds__(256)
 gemv_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
@@ -314,14 +577,15 @@ gemv_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float
 {
     using F = Fmt<T>;
     constexpr int UE = GemvUnit<T>::UE;
-    constexpr int SEGE = 64 * UE;                 // elements per segment
-    constexpr int SEGB = SEGE / F::BE * F::BB;    // bytes of one row's segment
+    using S = SegStage<T, R>;
+    constexpr int SEGE = S::SEGE, SEGB = S::SEGB;
     constexpr int XS = SEGE + (SEGE / UE) * 4;    // padded floats per batch
     __shared__ __attribute__((aligned(16))) float xs[B * XS];
-    __shared__ __attribute__((aligned(16))) uint32_t ws[4][R][SEGB / 4 + 4];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[4 * S::LDS_DW];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * 4 + wave) * R;
+    uint32_t *mw = ws + wave * S::LDS_DW;
     float acc[R][B];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -334,31 +598,55 @@ gemv_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float
         const int segE = min(SEGE, k - e0);
         const int segBytes = segE / F::BE * F::BB;
         __syncthreads();   // all reads of the previous segment are done
-        // stage x[b][e0 .. e0+segE) (segE is a multiple of 32)
-        for (int i4 = threadIdx.x; i4 < B * (segE >> 2); i4 += 256) {
-            const int b = i4 / (segE >> 2), e = 4 * (i4 - b * (segE >> 2));
-            const float4 v = *(const float4 *)(x + (int64_t)b * k + e0 + e);
-            *(float4 *)(xs + b * XS + xpad<UE>(e)) = v;
-        }
-        // stage this wave's row segments
+        S st;
+        if constexpr (A16)
+            st.load(w, rb, n, row0, seg, segBytes >> 4, lane);
+        // stage x[b][e0 .. e0+segE): XB vectors per thread per batch of loads
+        {
+            constexpr int XB = 8;
+            const int nx4 = B * (segE >> 2);
+            for (int base = 0; base < nx4; base += 256 * XB) {
+                f32x4 v[XB];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = row0 + r;
-            if (row < n) {
-                const uint8_t *src = w + (int64_t)row * rb + (int64_t)seg * SEGB;
-                if constexpr (A16) {
-                    for (int c = lane; c < (segBytes >> 4); c += 64)
-                        *(uint4 *)(&ws[wave][r][4 * c]) = *(const uint4 *)(src + 16 * c);
-                } else {
-                    uint16_t *dst = (uint16_t *)&ws[wave][r][0];
+                for (int j = 0; j < XB; ++j) {
+                    const int i4 = base + threadIdx.x + 256 * j;
+                    const int ic = i4 < nx4 ? i4 : 0;
+                    const int b = ic / (segE >> 2), e = 4 * (ic - b * (segE >> 2));
+                    v[j] = *(const f32x4 *)(x + (int64_t)b * k + e0 + e);
+                }
+#pragma unroll
+                for (int j = 0; j < XB; ++j) {
+                    const int i4 = base + threadIdx.x + 256 * j;
+                    if (i4 < nx4) {
+                        const int b = i4 / (segE >> 2), e = 4 * (i4 - b * (segE >> 2));
+                        *(f32x4 *)(xs + b * XS + xpad<UE>(e)) = v[j];
+                    }
+                }
+            }
+        }
+        if constexpr (A16) {
+            st.store(mw, lane);
+        } else {
+            // rows not 16-byte aligned: 2-byte copies
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = row0 + r;
+                if (row < n) {
+                    const uint8_t *src = w + (int64_t)row * rb + (int64_t)seg * SEGB;
+                    uint16_t *dst = (uint16_t *)(mw + r * S::RS);
                     for (int c = lane; c < (segBytes >> 1); c += 64)
                         dst[c] = ((const uint16_t *)src)[c];
                 }
             }
         }
         __syncthreads();
-        if (lane < segE / UE)
-            gemv_unit<T, B, R, 4 * (SEGB / 4 + 4), XS>(&ws[wave][0][0], xs, lane, acc);
+        if (lane < segE / UE) {
+            URaw<T> cur[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
+            const XFromLds<T, XS> xg{xs, lane};
+            unit_dot<T, B, R>(cur, lane, xg, acc);
+        }
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -371,23 +659,76 @@ gemv_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float
         }
 }
 
+// ------------------------------------------------------------- launchers --
+
+// Persistent launches: at most as many workgroups as fit on the device at once.
+template <class K>
+static int resident_wgs(K kernel, int block)
+{
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1)
+        return 0;
+    return per_cu * cus;
+}
+
+template <int T, int R>
+static hipError_t launch_b1_regs(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
+                                 hipStream_t s)
+{
+    // at most 2 workgroups (8 waves) per CU: each wave then walks several
+    // row groups, which amortizes its x slice and keeps a load in flight
+    static int cap = 0;   // per-process cache (one device model)
+    if (cap == 0) {
+        int dev = 0, cus = 0;
+        const int res = resident_wgs(gemv2_kernel<T, R>, 256);
+        if (res == 0 || hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidValue;
+        cap = res < 2 * cus ? res : 2 * cus;
+    }
+    const int64_t want = ((n + R - 1) / R + 3) / 4;
+    const dim3 grid((unsigned)(want < cap ? want : cap)), block(256);
+    hipLaunchKernelGGL((gemv2_kernel<T, R>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
+    return hipGetLastError();
+}
+
+template <int T, int R, int NW, int XK>
+static hipError_t launch_b1_lds(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
+                                hipStream_t s)
+{
+    static int cap = 0;
+    if (cap == 0 && (cap = resident_wgs(gemv1_kernel<T, R, NW, XK>, 64 * NW)) == 0)
+        return hipErrorInvalidValue;
+    const int64_t want = ((n + R - 1) / R + NW - 1) / NW;
+    const dim3 grid((unsigned)(want < cap ? want : cap)), block(64 * NW);
+    hipLaunchKernelGGL((gemv1_kernel<T, R, NW, XK>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
+    return hipGetLastError();
+}
+
 template <int T, int B, int R>
-static hipError_t launch_tbr(const void *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
+static hipError_t launch_tbr(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                              hipStream_t s)
 {
     const dim3 grid((unsigned)((n + 4 * R - 1) / (4 * R))), block(256);
-    const uint8_t *wb = (const uint8_t *)w;
     if (rb % 16 == 0)
-        hipLaunchKernelGGL((gemv_kernel<T, B, R, true>), grid, block, 0, s, wb, (int)n, (int)k, (int64_t)rb, x, y);
+        hipLaunchKernelGGL((gemv_kernel<T, B, R, true>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
     else
-        hipLaunchKernelGGL((gemv_kernel<T, B, R, false>), grid, block, 0, s, wb, (int)n, (int)k, (int64_t)rb, x, y);
+        hipLaunchKernelGGL((gemv_kernel<T, B, R, false>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
     return hipGetLastError();
 }
 
 template <int T>
-static hipError_t launch_t(const void *w, int64_t n, int64_t k, size_t rb, const float *x, int batch, float *y,
+static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, int batch, float *y,
                            hipStream_t s)
 {
+    if (batch == 1 && rb % 16 == 0) {
+        if (k <= 64 * GemvUnit<T>::UE)
+            return launch_b1_regs<T, 2>(w, n, k, rb, x, y, s);
+        if (k <= 16384)
+            return launch_b1_lds<T, 2, 8, 16384>(w, n, k, rb, x, y, s);
+    }
     switch (batch) {
     case 1: return launch_tbr<T, 1, 2>(w, n, k, rb, x, y, s);
     case 2: return launch_tbr<T, 2, 2>(w, n, k, rb, x, y, s);
@@ -404,11 +745,12 @@ static hipError_t launch_t(const void *w, int64_t n, int64_t k, size_t rb, const
 hipError_t launch_gemv(int type, const void *w, int64_t n, int64_t k, size_t rb, const float *x, int batch,
                        float *y, hipStream_t s)
 {
+    const uint8_t *wb = (const uint8_t *)w;
     switch (type) {
-    case T_Q4_0: return launch_t<T_Q4_0>(w, n, k, rb, x, batch, y, s);
-    case T_Q8_0: return launch_t<T_Q8_0>(w, n, k, rb, x, batch, y, s);
-    case T_Q4_K: return launch_t<T_Q4_K>(w, n, k, rb, x, batch, y, s);
-    case T_Q6_K: return launch_t<T_Q6_K>(w, n, k, rb, x, batch, y, s);
+    case T_Q4_0: return launch_t<T_Q4_0>(wb, n, k, rb, x, batch, y, s);
+    case T_Q8_0: return launch_t<T_Q8_0>(wb, n, k, rb, x, batch, y, s);
+    case T_Q4_K: return launch_t<T_Q4_K>(wb, n, k, rb, x, batch, y, s);
+    case T_Q6_K: return launch_t<T_Q6_K>(wb, n, k, rb, x, batch, y, s);
     default: return hipErrorInvalidValue;
     }
 }

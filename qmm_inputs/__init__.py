@@ -28,6 +28,9 @@ Seeds: matrix i of workload c uses seed 1000*c + i; its activation uses
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
@@ -50,27 +53,55 @@ def _f16_bytes(v: np.ndarray) -> np.ndarray:
     return v.astype("<f2").view(np.uint8).reshape(v.shape + (2,))
 
 
+_CHUNK = 1 << 24   # bytes per independent uniform stream
+
+
+def uniform_bytes(seed: int, nbytes: int) -> np.ndarray:
+    """nbytes uniform random bytes.  Chunk c of 16 MiB comes from its own
+    PCG64 stream seeded with (seed, c), so the result does not depend on how
+    many threads draw it."""
+    nch = (nbytes + _CHUNK - 1) // _CHUNK
+    out = np.empty(nch * (_CHUNK // 8), dtype=np.uint64)
+
+    def work(c):
+        g = np.random.Generator(np.random.PCG64([seed, c]))
+        out[c * (_CHUNK // 8):(c + 1) * (_CHUNK // 8)] = g.integers(
+            0, 2 ** 64 - 1, size=_CHUNK // 8, dtype=np.uint64, endpoint=True)
+
+    if nch == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1, nch))) as ex:
+            list(ex.map(work, range(nch)))
+    return out.view(np.uint8)[:nbytes]
+
+
 def gen_weights(qtype: int, n: int, k: int, seed: int, d_range=None) -> np.ndarray:
-    """Random quantized weight matrix as raw bytes, shape [n, row_bytes]."""
+    """Random quantized weight matrix as raw bytes, shape [n, row_bytes].
+
+    Draw order (fixed, so a seed always gives the same bytes): one uniform
+    byte string covering every block (``uniform_bytes``), then, from
+    default_rng(seed), the fp16 scale fields (overwritten in place) and --
+    for Q8_0 only -- the int8 codes."""
     rng = np.random.default_rng(seed)
     nb = k // BLOCK_ELEMS[qtype]
     rb = row_bytes(qtype, k)
     lo, hi = d_range if d_range is not None else DEFAULT_D_RANGE[qtype]
-    blk = np.empty((n, nb, BLOCK_BYTES[qtype]), dtype=np.uint8)
+    blk = uniform_bytes(seed, n * rb).reshape(n, nb, BLOCK_BYTES[qtype])
     if qtype == Q8_0:
         blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
         blk[:, :, 2:34] = rng.integers(-127, 128, size=(n, nb, 32), dtype=np.int8).view(np.uint8)
     elif qtype == Q4_0:
+        # code bytes stay uniform: each nibble ~ U{0..15}
         blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
-        blk[:, :, 2:18] = rng.integers(0, 256, size=(n, nb, 16), dtype=np.uint8)
     elif qtype == Q4_K:
+        # scale bytes and code bytes stay uniform
         blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
         blk[:, :, 2:4] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
-        blk[:, :, 4:16] = rng.integers(0, 256, size=(n, nb, 12), dtype=np.uint8)
-        blk[:, :, 16:144] = rng.integers(0, 256, size=(n, nb, 128), dtype=np.uint8)
     elif qtype == Q6_K:
-        blk[:, :, 0:192] = rng.integers(0, 256, size=(n, nb, 192), dtype=np.uint8)
-        blk[:, :, 192:208] = rng.integers(-64, 64, size=(n, nb, 16), dtype=np.int8).view(np.uint8)
+        # ql, qh uniform (q ~ U{0..63}); scale = (uniform byte & 127) - 64 ~ U{-64..63}
+        sc = (blk[:, :, 192:208] & 0x7F).astype(np.int16) - 64
+        blk[:, :, 192:208] = sc.astype(np.int8).view(np.uint8)
         blk[:, :, 208:210] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
     else:
         raise ValueError("unknown type %r" % (qtype,))
