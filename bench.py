@@ -35,6 +35,12 @@ import qmm_inputs as G  # noqa: E402
 METRIC = "quantized GEMV HBM GB/s (% of peak) + decode tok/s equiv; prefill GEMM TFLOP/s"
 HBM_PEAK_GBS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
+# HBM bytes per launch of the dominant kernel (the batch-1 Q4_0 GEMV over the
+# decode stream) from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by what the
+# same counters read for a plain 256 MiB device copy (reads x2.0, writes
+# x1.0).  It describes the kernels it was measured on: set it to None when
+# they change, until the counters are taken again.
+TRAFFIC = 3695210
 
 
 def log(*a):
@@ -49,6 +55,8 @@ def parse():
     p.add_argument("--secondary", choices=["all", "none"], default="all")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU oracle sample")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB 10 times (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -138,24 +146,6 @@ def time_eager(torch, q, probs, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def per_launch_times(torch, q, probs, reps):
-    """Kernel durations from HIP events recorded right before and after each
-    launch, on the stream the kernels run on (torch's current stream, which
-    the library launches on).  Returns the summed duration of one pass (s),
-    averaged over reps passes."""
-    stream = torch.cuda.current_stream().cuda_stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in probs]
-    total = 0.0
-    for _ in range(reps):
-        for p, (a, b) in zip(probs, ev):
-            a.record()
-            p.launch(q, stream)
-            b.record()
-        torch.cuda.synchronize()
-        total += sum(a.elapsed_time(b) for a, b in ev) * 1e-3
-    return total / reps
-
-
 def cpu_baseline(cfg_probs_host, target_s):
     """The oracle (plain C, fp64, OpenMP over rows) on a bounded sample of the
     same workload: whole layers of the decode stream, as many as fit in
@@ -195,12 +185,10 @@ def sec_cfg1(torch, q, steps, warmup, dev):
     hot = [Problem(torch, "hot", G.Q8_0, n, k, w0, x, y)] * 256
     gh = capture(torch, q, hot)
     th = time_graph(torch, gh, max(2, steps // 4), 2) / 256
-    kt = per_launch_times(torch, q, probs, 1) / len(probs)
     b = probs[0].bytes
     del copies, probs, g, gh
     return {"workload": "Q8_0 2048x2048 GEMV, batch 1, over 256 rotating copies",
             "us_per_gemv": t * 1e6, "GB_s": b / t / 1e9, "pct_hbm_peak": 100 * b / t / 1e9 / HBM_PEAK_GBS,
-            "kernel_us_event": kt * 1e6,
             "hot_us_per_gemv_cache_resident": th * 1e6}
 
 
@@ -210,10 +198,9 @@ def sec_stream(torch, q, cfg, weights, batch, steps, warmup, dev, label, with_ge
     tbytes = sum(p.bytes for p in probs)
     g = capture(torch, q, probs)
     tg = time_graph(torch, g, steps, warmup)
-    kt = per_launch_times(torch, q, probs, 2)
     out = {"workload": label, "gemvs": len(probs), "batch": batch, "weight_bytes": wbytes,
            "ms_per_pass": tg * 1e3, "GB_s": tbytes / tg / 1e9, "pct_hbm_peak": 100 * tbytes / tg / 1e9 / HBM_PEAK_GBS,
-           "decode_tok_s": batch / tg, "kernel_sum_ms": kt * 1e3, "GB_s_kernel_sum": tbytes / kt / 1e9}
+           "decode_tok_s": batch / tg}
     del g
     if with_gemm:
         # the same pass as a skinny GEMM (fp16 activations, M = batch)
@@ -243,12 +230,9 @@ def sec_prefill(torch, q, steps, warmup, dev):
             probs.append(Problem(torch, "%s.c%d" % (name, c), t, n, k, w, X, Y, kind="gemm"))
         g = capture(torch, q, probs)
         tg = time_graph(torch, g, steps, warmup)
-        kt = per_launch_times(torch, q, probs, 2)
         flops = sum(p.flops for p in probs)
         res[name] = {"shape": "4 x (%d x %d x %d)" % (m, n, k), "ms_4_chunks": tg * 1e3,
-                     "TFLOP_s": flops / tg / 1e12, "pct_fp16_peak": 100 * flops / tg / 1e12 / FP16_PEAK_TFLOPS,
-                     "kernel_us_per_chunk": kt / len(probs) * 1e6,
-                     "TFLOP_s_kernel": flops / kt / 1e12}
+                     "TFLOP_s": flops / tg / 1e12, "pct_fp16_peak": 100 * flops / tg / 1e12 / FP16_PEAK_TFLOPS}
         del g, probs, w
     torch.cuda.empty_cache()
     return res
@@ -263,9 +247,19 @@ def main():
               "(GEMV rows / GEMM columns would shard across GPUs; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
     import torch
-    import dequant_matmul_amd as q
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        nb = args.calibrate_copy << 20
+        a = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": nb, "bytes_written": nb, "launches": 10}))
+        return
+    import dequant_matmul_amd as q
     log("device:", torch.cuda.get_device_name(0), "| lib:", q.version())
 
     # primary: TinyLlama-shaped Q4_0 decode stream, batch 1
@@ -286,16 +280,21 @@ def main():
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
+    # HIP events on the stream the graph (and so every GEMV kernel) runs on
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()
     for _ in range(args.steps):
         g.replay()
+    ev1.record()
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
+    ev_step_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
     value = tot_bytes / step_s / 1e9
-
-    # dominant kernel: per-launch event durations over the same pass
-    kt = per_launch_times(torch, q, probs, max(3, args.steps // 4))
-    achieved = tot_bytes / kt / 1e9
+    # dominant kernel: every launch of the pass is the Q4_0 GEMV; its average
+    # launch duration is the event time of the pass divided by the launches
+    avg_launch_s = ev_step_s / len(probs)
+    achieved = (tot_bytes / len(probs)) / avg_launch_s / 1e9
     eager_s = time_eager(torch, q, probs, max(3, args.steps // 2), 2)
 
     line = {
@@ -309,11 +308,11 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tok_s": round(1.0 / step_s, 1),
         "eager_ms_per_step": round(eager_s * 1e3, 4),
-        "kernel_sum_ms_per_step": round(kt * 1e3, 4),
+        "event_ms_per_step": round(ev_step_s * 1e3, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_kernel<Q4_0, batch 1, 2 rows/wave>",
-                     "avg_launch_us": round(kt / len(probs) * 1e6, 3),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": TRAFFIC,
+                     "kernel": "Q4_0 batch-1 GEMV (gemv2_kernel / gemv1_kernel for k=5632)",
+                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
                      "bytes_per_launch": tot_bytes / len(probs)},
     }
     del g
