@@ -90,6 +90,43 @@ class Problem:
             raise RuntimeError("%s %s: %s" % (self.kind, self.name, q.status_str(st)))
 
 
+class Group:
+    """Several same-type, same-k batch-1 GEMVs issued as one qmm_gemv_multi call."""
+
+    def __init__(self, probs):
+        import ctypes
+        self.probs = probs
+        npb = len(probs)
+        self.t, self.k, self.batch = probs[0].t, probs[0].k, probs[0].batch
+        self.np = npb
+        self.w = (ctypes.c_void_p * npb)(*[p.w.data_ptr() for p in probs])
+        self.x = (ctypes.c_void_p * npb)(*[p.x.data_ptr() for p in probs])
+        self.y = (ctypes.c_void_p * npb)(*[p.y.data_ptr() for p in probs])
+        self.n = (ctypes.c_int64 * npb)(*[p.n for p in probs])
+        self.name = "+".join(p.name for p in probs)
+
+    def launch(self, q, stream):
+        st = q.lib.qmm_gemv_multi(self.t, self.np, self.w, self.n, self.k, self.x, self.batch, self.y, stream)
+        if st != 0:
+            raise RuntimeError("gemv_multi %s: %s" % (self.name, q.status_str(st)))
+
+
+def group_layers(probs, fuse):
+    """Split a 7-projections-per-layer list into launch groups: fuse = set of
+    projection-name tuples issued together (e.g. ("gate", "up"))."""
+    out = []
+    for L in range(0, len(probs), 7):
+        layer = {p.name.split(".")[-1]: p for p in probs[L:L + 7]}
+        done = set()
+        for nm in ("q", "k", "v", "o", "gate", "up", "down"):
+            if nm in done:
+                continue
+            grp = next((g for g in fuse if nm in g), (nm,))
+            out.append(Group([layer[g] for g in grp]) if len(grp) > 1 else layer[nm])
+            done.update(grp)
+    return out
+
+
 def build_weights(torch, cfg, dev="cuda:0"):
     return [(name, t, n, k, torch.from_numpy(G.gen_weights(t, n, k, seed)).to(dev))
             for (name, t, n, k, seed) in G.workload(cfg)]
@@ -296,6 +333,18 @@ def main():
     avg_launch_s = ev_step_s / len(probs)
     achieved = (tot_bytes / len(probs)) / avg_launch_s / 1e9
     eager_s = time_eager(torch, q, probs, max(3, args.steps // 2), 2)
+    # the same 154 GEMVs with fewer launches per token: gate|up as one launch
+    # (the dispatch count shimmy's pipeline page gives: 6 per layer) and
+    # q|k|v + gate|up (4 per layer)
+    grouped = {}
+    for label, fuse in (("6_launches_per_layer", (("gate", "up"),)),
+                        ("4_launches_per_layer", (("q", "k", "v"), ("gate", "up")))):
+        gp = group_layers(probs, fuse)
+        gg = capture(torch, q, gp)
+        tg = time_graph(torch, gg, args.steps, args.warmup)
+        grouped[label] = {"launches": len(gp), "ms_per_pass": round(tg * 1e3, 4),
+                          "GB_s": round(tot_bytes / tg / 1e9, 1), "decode_tok_s": round(1.0 / tg, 1)}
+        del gg
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -309,6 +358,7 @@ def main():
         "decode_tok_s": round(1.0 / step_s, 1),
         "eager_ms_per_step": round(eager_s * 1e3, 4),
         "event_ms_per_step": round(ev_step_s * 1e3, 4),
+        "grouped_launches": grouped,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": TRAFFIC,
                      "kernel": "Q4_0 batch-1 GEMV (gemv2_kernel / gemv1_kernel for k=5632)",

@@ -34,6 +34,7 @@ SIGNATURES = {
     "qmm_row_bytes": (_SZ, [_I, _I64]),
     "qmm_dequant": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "qmm_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "qmm_gemv_multi": (_I, [_I, _I, _P, _P, _I64, _P, _I64, _P, _P]),
     "qmm_gemm_prefill": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
     "qmm_status_str": (ctypes.c_char_p, [_I]),
     "qmm_version": (ctypes.c_char_p, []),
@@ -48,7 +49,7 @@ class QmmError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libqmm.so not built: run `python -m dequant_matmul_amd.build` "
+        raise ImportError("libqmm.so not built: run `python dequant_matmul_amd/build.py` "
                           "(expected at %s)" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
@@ -132,6 +133,31 @@ def gemv(w, qtype: int, n: int, k: int, x, out=None):
     _call(lib.qmm_gemv(qtype, w.data_ptr(), n, k, x.data_ptr(), B, out.data_ptr(), _stream_ptr(w.device)),
           "qmm_gemv")
     return out[0] if squeeze else out
+
+
+def gemv_multi(ws, qtype: int, ns, k: int, xs, outs=None):
+    """Grouped GEMV: problem i computes W_i x_i (same type, k and batch) in
+    as few launches as possible.  Returns the list of outputs."""
+    torch = _torch()
+    np_ = len(ws)
+    if not (len(ns) == len(xs) == np_):
+        raise ValueError("ws, ns and xs must have the same length")
+    xs = [x.unsqueeze(0) if x.dim() == 1 else x for x in xs]
+    B = xs[0].shape[0] if np_ else 0
+    for w, n, x in zip(ws, ns, xs):
+        _check_w(w, qtype, n, k)
+        if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or tuple(x.shape) != (B, k):
+            raise ValueError("each x must be a contiguous fp32 device tensor [B, k] with the same B")
+    if outs is None:
+        outs = [torch.empty((B, n), dtype=torch.float32, device=w.device) for w, n in zip(ws, ns)]
+    wp = (ctypes.c_void_p * max(np_, 1))(*[w.data_ptr() for w in ws])
+    xp = (ctypes.c_void_p * max(np_, 1))(*[x.data_ptr() for x in xs])
+    yp = (ctypes.c_void_p * max(np_, 1))(*[o.data_ptr() for o in outs])
+    nn = (ctypes.c_int64 * max(np_, 1))(*ns)
+    dev = ws[0].device if np_ else None
+    _call(lib.qmm_gemv_multi(qtype, np_, wp, nn, k, xp, B, yp, _stream_ptr(dev) if np_ else None),
+          "qmm_gemv_multi")
+    return outs
 
 
 def gemm_prefill(w, qtype: int, n: int, k: int, x, out=None):

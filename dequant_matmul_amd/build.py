@@ -1,6 +1,8 @@
 """Build libqmm.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m dequant_matmul_amd.build
+    python dequant_matmul_amd/build.py
+
+(Run the file, not the module: importing the package needs the library.)
 
 Compiles every source under dequant_matmul_amd/csrc into
 dequant_matmul_amd/libqmm.so.  Runs without a GPU (hipcc cross-compiles).
@@ -23,6 +25,9 @@ FLAGS = [
     "-fvisibility=hidden", "-Wall",
     # no packed fp32 (v_pk_*_f32) instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments preloaded into SGPRs by the dispatcher: saves the first
+    # dependent scalar load of every wave (about 0.5 us on small launches)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

@@ -104,6 +104,48 @@ int qmm_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int6
     return hip_status(qmm::launch_gemv(type, w, n, k, rb, x, (int)batch, y, (hipStream_t)stream));
 }
 
+int qmm_gemv_multi(int type, int nprob, const void *const *w, const int64_t *n, int64_t k,
+                   const float *const *x, int64_t batch, float *const *y, void *stream)
+{
+    if (nprob < 0)
+        return QMM_ERR_SHAPE;
+    if (nprob == 0)
+        return QMM_OK;
+    if (w == nullptr || n == nullptr || x == nullptr || y == nullptr)
+        return QMM_ERR_NULL;
+    if (block_elems(type) == 0)
+        return QMM_ERR_TYPE;
+    if (batch < 0 || batch > 8)
+        return QMM_ERR_SHAPE;
+    size_t rb = 0;
+    int64_t rows = 0;
+    for (int i = 0; i < nprob; ++i) {
+        int st = check_common(type, w[i], n[i], k, &rb);
+        if (st != QMM_OK)
+            return st;
+        rows += n[i];
+        if (n[i] == 0 || batch == 0)
+            continue;
+        if (y[i] == nullptr || (k > 0 && x[i] == nullptr))
+            return QMM_ERR_NULL;
+        if (!aligned16(y[i]) || (k > 0 && !aligned16(x[i])))
+            return QMM_ERR_ALIGN;
+    }
+    if (batch == 0 || rows == 0)
+        return QMM_OK;
+    if (k == 0) {
+        for (int i = 0; i < nprob; ++i) {
+            if (n[i] == 0)
+                continue;
+            const int st = hip_status(qmm::launch_fill_zero(y[i], batch * n[i], (hipStream_t)stream));
+            if (st != QMM_OK)
+                return st;
+        }
+        return QMM_OK;
+    }
+    return hip_status(qmm::launch_gemv_multi(type, nprob, w, n, k, rb, x, (int)batch, y, (hipStream_t)stream));
+}
+
 int qmm_gemm_prefill(int type, const void *w, int64_t n, int64_t k, const uint16_t *x, int64_t m, float *y,
                      void *stream)
 {

@@ -422,39 +422,101 @@ __device__ __forceinline__ void reduce_store(float (&acc)[R][1], int row0, int n
 
 // --------------------------------------------------------------- gemv2 --
 // Batch 1, k <= one segment, x in registers, independent persistent waves.
-template <int T, int R>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
-gemv2_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
-             float *__restrict__ y)
+// One launch serves up to MAXP problems with the same type and k (e.g. the
+// q / k / v or gate / up projections of a layer): row groups are numbered
+// across the problems and each wave walks them with a stride.
+constexpr int GEMV_MAXP = 8;
+struct GemvProbs {
+    const uint8_t *w[GEMV_MAXP];
+    const float *x[GEMV_MAXP];
+    float *y[GEMV_MAXP];
+    int n[GEMV_MAXP];
+    int rg0[GEMV_MAXP + 1];   // first row group of each problem; rg0[np] = total
+    int np;
+};
+
+// Problem sources: one problem passed as plain kernel arguments (held in
+// SGPRs from the start), or a table of problems (its entries are scalar loads
+// whose latency shows in small launches, so single problems avoid it).
+struct OneProb {
+    const uint8_t *w;
+    const float *x;
+    float *y;
+    int n;
+    __device__ __forceinline__ int total_rg(int R) const { return (n + R - 1) / R; }
+    __device__ __forceinline__ int find(int) const { return 0; }
+    __device__ __forceinline__ int rg_begin(int) const { return 0; }
+    __device__ __forceinline__ const uint8_t *W(int) const { return w; }
+    __device__ __forceinline__ const float *X(int) const { return x; }
+    __device__ __forceinline__ float *Y(int) const { return y; }
+    __device__ __forceinline__ int N(int) const { return n; }
+};
+struct TableProbs {
+    const GemvProbs &P;
+    __device__ __forceinline__ int total_rg(int) const { return P.rg0[P.np]; }
+    __device__ __forceinline__ int find(int rg) const
+    {
+        int pp = 0;
+        for (int q = 1; q < P.np; ++q)
+            if (rg >= P.rg0[q]) pp = q;
+        return pp;
+    }
+    __device__ __forceinline__ int rg_begin(int pp) const { return P.rg0[pp]; }
+    __device__ __forceinline__ const uint8_t *W(int pp) const { return P.w[pp]; }
+    __device__ __forceinline__ const float *X(int pp) const { return P.x[pp]; }
+    __device__ __forceinline__ float *Y(int pp) const { return P.y[pp]; }
+    __device__ __forceinline__ int N(int pp) const { return P.n[pp]; }
+};
+
+template <int T, int R, class PS>
+__device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint32_t *ws)
 {
     constexpr int UE = GemvUnit<T>::UE, NRUN = GemvUnit<T>::NRUN;
     using S = SegStage<T, R>;
     constexpr bool DIRECT = (T == T_Q4_K);
-    __shared__ __attribute__((aligned(16))) uint32_t ws[DIRECT ? 4 : 4 * S::LDS_DW];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gw = blockIdx.x * 4 + wave, tw = gridDim.x * 4;
-    const int nrg = (n + R - 1) / R;
+    const int nrg = P.total_rg(R);
     const int nit = gw < nrg ? (nrg - gw + tw - 1) / tw : 0;
     const bool active = lane < k / UE;
     const int cpr = k / Fmt<T>::BE * Fmt<T>::BB / 16;
 
-    // this lane's slice of x
+    // problem and first row of item it (past the end: the last item)
+    auto locate = [&](int it, int &pp, int &row0) __attribute__((always_inline)) {
+        it = min(it, max(nit - 1, 0));
+        const int rg = gw + tw * it;
+        pp = P.find(rg);
+        row0 = (rg - P.rg_begin(pp)) * R;
+    };
+
+    // this lane's slice of x for the current problem
     f32x4 xr[NRUN];
+    auto load_x = [&](int pp) __attribute__((always_inline)) {
+        const float *x = P.X(pp);
 #pragma unroll
-    for (int j = 0; j < NRUN; ++j)
-        xr[j] = *(const f32x4 *)(x + (active ? run_elem<T>(lane, j) : 0));
+        for (int j = 0; j < NRUN; ++j)
+            xr[j] = *(const f32x4 *)(x + (active ? run_elem<T>(lane, j) : 0));
+    };
     const XFromRegs<T> xg{xr};
 
     float acc[R][1];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r][0] = 0.f;
 
+    int p0, r0;
+    locate(0, p0, r0);
+    int xp = p0;
+    load_x(xp);
+
     if constexpr (DIRECT) {
         URaw<T> pr[R];
         auto load = [&](int it) __attribute__((always_inline)) {
-            it = min(it, max(nit - 1, 0));
-            const int row0 = (gw + tw * it) * R;
+            int pp, row0;
+            locate(it, pp, row0);
+            const uint8_t *w = P.W(pp);
+            const int n = P.N(pp);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const bool ok = active && row0 + r < n;
@@ -463,23 +525,36 @@ gemv2_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
         };
         load(0);
         for (int it = 0; it < nit; ++it) {
+            int pp, row0;
+            locate(it, pp, row0);
+            if (pp != xp) {   // wave-uniform: the next problem's x
+                xp = pp;
+                load_x(xp);
+            }
             URaw<T> cur[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) cur[r] = pr[r];
             load(it + 1);
             if (active)
                 unit_dot<T, 1, R>(cur, lane, xg, acc);
-            reduce_store<R>(acc, (gw + tw * it) * R, n, lane, y);
+            reduce_store<R>(acc, row0, P.N(pp), lane, P.Y(pp));
         }
     } else {
         uint32_t *mw = ws + wave * S::LDS_DW;
         S st;
         auto load = [&](int it) __attribute__((always_inline)) {
-            it = min(it, max(nit - 1, 0));
-            st.load(w, rb, n, (gw + tw * it) * R, 0, cpr, lane);
+            int pp, row0;
+            locate(it, pp, row0);
+            st.load(P.W(pp), rb, P.N(pp), row0, 0, cpr, lane);
         };
         load(0);
         for (int it = 0; it < nit; ++it) {
+            int pp, row0;
+            locate(it, pp, row0);
+            if (pp != xp) {
+                xp = pp;
+                load_x(xp);
+            }
             st.store(mw, lane);
             wave_lds_sync();
             load(it + 1);
@@ -489,10 +564,29 @@ gemv2_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
                 for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
                 unit_dot<T, 1, R>(cur, lane, xg, acc);
             }
-            reduce_store<R>(acc, (gw + tw * it) * R, n, lane, y);
+            reduce_store<R>(acc, row0, P.N(pp), lane, P.Y(pp));
             wave_lds_sync();
         }
     }
+}
+
+template <int T, int R>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
+gemv2_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
+             float *__restrict__ y)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : 4 * SegStage<T, R>::LDS_DW];
+    const OneProb P{w, x, y, n};
+    gemv2_body<T, R>(P, k, rb, ws);
+}
+
+template <int T, int R>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
+gemv2m_kernel(const GemvProbs Pt, int k, int64_t rb)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : 4 * SegStage<T, R>::LDS_DW];
+    const TableProbs P{Pt};
+    gemv2_body<T, R>(P, k, rb, ws);
 }
 
 // --------------------------------------------------------------- gemv1 --
@@ -673,24 +767,47 @@ static int resident_wgs(K kernel, int block)
     return per_cu * cus;
 }
 
+// at most 2 workgroups (8 waves) per CU: each wave then walks several row
+// groups, which amortizes its x slice and keeps a load in flight
+template <class K>
+static int gemv2_cap(K kernel)
+{
+    int dev = 0, cus = 0;
+    const int res = resident_wgs(kernel, 256);
+    if (res == 0 || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    return res < 2 * cus ? res : 2 * cus;
+}
+
 template <int T, int R>
 static hipError_t launch_b1_regs(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                                  hipStream_t s)
 {
-    // at most 2 workgroups (8 waves) per CU: each wave then walks several
-    // row groups, which amortizes its x slice and keeps a load in flight
     static int cap = 0;   // per-process cache (one device model)
-    if (cap == 0) {
-        int dev = 0, cus = 0;
-        const int res = resident_wgs(gemv2_kernel<T, R>, 256);
-        if (res == 0 || hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return hipErrorInvalidValue;
-        cap = res < 2 * cus ? res : 2 * cus;
-    }
-    const int64_t want = ((n + R - 1) / R + 3) / 4;
-    const dim3 grid((unsigned)(want < cap ? want : cap)), block(256);
+    if (cap == 0 && (cap = gemv2_cap(gemv2_kernel<T, R>)) == 0)
+        return hipErrorInvalidValue;
+    const int64_t nrg = (n + R - 1) / R;
+    // mid-size matrices run best with one workgroup per CU (each wave then
+    // walks two row groups), large ones with two (measured on MI355X)
+    const int64_t lim = nrg <= 4 * (int64_t)cap ? cap / 2 : cap;
+    const int64_t want = (nrg + 3) / 4;
+    const dim3 grid((unsigned)(want < lim ? want : lim)), block(256);
     hipLaunchKernelGGL((gemv2_kernel<T, R>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
+    return hipGetLastError();
+}
+
+template <int T, int R>
+static hipError_t launch_b1_table(const GemvProbs &P, int64_t k, size_t rb, hipStream_t s)
+{
+    static int cap = 0;
+    if (cap == 0 && (cap = gemv2_cap(gemv2m_kernel<T, R>)) == 0)
+        return hipErrorInvalidValue;
+    const int64_t want = ((int64_t)P.rg0[P.np] + 3) / 4;
+    if (want == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)(want < cap ? want : cap)), block(256);
+    hipLaunchKernelGGL((gemv2m_kernel<T, R>), grid, block, 0, s, P, (int)k, (int64_t)rb);
     return hipGetLastError();
 }
 
@@ -725,7 +842,8 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
 {
     if (batch == 1 && rb % 16 == 0) {
         if (k <= 64 * GemvUnit<T>::UE)
-            return launch_b1_regs<T, 2>(w, n, k, rb, x, y, s);
+            return n <= 1024 ? launch_b1_regs<T, 1>(w, n, k, rb, x, y, s)
+                             : launch_b1_regs<T, 2>(w, n, k, rb, x, y, s);
         if (k <= 16384)
             return launch_b1_lds<T, 2, 8, 16384>(w, n, k, rb, x, y, s);
     }
@@ -751,6 +869,51 @@ hipError_t launch_gemv(int type, const void *w, int64_t n, int64_t k, size_t rb,
     case T_Q8_0: return launch_t<T_Q8_0>(wb, n, k, rb, x, batch, y, s);
     case T_Q4_K: return launch_t<T_Q4_K>(wb, n, k, rb, x, batch, y, s);
     case T_Q6_K: return launch_t<T_Q6_K>(wb, n, k, rb, x, batch, y, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int T>
+static hipError_t launch_multi_t(int np, const void *const *w, const int64_t *n, int64_t k, size_t rb,
+                                 const float *const *x, int batch, float *const *y, hipStream_t s)
+{
+    if (batch == 1 && rb % 16 == 0 && k <= 64 * GemvUnit<T>::UE) {
+        for (int base = 0; base < np; base += GEMV_MAXP) {
+            GemvProbs P{};
+            P.np = np - base < GEMV_MAXP ? np - base : GEMV_MAXP;
+            P.rg0[0] = 0;
+            for (int i = 0; i < P.np; ++i) {
+                P.w[i] = (const uint8_t *)w[base + i];
+                P.x[i] = x[base + i];
+                P.y[i] = y[base + i];
+                P.n[i] = (int)n[base + i];
+                P.rg0[i + 1] = P.rg0[i] + (int)((n[base + i] + 1) / 2);
+            }
+            const hipError_t e = launch_b1_table<T, 2>(P, k, rb, s);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
+    // other shapes: one launch per problem
+    for (int i = 0; i < np; ++i) {
+        if (n[i] == 0)
+            continue;
+        const hipError_t e = launch_t<T>((const uint8_t *)w[i], n[i], k, rb, x[i], batch, y[i], s);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gemv_multi(int type, int np, const void *const *w, const int64_t *n, int64_t k, size_t rb,
+                             const float *const *x, int batch, float *const *y, hipStream_t s)
+{
+    switch (type) {
+    case T_Q4_0: return launch_multi_t<T_Q4_0>(np, w, n, k, rb, x, batch, y, s);
+    case T_Q8_0: return launch_multi_t<T_Q8_0>(np, w, n, k, rb, x, batch, y, s);
+    case T_Q4_K: return launch_multi_t<T_Q4_K>(np, w, n, k, rb, x, batch, y, s);
+    case T_Q6_K: return launch_multi_t<T_Q6_K>(np, w, n, k, rb, x, batch, y, s);
     default: return hipErrorInvalidValue;
     }
 }

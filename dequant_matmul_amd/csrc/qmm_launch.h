@@ -17,6 +17,9 @@ hipError_t launch_dequant(int type, const void *w, int64_t n, int64_t k, size_t 
 hipError_t launch_gemv(int type, const void *w, int64_t n, int64_t k, size_t rb, const float *x,
                        int batch, float *y, hipStream_t s);
 
+hipError_t launch_gemv_multi(int type, int np, const void *const *w, const int64_t *n, int64_t k, size_t rb,
+                             const float *const *x, int batch, float *const *y, hipStream_t s);
+
 hipError_t launch_gemm(int type, const void *w, int64_t n, int64_t k, size_t rb, const uint16_t *x,
                        int64_t m, float *y, hipStream_t s);
 

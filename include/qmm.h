@@ -111,6 +111,21 @@ QMM_API int qmm_gemv(int type, const void *w, int64_t n, int64_t k,
              const float *x, int64_t batch, float *y, void *stream);
 
 /*
+ * Grouped decode GEMV: for each problem i < nprob, y[i][b][j] =
+ * sum_l w[i][j][l] * x[i][b][l], all problems sharing the block type, k and
+ * batch -- e.g. the q, k, v projections or the gate and up projections of a
+ * layer.  Small batch-1 problems then share one launch (up to 8 per launch)
+ * instead of one launch each; shimmy "Airframe GPU pipeline" (dispatch
+ * counts) already issues the FFN gate and up projections as one dispatch.
+ * w, n, x, y are host arrays of nprob entries (device pointers / row counts),
+ * read during the call only.  Per problem the same conventions and errors as
+ * qmm_gemv apply; n[i] == 0 problems are skipped; nprob == 0 is a no-op.
+ * Results are identical to nprob separate qmm_gemv calls.
+ */
+QMM_API int qmm_gemv_multi(int type, int nprob, const void *const *w, const int64_t *n, int64_t k,
+                           const float *const *x, int64_t batch, float *const *y, void *stream);
+
+/*
  * Prefill GEMM: y[r][j] = sum_i x[r][i] * w[j][i] for r < m, j < n.
  * x: IEEE fp16 bit patterns [m][k], y: fp32 [m][n].  Weight tiles are decoded
  * to fp16 (round to nearest even) in on-chip memory and fed to fp16 matrix

@@ -15,8 +15,11 @@ LIB = os.path.join(ROOT, "dequant_matmul_amd", "libqmm.so")
 
 def _lib():
     if not os.path.exists(LIB):
-        from dequant_matmul_amd import build
-        build.build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("qmm_hip_build", os.path.join(ROOT, "dequant_matmul_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import dequant_matmul_amd as q
     return q
 
@@ -28,8 +31,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    assert {"qmm_dequant", "qmm_gemv", "qmm_gemm_prefill", "qmm_row_bytes", "qmm_block_elems",
-            "qmm_block_bytes", "qmm_status_str", "qmm_version"} == set(syms)
+    assert {"qmm_dequant", "qmm_gemv", "qmm_gemv_multi", "qmm_gemm_prefill", "qmm_row_bytes",
+            "qmm_block_elems", "qmm_block_bytes", "qmm_status_str", "qmm_version"} == set(syms)
 
 
 def test_library_exports_every_declared_symbol():
@@ -103,6 +106,31 @@ def test_validation_errors_dequant_and_gemm():
     assert L.qmm_gemm_prefill(q.Q4_0, A, 4, 32, A + 8, 8, A, None) == q.ERR_ALIGN
     assert L.qmm_gemm_prefill(q.Q4_0, A, 4, 32, A, 0, None, None) == q.OK
     assert L.qmm_gemm_prefill(q.Q4_0, None, 0, 32, None, 8, None, None) == q.OK
+
+
+def test_validation_errors_gemv_multi():
+    q = _lib()
+    L = q.lib
+    P2 = ctypes.c_void_p * 2
+    N2 = ctypes.c_int64 * 2
+    w, x, y = P2(A, A + 4096), P2(A, A), P2(A, A + 256)
+    n = N2(4, 8)
+    assert L.qmm_gemv_multi(q.Q4_K, 0, None, None, 256, None, 1, None, None) == q.OK
+    assert L.qmm_gemv_multi(q.Q4_K, -1, w, n, 256, x, 1, y, None) == q.ERR_SHAPE
+    assert L.qmm_gemv_multi(q.Q4_K, 2, None, n, 256, x, 1, y, None) == q.ERR_NULL
+    assert L.qmm_gemv_multi(q.Q4_K, 2, w, None, 256, x, 1, y, None) == q.ERR_NULL
+    assert L.qmm_gemv_multi(9, 2, w, n, 256, x, 1, y, None) == q.ERR_TYPE
+    assert L.qmm_gemv_multi(q.Q4_K, 2, w, n, 128, x, 1, y, None) == q.ERR_SHAPE
+    assert L.qmm_gemv_multi(q.Q4_K, 2, w, n, 256, x, 9, y, None) == q.ERR_SHAPE
+    assert L.qmm_gemv_multi(q.Q4_K, 2, w, N2(4, -1), 256, x, 1, y, None) == q.ERR_SHAPE
+    assert L.qmm_gemv_multi(q.Q4_K, 2, P2(A, A + 4), n, 256, x, 1, y, None) == q.ERR_ALIGN
+    assert L.qmm_gemv_multi(q.Q4_K, 2, P2(A, None), n, 256, x, 1, y, None) == q.ERR_NULL
+    assert L.qmm_gemv_multi(q.Q4_K, 2, w, n, 256, P2(A, MIS), 1, y, None) == q.ERR_ALIGN
+    assert L.qmm_gemv_multi(q.Q4_K, 2, w, n, 256, x, 1, P2(A, None), None) == q.ERR_NULL
+    # the second problem is bad: nothing of the first may be enqueued either
+    assert L.qmm_gemv_multi(q.Q4_K, 2, w, N2(4, 8), 256, P2(A, None), 1, y, None) == q.ERR_NULL
+    assert L.qmm_gemv_multi(q.Q4_K, 2, w, n, 256, x, 0, y, None) == q.OK
+    assert L.qmm_gemv_multi(q.Q4_K, 2, P2(None, None), N2(0, 0), 256, x, 1, y, None) == q.OK
 
 
 def test_binding_has_no_cpu_fallback():

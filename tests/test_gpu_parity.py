@@ -245,3 +245,27 @@ def test_native_library_loaded():
     import os
     maps = open("/proc/self/maps").read()
     assert os.path.realpath(q.LIB_PATH) in maps
+
+
+# ------------------------------------------------------------ gemv_multi ---
+
+@pytest.mark.parametrize("t,k,ns", [(G.Q4_K, 4096, [4096, 1024, 1024]), (G.Q4_0, 2048, [5632, 5632]),
+                                    (G.Q6_K, 4096, [1024, 3, 0, 700]), (G.Q8_0, 2048, [37] * 9),
+                                    (G.Q4_K, 14336, [300, 200])])
+@pytest.mark.parametrize("batch", [1, 4])
+def test_gemv_multi_matches_single_calls(t, k, ns, batch):
+    """One grouped call gives bit-identical results to one qmm_gemv call per
+    problem, and each matches the oracle."""
+    say("gemv_multi", G.NAMES[t], k, ns, batch)
+    ws = [G.gen_weights(t, n, k, seed=600 + i) for i, n in enumerate(ns)]
+    xs = [G.gen_x(k, batch, seed=700 + i) for i in range(len(ns))]
+    wd = [upload(w) for w in ws]
+    xd = [upload(x) for x in xs]
+    ys = q.gemv_multi(wd, t, ns, k, xd)
+    for w, n, x, y, a, b in zip(ws, ns, xs, ys, wd, xd):
+        single = q.gemv(a, t, n, k, b).cpu().numpy()
+        got = y.cpu().numpy()
+        assert np.array_equal(got, single)
+        if n:
+            ref, absum = oracle.gemv(t, w, n, k, x)
+            check_tol(got, ref, absum, GEMV_TOL, "gemv_multi")
