@@ -1,5 +1,5 @@
 // qmm_api.cpp -- the C ABI of libqmm.so (declared in include/qmm.h): argument
-// validation on the host, then one kernel launch on the caller's stream.
+// validation on the host, then kernel launches on the caller's stream.
 // Nothing here allocates, synchronizes or keeps state.
 #include <hip/hip_runtime.h>
 

@@ -5,285 +5,573 @@
 // FP16 contraction; instead of dequantizing a whole projection to an FP16
 // scratch buffer and calling a library HGEMM, a fused kernel decodes the
 // weights as it goes.  shimmy "Airframe GPU pipeline" prefills prompts in
-// 512-token chunks; dequantization happens inline inside each matmul.
+// 512-token chunks; dequantization happens inline inside each matmul.  Each
+// weight enters the contraction as fp16_RNE(w), w being its exact fp32
+// dequantized value.
 //
-// gfx950 design (first version)
-//   - Workgroup tile 128 (m) x 128 (n), K step 128; 4 wavefronts in a 2 x 2
-//     grid, each owning a 64 x 64 sub-tile = 4 x 4 blocks of
-//     v_mfma_f32_16x16x32_f16 with fp32 accumulators.
-//   - Each K step, the workgroup decodes the 128 x 128 weight tile straight
-//     from the quantized bytes (one 32-element group per thread-item) to fp32,
-//     rounds to fp16 with round-to-nearest-even, and stores it in LDS as
-//     [n][k]; the X tile is copied to LDS as [m][k].  Rows are padded by
-//     8 halves so the 128-bit fragment reads are bank-conflict free.
-//   - The global loads of step t+1 are issued before the MFMAs of step t
-//     (register double buffering); the decode of step t+1 follows them.
-//   - Ragged M, N and K are handled by zero-filling LDS outside the matrix and
-//     masking the stores.
+// gfx950 design
+//   Measured on MI355X: v_mfma_f32_16x16x32_f16 sustains ~2.0-2.2 PFLOP/s;
+//   VALU work co-issues with MFMA only up to ~3-4 wave instructions per MFMA
+//   before it becomes the limit, and LDS delivers ~128 B/clk per CU.  So:
+//   - Workgroup tile BM (m) x BN (n) = 256 x 128 with 8 wavefronts stacked
+//     along m, each owning 32 x 128 = 2 x 8 MFMA blocks.  Every wave loads
+//     only its own X rows (two waves loading the same X lines doubled the L2
+//     traffic and was 2.5x slower); all share the weight tile.  The decode of
+//     a weight element is shared by BM rows of X.
+//   - Only the weight tile goes through LDS: it is decoded once per workgroup
+//     into fp16 [n][k] (row stride padded by 8 halves, conflict-free 128-bit
+//     fragment reads), double buffered, K step 128.  The decode of tile t+1
+//     runs between the MFMAs of tile t; one barrier per K step.
+//   - X fragments are loaded straight from global memory into the MFMA
+//     operand registers (16 bytes per lane; L2-resident), one K step ahead in
+//     a rolling window.  The raw weight bytes of tile t+2 are requested at the
+//     start of tile t, right after the first X load of the next tile, so the
+//     in-order vmcnt waits for X cover them only a tile later.
+//   - Weight decode to fp16: Q8_0 / Q4_0 codes become exact fp16 integers
+//     (byte permute into 0x64xx = 1024 + byte, then subtract the bias) and one
+//     v_pk_mul_f16 by d rounds d*q exactly once: d*q is exact in fp32, so this
+//     equals fp16_RNE(fp32 w).  Q4_K / Q6_K values are formed in fp32 with one
+//     fma (the exact dequantized fp32 value) and packed with v_cvt_pk_f16_f32.
+//   - Workgroups are remapped so that each XCD (dispatched round-robin) owns a
+//     contiguous run of tiles along n with one X slice, which stays in its L2.
+//   - Ragged m / n: loads clamp to the last valid row, stores are masked (row
+//     r of Y depends only on row r of X and column j only on row j of W).
+//     Ragged K (Q8_0 / Q4_0, K a multiple of 32): 32-wide K sub-steps past K
+//     are skipped.
 #include "qmm_device.h"
 #include "qmm_launch.h"
+
+#include <type_traits>
 
 namespace qmm {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
-constexpr int GBM = 128, GBN = 128, GBK = 128;
-constexpr int GLD = GBK + 8;        // LDS row stride in halves
-constexpr int GITEMS = GBN * (GBK / 32) / 256;   // 32-element weight groups per thread per step = 2
+constexpr int GKT = 128;            // K step
+#ifndef QMM_GEMM_SCHED
+#define QMM_GEMM_SCHED 1
+#endif
+constexpr bool SCHED = QMM_GEMM_SCHED;   // explicit MFMA / VALU interleave
+constexpr int GLD = GKT + 8;        // LDS row stride of the weight tile, halves
 
-// NDW dwords from an even byte address p, realigned in registers, reading
-// only bytes in [p - 2, p + 4*NDW): the last two bytes come from a 2-byte
-// load when p is not 4-byte aligned, so nothing past the range is touched.
+// Unaligned byte runs: NDW dwords starting at an even byte address p are
+// fetched as the NDW aligned dwords at or below p plus a 2-byte tail, reading
+// only bytes in [p - 2, p + 4*NDW); the realignment (v_alignbyte_b32 by
+// sh = p % 4, 0 or 2) happens at decode time, so the loads are not waited for
+// where they are issued.  When p is 4-byte aligned the tail load reads the
+// run's last two bytes instead (unused): it is unconditional -- a load under a
+// branch is waited for at once -- and never touches memory past the run.
 template <int NDW>
-__device__ __forceinline__ void gload_bytes(const uint8_t *p, uint32_t *out)
-{
-    const uintptr_t a = (uintptr_t)p & ~(uintptr_t)3;
-    const uint32_t sh = (uint32_t)((uintptr_t)p & 3u);
-    const uint32_t *q = (const uint32_t *)a;
+struct URun {
     uint32_t d[NDW + 1];
+};
+
+template <int NDW>
+__device__ __forceinline__ uint32_t gload_run(const uint8_t *p, URun<NDW> &r)
+{
+    // pointer arithmetic, not an integer round trip: the pointer keeps its
+    // global address space and the loads stay global_load, not flat_load
+    // (which would also count against the LDS wait counter)
+    const uint32_t sh = (uint32_t)((uintptr_t)p & 3u);
+    const uint32_t *q = (const uint32_t *)(p - sh);
 #pragma unroll
     for (int i = 0; i < NDW; ++i)
-        d[i] = q[i];
-    d[NDW] = sh ? (uint32_t)(*(const uint16_t *)(q + NDW)) : 0u;
-#pragma unroll
-    for (int i = 0; i < NDW; ++i)
-        out[i] = align_bytes(d[i + 1], d[i], sh);
+        r.d[i] = q[i];
+    r.d[NDW] = *(const uint16_t *)((const uint8_t *)(q + NDW) - (2u - sh));
+    return sh;
 }
 
-// Raw bytes of one 32-element weight group, as loaded from global memory.
-template <int T> struct GRaw;
-template <> struct GRaw<T_Q8_0> { uint32_t d; uint32_t c[8]; };
-template <> struct GRaw<T_Q4_0> { uint32_t d; uint32_t c[4]; };
-template <> struct GRaw<T_Q4_K> { uint32_t hd[4]; uint32_t c[8]; };
-template <> struct GRaw<T_Q6_K> { uint32_t dsc; uint32_t ql[8]; uint32_t qh[8]; };
-
-// Load group g (32 elements starting at element 32 g) of a row.
-template <int T>
-__device__ __forceinline__ void gload_group(const uint8_t *row, int g, GRaw<T> &r)
+template <int NDW>
+__device__ __forceinline__ void realign(const URun<NDW> &r, uint32_t sh, uint32_t *out)
 {
-    using F = Fmt<T>;
+#pragma unroll
+    for (int i = 0; i < NDW; ++i)
+        out[i] = align_bytes(r.d[i + 1], r.d[i], sh);
+}
+
+// ------------------------------------------------------- decode units --
+// A unit is 32 weights of one row inside K step t, quarter q (0..3):
+//   Q8_0 / Q4_0  block 4 t + q of the row (one run of 32 elements at 32 q);
+//   Q4_K         16 code bytes of super-block t / 2: low nibbles are 16
+//                elements of sub-block 2p, high nibbles the same 16 of
+//                sub-block 2p + 1 (p = 2 (t % 2) + q / 2);
+//   Q6_K         16 ql bytes and 16 qh bytes of super-block t / 2, half
+//                h = t % 2: 16 elements (l = 16 (q % 2) + i) of each of the
+//                groups g = q / 2 (low nibble) and g + 2 (high nibble).
+template <int T> struct WRaw;
+template <> struct WRaw<T_Q8_0> { uint32_t d; URun<8> c; uint32_t sh; };
+template <> struct WRaw<T_Q4_0> { uint32_t d; URun<4> c; uint32_t sh; };
+template <> struct WRaw<T_Q4_K> { u32x4 hd; u32x4 c; };
+template <> struct WRaw<T_Q6_K> { URun<4> ql; URun<4> qh; uint32_t sc; uint32_t d; uint32_t sh; };
+
+template <int T>
+__device__ __forceinline__ void load_unit(const uint8_t *row, int t, int q, WRaw<T> &r)
+{
     if constexpr (T == T_Q8_0) {
-        const uint8_t *blk = row + (int64_t)g * F::BB;
+        const uint8_t *blk = row + (int64_t)(4 * t + q) * 34;
         r.d = *(const uint16_t *)blk;
-        gload_bytes<8>(blk + 2, r.c);
+        r.sh = gload_run<8>(blk + 2, r.c);
     } else if constexpr (T == T_Q4_0) {
-        const uint8_t *blk = row + (int64_t)g * F::BB;
+        const uint8_t *blk = row + (int64_t)(4 * t + q) * 18;
         r.d = *(const uint16_t *)blk;
-        gload_bytes<4>(blk + 2, r.c);
+        r.sh = gload_run<4>(blk + 2, r.c);
     } else if constexpr (T == T_Q4_K) {
-        const uint8_t *blk = row + (int64_t)(g >> 3) * F::BB;   // 16-byte aligned
-        const int j = g & 7;
-        const u32x4 h = *(const u32x4 *)blk;
-        const u32x4 c0 = *(const u32x4 *)(blk + 16 + 32 * (j >> 1));
-        const u32x4 c1 = *(const u32x4 *)(blk + 32 + 32 * (j >> 1));
-        r.hd[0] = h.x; r.hd[1] = h.y; r.hd[2] = h.z; r.hd[3] = h.w;
-        r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
-        r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
+        const uint8_t *blk = row + (int64_t)(t >> 1) * 144;    // 16-byte aligned
+        r.hd = *(const u32x4 *)blk;
+        r.c = *(const u32x4 *)(blk + 16 + 64 * (t & 1) + 16 * q);
     } else {
-        // 32 elements (h, gq): e = 128h + 32gq + l, l = 0..31
-        const uint8_t *blk = row + (int64_t)(g >> 3) * F::BB;
-        const int part = g & 7, h = part >> 2, gq = part & 3;
-        gload_bytes<8>(blk + 64 * h + 32 * (gq & 1), r.ql);
-        gload_bytes<8>(blk + 128 + 32 * h, r.qh);
-        // the two scales of this group (bytes 192 + 8h + 2gq, +1) and d
-        const uint32_t s2 = *(const uint16_t *)(blk + 192 + 8 * h + 2 * gq);
-        const uint32_t dd = *(const uint16_t *)(blk + 208);
-        r.dsc = s2 | (dd << 16);
+        const uint8_t *blk = row + (int64_t)(t >> 1) * 210;
+        const int h = t & 1, gp = q >> 1, lq = q & 1;
+        // both runs start at the same offset mod 4 as the block
+        r.sh = gload_run<4>(blk + 64 * h + 32 * gp + 16 * lq, r.ql);
+        gload_run<4>(blk + 128 + 32 * h + 16 * lq, r.qh);
+        const uint32_t s0 = blk[192 + 8 * h + 2 * gp + lq];        // scale of group g = gp
+        const uint32_t s1 = blk[192 + 8 * h + 2 * gp + 4 + lq];    // scale of group g = gp + 2
+        r.sc = s0 | (s1 << 8);
+        r.d = *(const uint16_t *)(blk + 208);
     }
 }
 
-__device__ __forceinline__ uint32_t pack2h(float a, float b)
+__device__ __forceinline__ uint32_t h2_bits(half2v v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ half2v bits_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
+
+// fp16_RNE of two fp32 values, packed (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_rne(float a, float b)
 {
-    // round to nearest even (v_cvt_f16_f32), then pack
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+    return h2_bits(__builtin_convertvector((float2v){a, b}, half2v));
 }
 
-// Decode the group's 32 weights to fp16 (as 16 dwords of packed halves).
-template <int T>
-__device__ __forceinline__ void decode_group(const GRaw<T> &r, int g, uint32_t *o)
+// Bytes 2j and 2j+1 of c (j = 0, 1) as the fp16 values 1024 + byte.
+__device__ __forceinline__ uint32_t bytes_1024(uint32_t c, int j)
 {
-    float v[32];
-    if constexpr (T == T_Q8_0) {
-        const float d = h2f(r.d);
+    return __builtin_amdgcn_perm(0x64646464u, c, j ? 0x04030402u : 0x04010400u);
+}
+
+// Decode unit (t, q) to fp16 and store its runs into weight tile row ws
+// (tile-local element offsets).
+// Keep every loaded dword live up to the decode: a dword the decode does not
+// need (e.g. the third Q4_K scale dword in even K steps) would otherwise be
+// reused as a temporary while its load is in flight, and the write-after-write
+// forces a wait for all outstanding loads.
+template <int T>
+__device__ __forceinline__ void keep_raw(const WRaw<T> &r)
+{
+    constexpr int N = sizeof(WRaw<T>) / 4;
+    const uint32_t *v = (const uint32_t *)&r;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            v[4 * i + 0] = d * sb0(r.c[i]); v[4 * i + 1] = d * sb1(r.c[i]);
-            v[4 * i + 2] = d * sb2(r.c[i]); v[4 * i + 3] = d * sb3(r.c[i]);
-        }
-    } else if constexpr (T == T_Q4_0) {
-        const float d = h2f(r.d);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = r.c[i] & 0x0f0f0f0fu, hi = (r.c[i] >> 4) & 0x0f0f0f0fu;
-            v[4 * i + 0] = d * (ub0(lo) - 8.f); v[4 * i + 1] = d * (ub1(lo) - 8.f);
-            v[4 * i + 2] = d * (ub2(lo) - 8.f); v[4 * i + 3] = d * (ub3(lo) - 8.f);
-            v[16 + 4 * i + 0] = d * (ub0(hi) - 8.f); v[16 + 4 * i + 1] = d * (ub1(hi) - 8.f);
-            v[16 + 4 * i + 2] = d * (ub2(hi) - 8.f); v[16 + 4 * i + 3] = d * (ub3(hi) - 8.f);
-        }
-    } else if constexpr (T == T_Q4_K) {
-        const int j = g & 7;
-        uint32_t sc, m;
-        q4k_scale_min(r.hd[1], r.hd[2], r.hd[3], j, sc, m);
-        const float dsc = h2f(r.hd[0] & 0xffffu) * (float)sc;
-        const float dm = h2f(r.hd[0] >> 16) * (float)m;
-        const uint32_t sh = (j & 1) ? 4u : 0u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t q = (r.c[i] >> sh) & 0x0f0f0f0fu;
-            v[4 * i + 0] = __builtin_fmaf(ub0(q), dsc, -dm); v[4 * i + 1] = __builtin_fmaf(ub1(q), dsc, -dm);
-            v[4 * i + 2] = __builtin_fmaf(ub2(q), dsc, -dm); v[4 * i + 3] = __builtin_fmaf(ub3(q), dsc, -dm);
-        }
-    } else {
-        const int part = g & 7, gq = part & 3;
-        const float d = h2f(r.dsc >> 16);
-        const float dsc0 = d * (float)(int8_t)(r.dsc & 0xffu);        // elements l = 0..15
-        const float dsc1 = d * (float)(int8_t)((r.dsc >> 8) & 0xffu); // elements l = 16..31
-        const uint32_t nsh = (gq >= 2) ? 4u : 0u, hsh = 2u * (uint32_t)gq;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t q = ((r.ql[i] >> nsh) & 0x0f0f0f0fu) | (((r.qh[i] >> hsh) & 0x03030303u) << 4);
-            const float ds = (i < 4) ? dsc0 : dsc1;
-            v[4 * i + 0] = ds * (ub0(q) - 32.f); v[4 * i + 1] = ds * (ub1(q) - 32.f);
-            v[4 * i + 2] = ds * (ub2(q) - 32.f); v[4 * i + 3] = ds * (ub3(q) - 32.f);
-        }
+    for (int i = 0; i < N; ++i)
+        asm volatile("" : : "v"(v[i]));
+}
+
+__device__ __forceinline__ void st64(_Float16 *dst, uint32_t a, uint32_t b)
+{
+    *(uint32_t __attribute__((ext_vector_type(2))) *)dst = (uint32_t __attribute__((ext_vector_type(2)))){a, b};
+}
+
+// Decoder of one unit, in four parts of 8 weights (one code dword pair /
+// dword each), so that the decode can be spread between the MFMAs of the four
+// 32-wide sub-steps of a K step.  setup() prepares the scales; part(i, ws)
+// stores its 8 fp16 weights into weight tile row ws.
+template <int T> struct Dec;
+
+template <> struct Dec<T_Q8_0> {
+    half2v d2;
+    int off;
+    __device__ __forceinline__ void setup(const WRaw<T_Q8_0> &r, int, int q)
+    {
+        keep_raw(r);
+        d2 = bits_h2(r.d | (r.d << 16));
+        off = 32 * q;
     }
+    __device__ __forceinline__ void part(const WRaw<T_Q8_0> &r, int i, _Float16 *ws) const
+    {
+        const half2v bias = {(_Float16)1152.f, (_Float16)1152.f};
+        uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        o[i] = pack2h(v[2 * i], v[2 * i + 1]);
-}
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t c = align_bytes(r.c.d[2 * i + h + 1], r.c.d[2 * i + h], r.sh) ^ 0x80808080u;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                o[2 * h + j] = h2_bits((bits_h2(bytes_1024(c, j)) - bias) * d2);   // q exact, one rounding
+        }
+        *(u32x4 *)(ws + off + 8 * i) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+};
 
-template <int T>
-__global__ void __launch_bounds__(256)
+template <> struct Dec<T_Q4_0> {
+    half2v d2;
+    int off;
+    __device__ __forceinline__ void setup(const WRaw<T_Q4_0> &r, int, int q)
+    {
+        keep_raw(r);
+        d2 = bits_h2(r.d | (r.d << 16));
+        off = 32 * q;
+    }
+    __device__ __forceinline__ void part(const WRaw<T_Q4_0> &r, int i, _Float16 *ws) const
+    {
+        const half2v bias = {(_Float16)1032.f, (_Float16)1032.f};
+        const uint32_t c = align_bytes(r.c.d[i + 1], r.c.d[i], r.sh);
+        uint32_t lo[2], hi[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t b = bytes_1024(c, j);                   // [c, 0x64, c', 0x64]
+            lo[j] = h2_bits((bits_h2(b & 0x640f640fu) - bias) * d2);
+            hi[j] = h2_bits((bits_h2(((b >> 4) & 0x000f000fu) | 0x64006400u) - bias) * d2);
+        }
+        st64(ws + off + 4 * i, lo[0], lo[1]);          // elements 4i .. 4i+3
+        st64(ws + off + 16 + 4 * i, hi[0], hi[1]);     // elements 16+4i .. 16+4i+3
+    }
+};
+
+template <> struct Dec<T_Q4_K> {
+    float dsc0, dm0, dsc1, dm1;
+    int base;
+    __device__ __forceinline__ void setup(const WRaw<T_Q4_K> &r, int t, int q)
+    {
+        keep_raw(r);
+        const int p = 2 * (t & 1) + (q >> 1);
+        uint32_t sc0, m0, sc1, m1;
+        q4k_scale_min(r.hd.y, r.hd.z, r.hd.w, 2 * p, sc0, m0);
+        q4k_scale_min(r.hd.y, r.hd.z, r.hd.w, 2 * p + 1, sc1, m1);
+        const float d = h2f(r.hd.x & 0xffffu), dmin = h2f(r.hd.x >> 16);
+        // high nibbles convert as 16 q: the 1/16 goes into their scale (exact,
+        // so the fma still yields the exact fp32 value, rounded once)
+        dsc0 = d * (float)sc0;
+        dm0 = dmin * (float)m0;
+        dsc1 = d * (float)sc1 * 0.0625f;
+        dm1 = dmin * (float)m1;
+        base = 64 * (q >> 1) + 16 * (q & 1);
+    }
+    __device__ __forceinline__ void part(const WRaw<T_Q4_K> &r, int i, _Float16 *ws) const
+    {
+        const uint32_t c = i == 0 ? r.c.x : i == 1 ? r.c.y : i == 2 ? r.c.z : r.c.w;
+        const uint32_t lo = opaque(c & 0x0f0f0f0fu), hi = opaque(c & 0xf0f0f0f0u);
+        st64(ws + base + 4 * i,
+             pack_rne(__builtin_fmaf(ub0(lo), dsc0, -dm0), __builtin_fmaf(ub1(lo), dsc0, -dm0)),
+             pack_rne(__builtin_fmaf(ub2(lo), dsc0, -dm0), __builtin_fmaf(ub3(lo), dsc0, -dm0)));
+        st64(ws + base + 32 + 4 * i,
+             pack_rne(__builtin_fmaf(ub0(hi), dsc1, -dm1), __builtin_fmaf(ub1(hi), dsc1, -dm1)),
+             pack_rne(__builtin_fmaf(ub2(hi), dsc1, -dm1), __builtin_fmaf(ub3(hi), dsc1, -dm1)));
+    }
+};
+
+template <> struct Dec<T_Q6_K> {
+    float ds0, nb0, ds1, nb1;
+    uint32_t hs0;
+    int base;
+    __device__ __forceinline__ void setup(const WRaw<T_Q6_K> &r, int, int q)
+    {
+        keep_raw(r);
+        const int gp = q >> 1, lq = q & 1;
+        const float d = h2f(r.d);
+        ds0 = d * (float)(int8_t)(r.sc & 0xffu);          // group gp
+        ds1 = d * (float)(int8_t)((r.sc >> 8) & 0xffu);   // group gp + 2
+        nb0 = -32.f * ds0;                                // fma(q, ds, -32 ds) = ds (q - 32), rounded once
+        nb1 = -32.f * ds1;
+        hs0 = 2u * (uint32_t)gp;
+        base = 32 * gp + 16 * lq;
+    }
+    __device__ __forceinline__ void part(const WRaw<T_Q6_K> &r, int i, _Float16 *ws) const
+    {
+        const uint32_t ql = align_bytes(r.ql.d[i + 1], r.ql.d[i], r.sh);
+        const uint32_t qh = align_bytes(r.qh.d[i + 1], r.qh.d[i], r.sh);
+        const uint32_t q0 = opaque((ql & 0x0f0f0f0fu) | (((qh >> hs0) & 0x03030303u) << 4));
+        const uint32_t q1 = opaque(((ql >> 4) & 0x0f0f0f0fu) | (((qh >> (hs0 + 4u)) & 0x03030303u) << 4));
+        st64(ws + base + 4 * i,
+             pack_rne(__builtin_fmaf(ub0(q0), ds0, nb0), __builtin_fmaf(ub1(q0), ds0, nb0)),
+             pack_rne(__builtin_fmaf(ub2(q0), ds0, nb0), __builtin_fmaf(ub3(q0), ds0, nb0)));
+        st64(ws + base + 64 + 4 * i,
+             pack_rne(__builtin_fmaf(ub0(q1), ds1, nb1), __builtin_fmaf(ub1(q1), ds1, nb1)),
+             pack_rne(__builtin_fmaf(ub2(q1), ds1, nb1), __builtin_fmaf(ub3(q1), ds1, nb1)));
+    }
+};
+
+// ---------------------------------------------------------------- kernel --
+// FM x FN MFMA blocks per wave, WM x WN waves; BM = 16 FM WM, BN = 16 FN WN.
+template <int T, int FM, int FN, int WM, int WN, int XD>
+struct GemmCfg {
+    static constexpr int MW = 16 * FM, NW = 16 * FN;
+    static constexpr int BM = MW * WM, BN = NW * WN;
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int UNITS = 4 * BN;              // decode units per K step
+    static constexpr int UPT = UNITS / NT;            // per thread
+    static_assert(UNITS % NT == 0 && UPT >= 1, "decode units must divide evenly");
+    static constexpr int LDS_HALVES = 2 * BN * GLD;
+};
+
+template <int T, int FM, int FN, int WM, int WN, int XD>
+__global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint16_t *__restrict__ x, int m,
-            float *__restrict__ y)
+            float *__restrict__ y, int nnt, int tiles, int ksplit, int remap)
 {
-    __shared__ __attribute__((aligned(16))) _Float16 As[GBM * GLD];
-    __shared__ __attribute__((aligned(16))) _Float16 Bs[GBN * GLD];
+    using C = GemmCfg<T, FM, FN, WM, WN, XD>;
+    __shared__ __attribute__((aligned(16))) _Float16 Ws[C::LDS_HALVES];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * GBN, m0 = blockIdx.y * GBM;
-    const int nk = (k + GBK - 1) / GBK;
-    const int ngroups = k >> 5;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
 
-    // per-thread load assignment
-    // X tile: 128 rows x 16 chunks of 8 halves -> 8 chunks per thread
-    // W tile: 128 rows x 4 groups -> 2 items per thread (row = tid/2 + 0/64... )
-    u32x4 xa[8];
-    GRaw<T> wr[GITEMS];
+    // Workgroup b = kc * tiles + tile: K chunk kc of the tile (split K adds
+    // the chunks into a zeroed Y).  XCD-aware tile order: workgroup b runs on
+    // XCD b % 8; give each XCD a contiguous range of tile ids (m-major), i.e.
+    // one X slice and a run of n.
+    const int kc = (int)blockIdx.x / tiles;
+    int b = (int)blockIdx.x - kc * tiles;
+    if (remap) {
+        const int per = tiles >> 3;
+        b = (b & 7) * per + (b >> 3);
+    }
+    const int mt = b / nnt, nt = b - mt * nnt;
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    const int nkt_all = (k + GKT - 1) / GKT;
+    const int chunk = (nkt_all + ksplit - 1) / ksplit;
+    const int kt0 = kc * chunk;
+    const int nkt = min(kt0 + chunk, nkt_all);   // end of this chunk's steps
 
-    auto load_step = [&](int kt) __attribute__((always_inline)) {
-        const int kb = kt * GBK;
+    // ---- X fragment addressing (A operand: row lane%16, k 8*(lane/16)..+7)
+    const uint16_t *xrow[FM];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + 256 * i;          // 0..2047
-            const int r = c >> 4, ch = c & 15;
-            const int gm = m0 + r, gk = kb + 8 * ch;
-            if (gm < m && gk < k)
-                xa[i] = *(const u32x4 *)(x + (int64_t)gm * k + gk);
-            else
-                xa[i] = u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int i = 0; i < FM; ++i) {
+        const int r = min(m0 + wm * C::MW + 16 * i + (lane & 15), m - 1);
+        xrow[i] = x + (int64_t)r * k + 8 * (lane >> 4);
+    }
+    // rolling window of XD sub-steps: sub-step (t, s) lives in slot (4t + s) % XD
+    static_assert(XD == 2 || XD == 4, "X prefetch distance");
+    half8 xa[XD][FM];
+    auto load_x = [&](int t, int s) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < GITEMS; ++it) {
-            const int item = tid + 256 * it;      // 0..511
-            const int r = item >> 2, gl = item & 3;
-            const int gn = n0 + r, g = (kb >> 5) + gl;
-            if (gn < n && g < ngroups)
-                gload_group<T>(w + (int64_t)gn * rb, g, wr[it]);
-        }
+        for (int i = 0; i < FM; ++i)
+            xa[s % XD][i] = *(const half8 *)(xrow[i] + GKT * t + 32 * s);
     };
 
-    auto store_step = [&](int kt) __attribute__((always_inline)) {
-        const int kb = kt * GBK;
+    // ---- weight units of this thread
+    const uint8_t *wrow[C::UPT];
+    int uq[C::UPT], ucol[C::UPT];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = tid + 256 * i;
-            const int r = c >> 4, ch = c & 15;
-            *(u32x4 *)(As + r * GLD + 8 * ch) = xa[i];
-        }
+    for (int u = 0; u < C::UPT; ++u) {
+        const int id = tid + C::NT * u;
+        ucol[u] = id >> 2;
+        uq[u] = id & 3;
+        wrow[u] = w + (int64_t)min(n0 + ucol[u], n - 1) * rb;
+    }
+    WRaw<T> wr[2][C::UPT];
+    // (full: step t lies wholly inside K, which always holds for 256-element
+    // super-blocks since K is then a multiple of 256)
+    auto load_w = [&](int par, int t, bool full) __attribute__((always_inline)) {
 #pragma unroll
-        for (int it = 0; it < GITEMS; ++it) {
-            const int item = tid + 256 * it;
-            const int r = item >> 2, gl = item & 3;
-            const int gn = n0 + r, g = (kb >> 5) + gl;
-            uint32_t o[16];
-            if (gn < n && g < ngroups) {
-                decode_group<T>(wr[it], g, o);
-            } else {
+        for (int u = 0; u < C::UPT; ++u)
+            if (full || Fmt<T>::BE == 256 || 4 * t + uq[u] < (k >> 5))
+                load_unit<T>(wrow[u], t, uq[u], wr[par][u]);
+    };
+    // decode of step t in four parts (part i between the MFMAs of sub-step i)
+    Dec<T> dec[C::UPT];
+    auto decode_w = [&](int par, int t, _Float16 *dst, bool full, int i) __attribute__((always_inline)) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o[i] = 0u;
+        for (int u = 0; u < C::UPT; ++u)
+            if (full || Fmt<T>::BE == 256 || 4 * t + uq[u] < (k >> 5)) {
+                if (i == 0)
+                    dec[u].setup(wr[par][u], t, uq[u]);
+                dec[u].part(wr[par][u], i, dst + ucol[u] * GLD);
             }
-            u32x4 *dst = (u32x4 *)(Bs + r * GLD + 32 * gl);
-            dst[0] = u32x4{o[0], o[1], o[2], o[3]};
-            dst[1] = u32x4{o[4], o[5], o[6], o[7]};
-            dst[2] = u32x4{o[8], o[9], o[10], o[11]};
-            dst[3] = u32x4{o[12], o[13], o[14], o[15]};
-        }
     };
 
-    float4v acc[4][4];
+    float4v acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    const int bro = (wn * C::NW + (lane & 15)) * GLD + 8 * (lane >> 4);   // B fragment offset
+
+    // One K step t with compile-time buffer parity PAR (= t % 2).  FULL: t is
+    // not among the last three steps, so every step, load and decode of the
+    // body is in range and the body has no branches (a branch around a load
+    // makes the compiler wait for it at once).
+    auto tile = [&](auto par_c, auto full_c, int t) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_c)::value;
+        constexpr bool FULL = decltype(full_c)::value;
+        const _Float16 *wcur = Ws + PAR * C::BN * GLD;
+        _Float16 *wnext = Ws + (1 - PAR) * C::BN * GLD;
+        const bool nx = FULL || t + 1 < nkt;
+        // weight fragments of step s + 1 are read from LDS while the MFMAs of
+        // step s run (two register sets)
+        half8 bf[2][FN];
+        auto read_b = [&](int s, half8 *dst) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                dst[j] = *(const half8 *)(wcur + bro + 16 * j * GLD + 32 * s);
+        };
+        if (FULL || GKT * t < k)
+            read_b(0, bf[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3 && (FULL || GKT * t + 32 * (s + 1) < k))
+                read_b(s + 1, bf[(s + 1) & 1]);
+            if (FULL || GKT * t + 32 * s < k) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[s % XD][i], bf[s & 1][j], acc[i][j], 0, 0, 0);
+            }
+            // FULL: a load past the last step re-reads the last step instead
+            // (in range, never used), so the body stays free of branches
+            {   // X of sub-step s + XD into the slot just consumed
+                const int tn = t + (s + XD) / 4, sn = (s + XD) % 4;
+                if (FULL)
+                    load_x(min(tn, nkt - 1), sn);
+                else if (tn < nkt && GKT * tn + 32 * sn < k)
+                    load_x(tn, sn);
+            }
+            if (s == 0 && (FULL || t + 2 < nkt))
+                load_w(PAR, FULL ? min(t + 2, nkt - 1) : t + 2, FULL);
+            if (nx)
+                decode_w(1 - PAR, FULL ? min(t + 1, nkt - 1) : t + 1, wnext, FULL, s);
+            if constexpr (FULL && SCHED) {
+                // interleave: the next sub-step's LDS reads and the X loads
+                // first, then each MFMA followed by ~2 VALU instructions of
+                // the decode, then its LDS writes
+                __builtin_amdgcn_sched_group_barrier(0x100, FN, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, FM, 0);
+#pragma unroll
+                for (int g = 0; g < FM * FN; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+            }
+        }
+        __syncthreads();
+    };
+
+    // prologue: X of the first step, raw weights of the first two, decode the first
+#pragma unroll
+    for (int s = 0; s < XD; ++s)
+        if (GKT * kt0 + 32 * s < k)
+            load_x(kt0, s);
+    load_w(0, kt0, false);
+    if (kt0 + 1 < nkt)
+        load_w(1, kt0 + 1, false);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+        decode_w(0, kt0, Ws, false, i);
+    __syncthreads();
 
-    load_step(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();
-        store_step(kt);
-        __syncthreads();
-        if (kt + 1 < nk)
-            load_step(kt + 1);
-        const int fr = lane & 15, fk = 8 * (lane >> 4);
-#pragma unroll
-        for (int kk = 0; kk < GBK / 32; ++kk) {
-            half8 a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *(const half8 *)(As + (wm * 64 + 16 * i + fr) * GLD + 32 * kk + fk);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = *(const half8 *)(Bs + (wn * 64 + 16 * j + fr) * GLD + 32 * kk + fk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using BT = std::integral_constant<bool, true>;
+    using BF = std::integral_constant<bool, false>;
+    // A step is FULL when it and every step it loads or decodes lie wholly
+    // inside K, loads past the last step being clamped to it.  When K is a
+    // multiple of 128 (always for 256-element super-blocks) every step is;
+    // otherwise only the last one is partial and the last pairs take the
+    // general path.
+    const bool whole = (k % GKT) == 0 || nkt < nkt_all;
+    const int full_pairs_end = whole ? nkt - 1 : nkt - 4;
+    int t = kt0;
+    for (; t < full_pairs_end; t += 2) {
+        tile(I0{}, BT{}, t);
+        tile(I1{}, BT{}, t + 1);
+    }
+    if (whole && t < nkt) {   // odd number of steps: the last one alone
+        tile(I0{}, BT{}, t);
+        ++t;
+    }
+    while (t < nkt) {
+        tile(I0{}, BF{}, t);
+        if (++t < nkt)
+            tile(I1{}, BF{}, t);
+        ++t;
     }
 
-    // C fragment: lane holds rows 4*(lane/16) + 0..3, column lane%16
+    // C fragment: lane holds rows 4*(lane/16) + 0..3 (of X), column lane%16 (of W)
     const int cr = 4 * (lane >> 4), cc = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int gn = n0 + wn * 64 + 16 * j + cc;
+        for (int j = 0; j < FN; ++j) {
+            const int gn = n0 + wn * C::NW + 16 * j + cc;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int gm = m0 + wm * 64 + 16 * i + cr + r;
-                if (gm < m && gn < n)
-                    y[(int64_t)gm * n + gn] = acc[i][j][r];
+                const int gm = m0 + wm * C::MW + 16 * i + cr + r;
+                if (gm < m && gn < n) {
+                    if (ksplit > 1)
+                        unsafeAtomicAdd(y + (int64_t)gm * n + gn, acc[i][j][r]);   // global_atomic_add_f32
+                    else
+                        y[(int64_t)gm * n + gn] = acc[i][j][r];
+                }
             }
         }
+}
+
+// Compute units of the current device (cached per device).
+static int cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s);
+
+template <int T, int FM, int FN, int WM, int WN, int XD>
+hipError_t launch_cfg(const uint8_t *w, int64_t n, int64_t k, size_t rb, const uint16_t *x, int64_t m, float *y,
+                      hipStream_t s)
+{
+    using C = GemmCfg<T, FM, FN, WM, WN, XD>;
+    const int nmt = (int)((m + C::BM - 1) / C::BM), nnt = (int)((n + C::BN - 1) / C::BN);
+    const int tiles = nmt * nnt;
+    const int remap = (tiles % 8 == 0) ? 1 : 0;
+    // Split K when the tiles alone leave most CUs idle (e.g. 512 x 4096: 64
+    // tiles): up to 4 chunks of at least 8 K steps, added with fp32 atomics
+    // into a zeroed Y (the order of the additions is not fixed).
+    const int nkt = (int)((k + GKT - 1) / GKT);
+    int ksplit = 1;
+    while (ksplit < 4 && tiles * ksplit * 2 <= cu_count() && nkt / (ksplit * 2) >= 8)
+        ksplit *= 2;
+    if (ksplit > 1) {
+        const hipError_t e = launch_fill_zero(y, m * n, s);
+        if (e != hipSuccess)
+            return e;
+    }
+    hipLaunchKernelGGL((gemm_kernel<T, FM, FN, WM, WN, XD>), dim3((unsigned)(tiles * ksplit)), dim3(C::NT), 0, s, w,
+                       (int)n, (int)k, (int64_t)rb, x, (int)m, y, nnt, tiles, ksplit, remap);
+    return hipGetLastError();
+}
+
+template <int T>
+hipError_t launch_gemm_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, const uint16_t *x, int64_t m,
+                         float *y, hipStream_t s)
+{
+    // 8 wavefronts stacked along m, each 16 FM x 128: every wave reads its own
+    // X rows (no wave loads X another wave loads), all share the weight tile
+    if (m <= 128)
+        return launch_cfg<T, 1, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);   // 128 x 128
+    return launch_cfg<T, 2, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);       // 256 x 128
 }
 
 hipError_t launch_gemm(int type, const void *w, int64_t n, int64_t k, size_t rb, const uint16_t *x, int64_t m,
                        float *y, hipStream_t s)
 {
-    const dim3 grid((unsigned)((n + GBN - 1) / GBN), (unsigned)((m + GBM - 1) / GBM)), block(256);
     const uint8_t *wb = (const uint8_t *)w;
     switch (type) {
-    case T_Q4_0: hipLaunchKernelGGL(gemm_kernel<T_Q4_0>, grid, block, 0, s, wb, (int)n, (int)k, (int64_t)rb, x, (int)m, y); break;
-    case T_Q8_0: hipLaunchKernelGGL(gemm_kernel<T_Q8_0>, grid, block, 0, s, wb, (int)n, (int)k, (int64_t)rb, x, (int)m, y); break;
-    case T_Q4_K: hipLaunchKernelGGL(gemm_kernel<T_Q4_K>, grid, block, 0, s, wb, (int)n, (int)k, (int64_t)rb, x, (int)m, y); break;
-    case T_Q6_K: hipLaunchKernelGGL(gemm_kernel<T_Q6_K>, grid, block, 0, s, wb, (int)n, (int)k, (int64_t)rb, x, (int)m, y); break;
+    case T_Q4_0: return launch_gemm_t<T_Q4_0>(wb, n, k, rb, x, m, y, s);
+    case T_Q8_0: return launch_gemm_t<T_Q8_0>(wb, n, k, rb, x, m, y, s);
+    case T_Q4_K: return launch_gemm_t<T_Q4_K>(wb, n, k, rb, x, m, y, s);
+    case T_Q6_K: return launch_gemm_t<T_Q6_K>(wb, n, k, rb, x, m, y, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 __global__ void fill_zero_kernel(float *p, int64_t count)

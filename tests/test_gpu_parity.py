@@ -209,6 +209,40 @@ def test_gemm_one_hot_rows_give_fp16_weights(t):
         assert np.array_equal(got[r], W16[:, c]), (r, c)
 
 
+def _tiny_scales(t, w, n, k, rng):
+    """Overwrite every fp16 scale field (d, and dmin for Q4_K) with a random
+    subnormal fp16 (bits 0x0001..0x03ff), so that many dequantized weights are
+    fp16 subnormals or need rounding near the subnormal range."""
+    w = w.copy().reshape(n, -1)
+    bb, be = G.BLOCK_BYTES[t], G.BLOCK_ELEMS[t]
+    nb = k // be
+    offs = {G.Q8_0: [0], G.Q4_0: [0], G.Q4_K: [0, 2], G.Q6_K: [208]}[t]
+    for b in range(nb):
+        for o in offs:
+            bits = rng.integers(1, 0x400, size=n).astype(np.uint16)
+            w[:, b * bb + o] = (bits & 0xff).astype(np.uint8)
+            w[:, b * bb + o + 1] = (bits >> 8).astype(np.uint8)
+    return w.reshape(-1)
+
+
+@pytest.mark.parametrize("t", TYPES)
+def test_gemm_one_hot_subnormal_scales(t):
+    """One-hot rows with subnormal fp16 scales: the weights entering the MFMA
+    are still exactly fp16_RNE of the fp32 dequantized values (no flush to
+    zero of subnormal inputs or results anywhere in the decode)."""
+    n, k = 140, 4 * G.BLOCK_ELEMS[t]
+    w = _tiny_scales(t, G.gen_weights(t, n, k, seed=9), n, k, np.random.default_rng(19))
+    W16 = oracle.dequant(t, w, n, k).astype(np.float16).astype(np.float32)
+    assert np.any((W16 != 0) & (np.abs(W16) < 2.0 ** -14)), "no subnormal weights in the case"
+    cols = list(range(0, k, max(1, k // 37)))[:40] + [k - 1]
+    X = np.zeros((len(cols), k), np.float16)
+    for r, c in enumerate(cols):
+        X[r, c] = 1.0
+    got = q.gemm_prefill(upload(w), t, n, k, upload(X)).cpu().numpy()
+    for r, c in enumerate(cols):
+        assert np.array_equal(got[r], W16[:, c]), (r, c)
+
+
 @pytest.mark.parametrize("t,n", [(G.Q8_0, 14336), (G.Q8_0, 4096), (G.Q4_K, 14336), (G.Q4_K, 4096),
                                  (G.Q4_0, 4096), (G.Q6_K, 4096)])
 def test_gemm_prefill_workload_shapes(t, n):
