@@ -40,7 +40,7 @@ FP16_PEAK_TFLOPS = 2500.0
 # same counters read for a plain 256 MiB device copy (reads x2.0, writes
 # x1.0).  It describes the kernels it was measured on: set it to None when
 # they change, until the counters are taken again.
-TRAFFIC = 3695210
+TRAFFIC = None   # re-measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE after kernel changes
 
 
 def log(*a):

@@ -92,6 +92,22 @@ __device__ __forceinline__ float wave_sum(float v)
     return (r0 + r1) + (r2 + r3);
 }
 
+// Sum over the 64 lanes, valid in lanes 48..63 only (read it from lane 63):
+// the four row sums as in wave_sum, then row_bcast:15 adds row 0 into row 1
+// and row 2 into row 3, and row_bcast:31 adds rows 0+1 into row 3.  The
+// additions associate as (r2 + r3) + (r0 + r1), i.e. the same value as
+// wave_sum, without the four v_readlane round trips.
+__device__ __forceinline__ float wave_sum_hi(float v)
+{
+    v += dpp_f(v, 0xB1);
+    v += dpp_f(v, 0x4E);
+    v += dpp_f(v, 0x141);
+    v += dpp_f(v, 0x140);
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
+    return v;
+}
+
 // Q4_K: 6-bit scale and min of sub-block j from the 3 dwords holding the 12
 // packed bytes (byte i of the 12 is byte i%4 of dword i/4).  For j < 4 the
 // scale / min are the low 6 bits of bytes j and j+4; for j >= 4 they are the

@@ -40,6 +40,8 @@
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
+#include <type_traits>
+
 namespace qmm {
 
 // ------------------------------------------------------------ unit layout --
@@ -170,34 +172,106 @@ __device__ __forceinline__ float dot4_s(uint32_t q, const f32x4 &x, float acc)
 
 __device__ __forceinline__ float sum4(const f32x4 &v) { return (v.x + v.y) + (v.z + v.w); }
 
+// Batch 1 keeps four partial sums per accumulator (one per byte position):
+// four independent FMA chains instead of one long dependent chain, which at
+// a few waves per SIMD is bound by the FMA latency.  Larger batches already
+// have B independent chains.
+__device__ __forceinline__ f32x4 dot4_u(uint32_t q, const f32x4 &x, f32x4 acc)
+{
+    acc.x = __builtin_fmaf(ub0(q), x.x, acc.x);
+    acc.y = __builtin_fmaf(ub1(q), x.y, acc.y);
+    acc.z = __builtin_fmaf(ub2(q), x.z, acc.z);
+    acc.w = __builtin_fmaf(ub3(q), x.w, acc.w);
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 dot4_s(uint32_t q, const f32x4 &x, f32x4 acc)
+{
+    acc.x = __builtin_fmaf(sb0(q), x.x, acc.x);
+    acc.y = __builtin_fmaf(sb1(q), x.y, acc.y);
+    acc.z = __builtin_fmaf(sb2(q), x.z, acc.z);
+    acc.w = __builtin_fmaf(sb3(q), x.w, acc.w);
+    return acc;
+}
+
+template <int B> struct AccOf { typedef float type; };
+template <> struct AccOf<1> { typedef f32x4 type; };
+__device__ __forceinline__ float fin(float v) { return v; }
+__device__ __forceinline__ float fin(const f32x4 &v) { return sum4(v); }
+template <class A> __device__ __forceinline__ A zero_acc();
+template <> __device__ __forceinline__ float zero_acc<float>() { return 0.f; }
+template <> __device__ __forceinline__ f32x4 zero_acc<f32x4>() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
 // x of run j for batch b, from LDS (padded layout) ...
 template <int T, int XS>
 struct XFromLds {
+    static constexpr bool PRE = false;   // offset sums of x computed alongside the dot
     const float *xs;
     int u;
     __device__ __forceinline__ f32x4 operator()(int j, int b) const
     {
         return *(const f32x4 *)(xs + b * XS + xpad<GemvUnit<T>::UE>(run_elem<T>(u, j)));
     }
+    __device__ __forceinline__ float sum(int, int) const { return 0.f; }
 };
 
-// ... or from registers (batch 1).
+// Sums of x over the groups of a unit that share a constant code offset:
+// Q4_0 the block (1), Q4_K the two sub-blocks (2), Q6_K the four 16-element
+// scale groups (4); Q8_0 has no offset.
+template <int T> struct XSumCount { static constexpr int N = T == T_Q4_0 ? 1 : T == T_Q4_K ? 2 : T == T_Q6_K ? 4 : 1; };
+
+// ... or from registers (batch 1): the lane's unit is the same for every row,
+// so its offset sums are computed once (sums()) and reused.
 template <int T>
 struct XFromRegs {
+    static constexpr bool PRE = true;
     const f32x4 *xr;
+    const float *xsum;
     __device__ __forceinline__ f32x4 operator()(int j, int) const { return xr[j]; }
+    __device__ __forceinline__ float sum(int, int g) const { return xsum[g]; }
 };
+
+template <int T>
+__device__ __forceinline__ void unit_x_sums(const f32x4 *xr, float *xs)
+{
+    if constexpr (T == T_Q4_0) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a += sum4(xr[i]) + sum4(xr[4 + i]);
+        xs[0] = a;
+    } else if constexpr (T == T_Q4_K) {
+        float a = 0.f, b = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a += sum4(xr[i]);
+            b += sum4(xr[8 + i]);
+        }
+        xs[0] = a;
+        xs[1] = b;
+    } else if constexpr (T == T_Q6_K) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a += sum4(xr[4 * g + i]);
+            xs[g] = a;
+        }
+    } else {
+        xs[0] = 0.f;
+    }
+}
 
 // Contribution of lane-unit u of R rows to acc[r][b].
 template <int T, int B, int R, class XG>
 __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const XG &xg, float (&acc)[R][B])
 {
+    typedef typename AccOf<B>::type AccT;
     if constexpr (T == T_Q8_0) {
-        float s[R][B];
+        AccT s[R][B];
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int b = 0; b < B; ++b) s[r][b] = 0.f;
+            for (int b = 0; b < B; ++b) s[r][b] = zero_acc<AccT>();
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             f32x4 xv[B];
@@ -212,15 +286,16 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
         for (int r = 0; r < R; ++r) {
             const float d = h2f(raw[r].d);
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d, s[r][b], acc[r][b]);
+            for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d, fin(s[r][b]), acc[r][b]);
         }
     } else if constexpr (T == T_Q4_0) {
-        float slo[R][B], shi[R][B], xsum[B];
+        AccT slo[R][B], shi[R][B];
+        float xsum[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             xsum[b] = 0.f;
 #pragma unroll
-            for (int r = 0; r < R; ++r) slo[r][b] = shi[r][b] = 0.f;
+            for (int r = 0; r < R; ++r) slo[r][b] = shi[r][b] = zero_acc<AccT>();
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -229,7 +304,8 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             for (int b = 0; b < B; ++b) {
                 xl[b] = xg(i, b);
                 xh[b] = xg(4 + i, b);
-                xsum[b] += sum4(xl[b]) + sum4(xh[b]);
+                if constexpr (!XG::PRE)
+                    xsum[b] += sum4(xl[b]) + sum4(xh[b]);
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -242,13 +318,16 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
                 }
             }
         }
+        if constexpr (XG::PRE)
+#pragma unroll
+            for (int b = 0; b < B; ++b) xsum[b] = xg.sum(b, 0);
         // d * sum (q - 8) x = d * (slo + shi/16 - 8 sum x)
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const float d = h2f(raw[r].d);
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                const float t = __builtin_fmaf(shi[r][b], 0.0625f, slo[r][b]);
+                const float t = __builtin_fmaf(fin(shi[r][b]), 0.0625f, fin(slo[r][b]));
                 acc[r][b] = __builtin_fmaf(d, __builtin_fmaf(-8.f, xsum[b], t), acc[r][b]);
             }
         }
@@ -268,12 +347,13 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             dm0[r] = dmin * (float)m0;
             dm1[r] = dmin * (float)m1;
         }
-        float s0[R][B], s1[R][B], x0[B], x1[B];
+        AccT s0[R][B], s1[R][B];
+        float x0[B], x1[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             x0[b] = x1[b] = 0.f;
 #pragma unroll
-            for (int r = 0; r < R; ++r) s0[r][b] = s1[r][b] = 0.f;
+            for (int r = 0; r < R; ++r) s0[r][b] = s1[r][b] = zero_acc<AccT>();
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -282,8 +362,10 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             for (int b = 0; b < B; ++b) {
                 xl[b] = xg(i, b);
                 xh[b] = xg(8 + i, b);
-                x0[b] += sum4(xl[b]);
-                x1[b] += sum4(xh[b]);
+                if constexpr (!XG::PRE) {
+                    x0[b] += sum4(xl[b]);
+                    x1[b] += sum4(xh[b]);
+                }
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
@@ -296,12 +378,18 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
                 }
             }
         }
+        if constexpr (XG::PRE)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                x0[b] = xg.sum(b, 0);
+                x1[b] = xg.sum(b, 1);
+            }
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                float t = dsc0[r] * s0[r][b];
-                t = __builtin_fmaf(dsc1[r], s1[r][b], t);
+                float t = dsc0[r] * fin(s0[r][b]);
+                t = __builtin_fmaf(dsc1[r], fin(s1[r][b]), t);
                 t = __builtin_fmaf(-dm0[r], x0[b], t);
                 t = __builtin_fmaf(-dm1[r], x1[b], t);
                 acc[r][b] += t;
@@ -322,14 +410,15 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             dsc[r][2] = d * (float)(int8_t)(raw[r].sc[1] >> sh);          // scale 8h + 4 + hf
             dsc[r][3] = d * (float)(int8_t)(raw[r].sc[1] >> (16 + sh));   // scale 8h + 6 + hf
         }
-        float s[R][B][4], xgs[B][4];
+        AccT s[R][B][4];
+        float xgs[B][4];
 #pragma unroll
         for (int b = 0; b < B; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 xgs[b][g] = 0.f;
 #pragma unroll
-                for (int r = 0; r < R; ++r) s[r][b][g] = 0.f;
+                for (int r = 0; r < R; ++r) s[r][b][g] = zero_acc<AccT>();
             }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -339,7 +428,8 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     xv[b] = xg(4 * g + i, b);
-                    xgs[b][g] += sum4(xv[b]);
+                    if constexpr (!XG::PRE)
+                        xgs[b][g] += sum4(xv[b]);
                 }
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
@@ -355,6 +445,11 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
                 }
             }
         }
+        if constexpr (XG::PRE)
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) xgs[b][g] = xg.sum(b, g);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -362,7 +457,7 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
                 float t = 0.f;
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    t = __builtin_fmaf(dsc[r][g], __builtin_fmaf(-32.f, xgs[b][g], s[r][b][g]), t);
+                    t = __builtin_fmaf(dsc[r][g], __builtin_fmaf(-32.f, xgs[b][g], fin(s[r][b][g])), t);
                 acc[r][b] += t;
             }
     }
@@ -468,8 +563,12 @@ struct TableProbs {
     __device__ __forceinline__ int N(int pp) const { return P.n[pp]; }
 };
 
-template <int T, int R, class PS>
-__device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint32_t *ws)
+// NW wavefronts per workgroup.  xl (X_LDS): the workgroup first copies the
+// single problem's x into LDS, and each wave takes its lane slice from there
+// (instead of every wave reading all of x from L2, which with many waves
+// costs more L2 traffic than the weights).
+template <int T, int R, class PS, int NW = 4, bool X_LDS = false>
+__device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint32_t *ws, float *xl = nullptr)
 {
     constexpr int UE = GemvUnit<T>::UE, NRUN = GemvUnit<T>::NRUN;
     using S = SegStage<T, R>;
@@ -477,29 +576,46 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int gw = blockIdx.x * 4 + wave, tw = gridDim.x * 4;
+    const int gw = blockIdx.x * NW + wave, tw = gridDim.x * NW;
+    if constexpr (X_LDS) {
+        // padded layout (4 floats per unit): lanes read their unit slices at a
+        // stride of UE + 4 floats, which keeps the 128-bit reads off a single
+        // bank group
+        const float *x = P.X(0);
+        for (int i = 4 * (int)threadIdx.x; i < k; i += 4 * 64 * NW)
+            *(f32x4 *)(xl + xpad<UE>(i)) = *(const f32x4 *)(x + i);
+        __syncthreads();
+    }
+    // each wave takes a contiguous run of row groups (run lengths differ by
+    // at most one, so every wave has work when there are enough), so that
+    // its results form contiguous runs of y (stored 64 at a time, below)
     const int nrg = P.total_rg(R);
-    const int nit = gw < nrg ? (nrg - gw + tw - 1) / tw : 0;
+    const int q = nrg / tw, rem = nrg - q * tw;    // one 32-bit division
+    const int rgs = gw * q + min(gw, rem);
+    const int nit = q + (gw < rem ? 1 : 0);
     const bool active = lane < k / UE;
     const int cpr = k / Fmt<T>::BE * Fmt<T>::BB / 16;
 
     // problem and first row of item it (past the end: the last item)
     auto locate = [&](int it, int &pp, int &row0) __attribute__((always_inline)) {
         it = min(it, max(nit - 1, 0));
-        const int rg = gw + tw * it;
+        const int rg = rgs + it;
         pp = P.find(rg);
         row0 = (rg - P.rg_begin(pp)) * R;
     };
 
-    // this lane's slice of x for the current problem
+    // this lane's slice of x for the current problem, and its offset sums
     f32x4 xr[NRUN];
+    float xsum[XSumCount<T>::N];
     auto load_x = [&](int pp) __attribute__((always_inline)) {
-        const float *x = P.X(pp);
 #pragma unroll
-        for (int j = 0; j < NRUN; ++j)
-            xr[j] = *(const f32x4 *)(x + (active ? run_elem<T>(lane, j) : 0));
+        for (int j = 0; j < NRUN; ++j) {
+            const int e = active ? run_elem<T>(lane, j) : 0;
+            xr[j] = X_LDS ? *(const f32x4 *)(xl + xpad<UE>(e)) : *(const f32x4 *)(P.X(pp) + e);
+        }
+        unit_x_sums<T>(xr, xsum);
     };
-    const XFromRegs<T> xg{xr};
+    const XFromRegs<T> xg{xr, xsum};
 
     float acc[R][1];
 #pragma unroll
@@ -510,42 +626,99 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     int xp = p0;
     load_x(xp);
 
+    // Two items of weight bytes in flight while an item computes: three
+    // prefetch register sets, the loop unrolled by three so that each has a
+    // fixed place.  An item computes in place and its set is reloaded (for
+    // item it + 3) only after its last use, with a scheduling barrier in
+    // between: a reload scheduled above the use would need other registers
+    // and a copy back at the loop edge, which waits for the load.  Prefetches
+    // past the wave's last item read offset 0 in every lane (one cache line,
+    // no branch: a load under a branch is waited for at once).  Lanes past k
+    // compute on offset-0 bytes and contribute 0 (select, not branch).
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    // Row results collect in lane (row - blk_row) of res and leave as one
+    // coalesced store per 64 rows (or at a problem change / the end); a
+    // one-lane store per row costs a divergent branch and a store each.
+    float res = 0.f;
+    int blk_row = 0, blk_cnt = 0, blk_pp = 0;
+    auto flush = [&]() __attribute__((always_inline)) {
+        if (blk_cnt > 0) {
+            const int row = blk_row + lane;
+            if (lane < blk_cnt && row < P.N(blk_pp))
+                P.Y(blk_pp)[row] = res;
+        }
+        blk_cnt = 0;
+    };
+    auto finish = [&](int pp, int row0) __attribute__((always_inline)) {
+        if (blk_cnt + R > 64 || (blk_cnt > 0 && pp != blk_pp))
+            flush();
+        if (blk_cnt == 0) {
+            blk_row = row0;
+            blk_pp = pp;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float v = wave_sum_hi(active ? acc[r][0] : 0.f);
+            const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+            res = lane == blk_cnt + r ? tot : res;
+            acc[r][0] = 0.f;
+        }
+        blk_cnt += R;
+    };
     if constexpr (DIRECT) {
-        URaw<T> pr[R];
-        auto load = [&](int it) __attribute__((always_inline)) {
+        URaw<T> pr[3][R];
+        auto load = [&](int it, URaw<T> (&dst)[R]) __attribute__((always_inline)) {
             int pp, row0;
             locate(it, pp, row0);
             const uint8_t *w = P.W(pp);
             const int n = P.N(pp);
+            const bool live = it < nit;   // past the wave's last item: a dummy load of offset 0
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const bool ok = active && row0 + r < n;
-                raw_from_global_q4k(w + (ok ? (int64_t)(row0 + r) * rb : 0), ok ? lane : 0, pr[r]);
+                const bool ok = live && active && row0 + r < n;
+                raw_from_global_q4k(w + (ok ? (int64_t)(row0 + r) * rb : 0), ok ? lane : 0, dst[r]);
             }
         };
-        load(0);
-        for (int it = 0; it < nit; ++it) {
+        load(0, pr[0]);
+        load(1, pr[1]);
+        load(2, pr[2]);
+        auto step = [&](auto bc, int it) __attribute__((always_inline)) {
+            constexpr int B = decltype(bc)::value;
             int pp, row0;
             locate(it, pp, row0);
             if (pp != xp) {   // wave-uniform: the next problem's x
                 xp = pp;
                 load_x(xp);
             }
-            URaw<T> cur[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) cur[r] = pr[r];
-            load(it + 1);
-            if (active)
-                unit_dot<T, 1, R>(cur, lane, xg, acc);
-            reduce_store<R>(acc, row0, P.N(pp), lane, P.Y(pp));
+            unit_dot<T, 1, R>(pr[B], lane, xg, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            load(it + 3, pr[B]);
+            finish(pp, row0);
+        };
+        int it = 0;
+        for (; it + 2 < nit; it += 3) {
+            step(I0{}, it);
+            step(I1{}, it + 1);
+            step(I2{}, it + 2);
         }
+        if (it < nit)
+            step(I0{}, it);
+        if (it + 1 < nit)
+            step(I1{}, it + 1);
+        flush();
     } else {
+        // LDS-staged rows: one prefetch register set suffices, since it is
+        // emptied into LDS before being refilled (no copy of an in-flight
+        // load); measured faster than three sets for these types
         uint32_t *mw = ws + wave * S::LDS_DW;
         S st;
         auto load = [&](int it) __attribute__((always_inline)) {
             int pp, row0;
             locate(it, pp, row0);
-            st.load(P.W(pp), rb, P.N(pp), row0, 0, cpr, lane);
+            // past the wave's last item: no row is in range, every chunk reads offset 0
+            st.load(P.W(pp), rb, it < nit ? P.N(pp) : 0, row0, 0, cpr, lane);
         };
         load(0);
         for (int it = 0; it < nit; ++it) {
@@ -558,15 +731,14 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
             st.store(mw, lane);
             wave_lds_sync();
             load(it + 1);
-            if (active) {
-                URaw<T> cur[R];
+            URaw<T> cur[R];
 #pragma unroll
-                for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
-                unit_dot<T, 1, R>(cur, lane, xg, acc);
-            }
-            reduce_store<R>(acc, row0, P.N(pp), lane, P.Y(pp));
+            for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
+            unit_dot<T, 1, R>(cur, lane, xg, acc);
+            finish(pp, row0);
             wave_lds_sync();
         }
+        flush();
     }
 }
 
@@ -578,6 +750,19 @@ gemv2_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
     __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : 4 * SegStage<T, R>::LDS_DW];
     const OneProb P{w, x, y, n};
     gemv2_body<T, R>(P, k, rb, ws);
+}
+
+// Batch 1, one problem, x staged in LDS, NW wavefronts per workgroup (one
+// workgroup per CU: 16 waves, 4 per SIMD, hide the weight latency).
+template <int T, int R, int NW>
+__global__ void __launch_bounds__(64 * NW)
+gemv3_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
+             float *__restrict__ y)
+{
+    __shared__ __attribute__((aligned(16))) float xl[64 * (GemvUnit<T>::UE + 4)];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : NW * SegStage<T, R>::LDS_DW];
+    const OneProb P{w, x, y, n};
+    gemv2_body<T, R, OneProb, NW, true>(P, k, rb, ws, xl);
 }
 
 template <int T, int R>
@@ -780,6 +965,25 @@ static int gemv2_cap(K kernel)
     return res < 2 * cus ? res : 2 * cus;
 }
 
+// Batch 1 through gemv3 (x staged in LDS, 8 waves per workgroup): at most
+// one workgroup per CU, each wave a contiguous run of rows.
+template <int T, int R, int NW>
+static hipError_t launch_b1_xlds(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
+                                 hipStream_t s)
+{
+    static int cus = 0;   // per-process cache (one device model)
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return hipErrorInvalidValue;
+    }
+    const int64_t want = ((n + R - 1) / R + NW - 1) / NW;
+    const dim3 grid((unsigned)(want < cus ? want : cus)), block(64 * NW);
+    hipLaunchKernelGGL((gemv3_kernel<T, R, NW>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
+    return hipGetLastError();
+}
+
 template <int T, int R>
 static hipError_t launch_b1_regs(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                                  hipStream_t s)
@@ -841,9 +1045,14 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
                            hipStream_t s)
 {
     if (batch == 1 && rb % 16 == 0) {
-        if (k <= 64 * GemvUnit<T>::UE)
+        if (k <= 64 * GemvUnit<T>::UE) {
+            // Q4_K (the cheapest decode per byte, so the most rows in flight
+            // per byte): x from LDS, 8 waves per CU, one row per item
+            if (T == T_Q4_K && n >= 2048)
+                return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
             return n <= 1024 ? launch_b1_regs<T, 1>(w, n, k, rb, x, y, s)
                              : launch_b1_regs<T, 2>(w, n, k, rb, x, y, s);
+        }
         if (k <= 16384)
             return launch_b1_lds<T, 2, 8, 16384>(w, n, k, rb, x, y, s);
     }
