@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized-weight matmul on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix]
 
 A step is one decode pass over the TinyLlama-shaped Q4_0 weight stream:
 22 layers x (q, k, v, o, gate, up, down) = 154 GEMVs at batch 1 on one
@@ -40,7 +40,7 @@ FP16_PEAK_TFLOPS = 2500.0
 # same counters read for a plain 256 MiB device copy (reads x2.0, writes
 # x1.0).  It describes the kernels it was measured on: set it to None when
 # they change, until the counters are taken again.
-TRAFFIC = None   # re-measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE after kernel changes
+TRAFFIC = 3374693   # bytes per launch, averaged over one pass (gemv2_kernel<0,2/1>, gemv1_kernel<0,...>)
 
 
 def log(*a):
@@ -52,7 +52,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--secondary", choices=["all", "none"], default="all")
+    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix"], default="all",
+                   help="which secondary workloads to run after the primary line's (all by default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU oracle sample")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -372,29 +373,34 @@ def main():
         line["cpu_baseline"] = cpu_baseline(host, args.cpu_seconds)
     del host
 
-    if args.secondary == "all":
+    if args.secondary != "none":
+        want = (lambda s: args.secondary in ("all", s))
         sec = {}
-        log("secondary: Q8_0 single matrix")
-        sec["q8_0_2048"] = sec_cfg1(torch, q, args.steps, args.warmup, dev)
         del probs
         torch.cuda.empty_cache()
-        log("secondary: Llama-3-8B Q4_K set")
-        wts = build_weights(torch, 3, dev)
-        sec["llama3_8b_q4_k"] = sec_stream(torch, q, 3, wts, 1, args.steps, args.warmup, dev,
-                                           "Llama-3-8B-shaped Q4_K, 224 GEMVs, batch 1")
-        del wts
-        torch.cuda.empty_cache()
-        log("secondary: prefill GEMMs")
-        sec["prefill_512"] = sec_prefill(torch, q, args.steps, args.warmup, dev)
-        log("secondary: Q4_K_M-style mix weights")
-        wts = build_weights(torch, 5, dev)
-        for b in (1, 4, 8):
-            log("secondary: Q4_K_M-style mix, batch", b)
-            sec["q4_k_m_mix_b%d" % b] = sec_stream(
-                torch, q, 5, wts, b, max(3, args.steps // 2), 2, dev,
-                "Q4_K_M-style mix (v, down, LM head 128256x4096 in Q6_K), 225 GEMVs, batch %d" % b,
-                with_gemm=True)
-        del wts
+        if want("q8_0"):
+            log("secondary: Q8_0 single matrix")
+            sec["q8_0_2048"] = sec_cfg1(torch, q, args.steps, args.warmup, dev)
+        if want("q4_k"):
+            log("secondary: Llama-3-8B Q4_K set")
+            wts = build_weights(torch, 3, dev)
+            sec["llama3_8b_q4_k"] = sec_stream(torch, q, 3, wts, 1, args.steps, args.warmup, dev,
+                                               "Llama-3-8B-shaped Q4_K, 224 GEMVs, batch 1")
+            del wts
+            torch.cuda.empty_cache()
+        if want("prefill"):
+            log("secondary: prefill GEMMs")
+            sec["prefill_512"] = sec_prefill(torch, q, args.steps, args.warmup, dev)
+        if want("mix"):
+            log("secondary: Q4_K_M-style mix weights")
+            wts = build_weights(torch, 5, dev)
+            for b in (1, 4, 8):
+                log("secondary: Q4_K_M-style mix, batch", b)
+                sec["q4_k_m_mix_b%d" % b] = sec_stream(
+                    torch, q, 5, wts, b, max(3, args.steps // 2), 2, dev,
+                    "Q4_K_M-style mix (v, down, LM head 128256x4096 in Q6_K), 225 GEMVs, batch %d" % b,
+                    with_gemm=True)
+            del wts
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 
