@@ -1056,6 +1056,8 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
         if (k <= 16384)
             return launch_b1_lds<T, 2, 8, 16384>(w, n, k, rb, x, y, s);
     }
+    if (gemv_mfma_supported(T, batch))
+        return launch_gemv_mfma(T, w, n, k, rb, x, batch, y, s);
     switch (batch) {
     case 1: return launch_tbr<T, 1, 2>(w, n, k, rb, x, y, s);
     case 2: return launch_tbr<T, 2, 2>(w, n, k, rb, x, y, s);

@@ -1,0 +1,503 @@
+// qmm_gemv_mfma.hip -- decode GEMV for small batches (2..8 activation rows)
+// on the fp16 matrix cores, for the K-quant formats Q4_K and Q6_K.
+//
+// At batch 1 the decode GEMV is a pure weight stream (qmm_gemv.hip).  With a
+// few activation rows the same weight bytes feed B dot products each, and the
+// fp32 vector ALU would need 2B flops per weight on top of the decode; the
+// matrix cores take that work instead.  The contraction per super-block of
+// 256 weights is one 16 x 16 x 256 product:
+//
+//   A (16 x 256, fp16): activation rows.  Row 2b holds the high part of
+//     x[b] * 2^sh, row 2b+1 the remainder (both fp16, round to nearest even),
+//     so hi + lo carries about 22 significant bits of the fp32 input.  sh is
+//     a power of two per (row b, super-block) that puts the block's largest
+//     |x| in [2^14, 2^15): no fp16 overflow, and the remainder stays normal
+//     for every element within 2^-17 of the largest.
+//   B (256 x 16, fp16): 16 weight rows, decoded to code x sub-block scale --
+//     q * sc for Q4_K (at most 945), (q - 32) * scale for Q6_K (at most 2048
+//     in magnitude).  Both are integers that fp16 holds exactly, formed by one
+//     fused fp16 multiply-add from a biased code.
+//   C (16 x 16, fp32): the sum over the super-block; then, per row j and
+//     batch b, y[b][j] += 2^-sh * (d * (C[2b][j] + C[2b+1][j])) in fp32 --
+//     the super-block scale d (and for Q4_K the dmin * sum_j m_j X_j term,
+//     one more 16x16x16 product of the eight 6-bit mins against the
+//     activation sums of the eight sub-blocks) never passes through fp16.
+//
+// Block layouts: Q4_K fp16 d, fp16 dmin, 12 bytes of packed 6-bit scales and
+// mins, 128 code bytes (sub-block j of 32: nibble j%2 of bytes 32(j/2)..+31);
+// Q6_K 128 bytes of low nibbles, 64 bytes of 2-bit high parts, 16 int8
+// scales (one per 16 weights), fp16 d (shimmy "Architecture", Quantization
+// table; dotLLM "GPU Inference", Quantization on GPU table, as read with the
+// Llama-3-8B Q4_K and Q4_K_M-mix workloads).
+//
+// Work split.  One workgroup of 8 waves per compute unit, persistent over a
+// contiguous range of 16-row tiles.  The waves split K: wave w owns a
+// contiguous run of super-blocks and keeps their A fragments in registers
+// (converted once, reused for every tile), streams the B bytes of its run for
+// each tile (the next tile's bytes in flight while the current one is decoded)
+// and leaves a partial sum per tile in LDS; after every 8 tiles the partials
+// are added in a fixed order and stored, so results do not depend on timing.
+// When a wave's run is longer than two super-blocks, it is taken two at a time
+// (fragments converted again per 8 tiles) and the partials accumulate in LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qmm_device.h"
+#include "qmm_launch.h"
+
+namespace qmm {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float fl2 __attribute__((ext_vector_type(2)));
+typedef float fl4 __attribute__((ext_vector_type(4)));
+
+constexpr int GB_W = 8;    // waves per workgroup
+constexpr int GB_TC = 8;   // tiles between cross-wave reductions
+constexpr int GB_C = 2;    // super-blocks per wave held in registers at a time
+
+__device__ __forceinline__ h2 as_h2(uint32_t v) { return __builtin_bit_cast(h2, v); }
+__device__ __forceinline__ uint32_t as_u(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// fp16 round-to-nearest-even of two fp32 values, packed (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pk_rne(float a, float b)
+{
+    return as_u(__builtin_convertvector((fl2){a, b}, h2));
+}
+
+// Bytes i and j of v as the fp16 pair (bias + byte_i, bias + byte_j), bias
+// given by the high byte hb: 0x64 -> 1024 (spacing 1), 0x60 -> 512 (the byte
+// is then twice the value added).
+__device__ __forceinline__ uint32_t byte_pair(uint32_t hb4, uint32_t v, uint32_t sel)
+{
+    return __builtin_amdgcn_perm(hb4, v, sel);
+}
+
+// ------------------------------------------------------------- A fragments --
+// The k order inside a super-block.  MFMA i (0..7) of a super-block takes, in
+// lane group G = lane/16, the 8 elements with lane-local index
+// 8i + {0, 2, 1, 3, 4, 6, 5, 7} of the 64 elements that group owns: pairs of
+// elements two apart share one packed register on the weight side, where a
+// dword holds 4 code bytes and one mask takes bytes 0 and 2.
+//   Q4_K: group G owns elements 64G .. 64G+63 (sub-blocks 2G, 2G+1).
+//   Q6_K: group G owns, for g' = 0..3, the 16 elements
+//         128(G/2) + 32g' + 16(G%2) + 0..15 (lane-local index 16g' + l).
+struct XFrag {
+    h8 a[8];      // A operands of the 8 MFMAs of the super-block
+    h4 a2;        // Q4_K: sub-block sums (min term), 16x16x16 A operand
+    float xs0;    // 2^-sh of batch rows 2G and 2G+1 (C layout of this lane)
+    float xs1;
+};
+
+template <int T>
+__device__ __forceinline__ void load_x(const float *__restrict__ xb, int G, fl4 v[16])
+{
+    if (T == T_Q4_K) {
+        const fl4 *p = (const fl4 *)(xb + 64 * G);
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            v[q] = p[q];
+    } else {
+        const float *p = xb + 128 * (G >> 1) + 16 * (G & 1);
+#pragma unroll
+        for (int gp = 0; gp < 4; ++gp)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v[4 * gp + q] = *(const fl4 *)(p + 32 * gp + 4 * q);
+    }
+}
+
+__device__ __forceinline__ float vget(const fl4 v[16], int j) { return v[j >> 2][j & 3]; }
+
+template <int T>
+__device__ __forceinline__ void convert_x(fl4 v[16], XFrag &f)
+{
+    const int lane = threadIdx.x & 63, r = lane & 15, G = lane >> 4;
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+        m = fmaxf(fmaxf(m, fmaxf(fabsf(v[q][0]), fabsf(v[q][1]))), fmaxf(fabsf(v[q][2]), fabsf(v[q][3])));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    // m in [2^(e-1), 2^e): scale the block so that it lands in [2^14, 2^15)
+    const int e = __builtin_amdgcn_frexp_expf(m);
+    const int sh = min(max(15 - e, -128), 126);
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            v[q][c] = __builtin_amdgcn_ldexpf(v[q][c], sh);
+    // row 2b keeps the fp16 value, row 2b+1 the fp16 of the remainder
+    const float pm = (r & 1) ? 1.f : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        uint32_t o[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+            const int j0 = 8 * i + (pr & 1) + 4 * (pr >> 1), j1 = j0 + 2;
+            const float a = vget(v, j0), b = vget(v, j1);
+            const h2 h = as_h2(pk_rne(a, b));
+            o[pr] = pk_rne(fmaf(-pm, (float)h[0], a), fmaf(-pm, (float)h[1], b));
+        }
+        f.a[i] = __builtin_bit_cast(h8, (u32x4){o[0], o[1], o[2], o[3]});
+    }
+    if (T == T_Q4_K) {
+        // sums of sub-blocks 2G and 2G+1 (of the scaled values)
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            s0 += (v[q][0] + v[q][1]) + (v[q][2] + v[q][3]);
+            s1 += (v[q + 8][0] + v[q + 8][1]) + (v[q + 8][2] + v[q + 8][3]);
+        }
+        // 16x16x16 A operand, lane (r, G): k slots 4G..4G+3 of row r.  Row 2b:
+        // slots 0..7 = high parts of the eight sums, 8..15 = remainders; row
+        // 2b+1 = 0.  Sums are below 2^20; the factor 2^-6 keeps them in fp16.
+        const int src = 32 * (G & 1) + r;     // lanes holding sub-blocks 4(G&1) .. +3
+        const float x0 = __shfl(s0, src) * 0x1p-6f, x1 = __shfl(s1, src) * 0x1p-6f;
+        const float x2 = __shfl(s0, src + 16) * 0x1p-6f, x3 = __shfl(s1, src + 16) * 0x1p-6f;
+        const uint32_t h01 = pk_rne(x0, x1), h23 = pk_rne(x2, x3);
+        const h2 a01 = as_h2(h01), a23 = as_h2(h23);
+        const uint32_t l01 = pk_rne(x0 - (float)a01[0], x1 - (float)a01[1]);
+        const uint32_t l23 = pk_rne(x2 - (float)a23[0], x3 - (float)a23[1]);
+        const bool odd = (r & 1) != 0, lo = G >= 2;
+        const uint32_t w0 = odd ? 0u : (lo ? l01 : h01), w1 = odd ? 0u : (lo ? l23 : h23);
+        f.a2 = __builtin_bit_cast(h4, (uint32_t __attribute__((ext_vector_type(2)))){w0, w1});
+    }
+    const float xs = __builtin_amdgcn_ldexpf(1.f, -sh);
+    f.xs0 = __shfl(xs, 4 * G);        // row 4G   = batch 2G
+    f.xs1 = __shfl(xs, 4 * G + 2);    // row 4G+2 = batch 2G+1
+}
+
+// ------------------------------------------------------------- B operands --
+template <int T> struct WRawB;
+
+// Q4_K, lane (n, g): header (d, dmin, 12 scale bytes) and code bytes
+// 32g .. 32g+31 (sub-blocks 2g and 2g+1).
+template <> struct WRawB<T_Q4_K> {
+    u32x4 hd, c0, c1;
+};
+
+// Q6_K, lane (n, g), h = g/2, l = g%2: ql bytes 64h+16l (+16) and 64h+32+16l
+// (+16), qh bytes 32h+16l (+16), scale bytes 8h..8h+7, d.  Super-blocks are
+// only 2-byte aligned (210 bytes): every run is read as aligned dwords plus a
+// trailing 16-bit word and realigned at decode time.
+template <> struct WRawB<T_Q6_K> {
+    u32x4 q0, q1, qh;
+    uint32_t q0t, q1t, qht;
+    uint32_t s0, s1, st;
+    uint32_t d;
+    uint32_t sh;
+};
+
+template <int T>
+__device__ __forceinline__ void load_b(const uint8_t *__restrict__ p, int64_t off, int g, WRawB<T> &r);
+
+template <>
+__device__ __forceinline__ void load_b<T_Q4_K>(const uint8_t *__restrict__ p, int64_t off, int g, WRawB<T_Q4_K> &r)
+{
+    const uint8_t *b = p + off;
+    r.hd = *(const u32x4 *)b;
+    r.c0 = *(const u32x4 *)(b + 16 + 32 * g);
+    r.c1 = *(const u32x4 *)(b + 32 + 32 * g);
+}
+
+template <>
+__device__ __forceinline__ void load_b<T_Q6_K>(const uint8_t *__restrict__ p, int64_t off, int g, WRawB<T_Q6_K> &r)
+{
+    const uint32_t sh = (uint32_t)off & 2u;        // p is 16-byte aligned
+    const uint8_t *a = p + (off - sh);             // dword aligned
+    const int h = g >> 1, l = g & 1;
+    const int o0 = 64 * h + 16 * l, o1 = o0 + 32, oh = 128 + 32 * h + 16 * l, os = 192 + 8 * h;
+    r.q0 = *(const u32x4 *)(a + o0);
+    r.q0t = *(const uint16_t *)(a + o0 + 16);
+    r.q1 = *(const u32x4 *)(a + o1);
+    r.q1t = *(const uint16_t *)(a + o1 + 16);
+    r.qh = *(const u32x4 *)(a + oh);
+    r.qht = *(const uint16_t *)(a + oh + 16);
+    const uint32_t *sp = (const uint32_t *)(a + os);
+    r.s0 = sp[0];
+    r.s1 = sp[1];
+    r.st = *(const uint16_t *)(a + os + 8);
+    r.d = *(const uint16_t *)(p + off + 208);
+    r.sh = sh;
+}
+
+// Keep every loaded dword live up to the decode, so that no register of a
+// load in flight is reused as a temporary (the write-after-write would wait
+// for all outstanding loads).
+template <int T>
+__device__ __forceinline__ void keep(const WRawB<T> &r)
+{
+    constexpr int N = sizeof(WRawB<T>) / 4;
+    const uint32_t *v = (const uint32_t *)&r;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        asm volatile("" : : "v"(v[i]));
+}
+
+__device__ __forceinline__ h2 h2c(float v) { return (h2){(_Float16)v, (_Float16)v}; }
+
+// One super-block of one 16-row tile: 8 (+1) MFMAs and the fp32 scaling into
+// acc0 / acc1 (batch rows 2g, 2g+1 of weight row n of the tile).
+template <int T>
+__device__ __forceinline__ void sb_dot(const WRawB<T> &r, const XFrag &f, int g, float &acc0, float &acc1);
+
+template <>
+__device__ __forceinline__ void sb_dot<T_Q4_K>(const WRawB<T_Q4_K> &r, const XFrag &f, int g, float &acc0,
+                                               float &acc1)
+{
+    keep(r);
+    const uint32_t hy = r.hd.y, hz = r.hd.z, hw = r.hd.w;
+    // 6-bit scales / mins of sub-blocks 0..3 (lo) and 4..7 (hi), one per byte
+    const uint32_t sclo = hy & 0x3f3f3f3fu;
+    const uint32_t schi = (hw & 0x0f0f0f0fu) | ((hy >> 2) & 0x30303030u);
+    const uint32_t mlo = hz & 0x3f3f3f3fu;
+    const uint32_t mhi = ((hw >> 4) & 0x0f0f0f0fu) | ((hz >> 2) & 0x30303030u);
+    const uint32_t sc = (g >= 2 ? schi : sclo) >> (16 * (g & 1));   // bytes: sc_2g, sc_2g+1
+    const uint32_t m4 = (g & 1) ? mhi : mlo;                        // mins 4(g&1) .. +3
+    const h2 k1024 = h2c(1024.f), kn1024 = h2c(-1024.f);
+    const h2 sa = as_h2(byte_pair(0x64646464u, sc, 0x04000400u)) - k1024;   // (sc_2g, sc_2g)
+    const h2 sb = as_h2(byte_pair(0x64646464u, sc, 0x04010401u)) - k1024;   // (sc_2g+1, sc_2g+1)
+    const h2 na = sa * kn1024, nb = sb * kn1024;
+    const uint32_t D[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+    fl4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t0 = 2 * (i & 3), ns = i < 4 ? 0 : 4;
+        const h2 s2 = i < 4 ? sa : sb, n2 = i < 4 ? na : nb;
+        uint32_t o[4];
+#pragma unroll
+        for (int pr = 0; pr < 4; ++pr) {
+            const uint32_t dw = D[t0 + (pr >> 1)] >> (ns + 8 * (pr & 1));
+            const h2 code = as_h2((dw & 0x000f000fu) | 0x64006400u);      // 1024 + q
+            o[pr] = as_u(__builtin_elementwise_fma(code, s2, n2));        // q * sc, exact
+        }
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){o[0], o[1], o[2], o[3]}),
+                                                   c, 0, 0, 0);
+    }
+    const uint32_t m01 = as_u(as_h2(byte_pair(0x64646464u, m4, 0x04010400u)) - k1024);
+    const uint32_t m23 = as_u(as_h2(byte_pair(0x64646464u, m4, 0x04030402u)) - k1024);
+    const fl4 c2 = __builtin_amdgcn_mfma_f32_16x16x16f16(
+        f.a2, __builtin_bit_cast(h4, (uint32_t __attribute__((ext_vector_type(2)))){m01, m23}),
+        (fl4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    const float d = h2f(r.hd.x & 0xffffu), dm = h2f(r.hd.x >> 16) * 64.f;
+    acc0 = fmaf(f.xs0, fmaf(d, c[0] + c[1], -dm * c2[0]), acc0);
+    acc1 = fmaf(f.xs1, fmaf(d, c[2] + c[3], -dm * c2[2]), acc1);
+}
+
+template <>
+__device__ __forceinline__ void sb_dot<T_Q6_K>(const WRawB<T_Q6_K> &r, const XFrag &f, int g, float &acc0,
+                                               float &acc1)
+{
+    keep(r);
+    const uint32_t sh = r.sh;
+    const uint32_t Q0[4] = {align_bytes(r.q0.y, r.q0.x, sh), align_bytes(r.q0.z, r.q0.y, sh),
+                            align_bytes(r.q0.w, r.q0.z, sh), align_bytes(r.q0t, r.q0.w, sh)};
+    const uint32_t Q1[4] = {align_bytes(r.q1.y, r.q1.x, sh), align_bytes(r.q1.z, r.q1.y, sh),
+                            align_bytes(r.q1.w, r.q1.z, sh), align_bytes(r.q1t, r.q1.w, sh)};
+    const uint32_t H[4] = {align_bytes(r.qh.y, r.qh.x, sh), align_bytes(r.qh.z, r.qh.y, sh),
+                           align_bytes(r.qh.w, r.qh.z, sh), align_bytes(r.qht, r.qh.w, sh)};
+    // int8 scales 8h + l + 2g' (g' = 0..3): bytes l, l+2 of the two dwords
+    const uint32_t S0 = align_bytes(r.s1, r.s0, sh) ^ 0x80808080u, S1 = align_bytes(r.st, r.s1, sh) ^ 0x80808080u;
+    const uint32_t l = (uint32_t)(g & 1);
+    const uint32_t sel0 = 0x04000400u + l * 0x00010001u, sel1 = sel0 + 0x00020002u;
+    const h2 k1152 = h2c(1152.f), kn544 = h2c(-544.f);
+    h2 s2[4], n2[4];
+#pragma unroll
+    for (int gp = 0; gp < 4; ++gp) {
+        s2[gp] = as_h2(byte_pair(0x64646464u, gp < 2 ? S0 : S1, (gp & 1) ? sel1 : sel0)) - k1152;   // scale
+        n2[gp] = s2[gp] * kn544;
+    }
+    fl4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int gp = i >> 1, t0 = 2 * (i & 1);
+        uint32_t o[4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const uint32_t ql = (gp & 1) ? Q1[t0 + tt] : Q0[t0 + tt];
+            // 2q per byte: low 4 bits from ql (nibble gp/2), bits 4-5 from qh (bits 2gp..2gp+1)
+            const uint32_t lo4 = gp < 2 ? (ql << 1) & 0x1e1e1e1eu : (ql >> 3) & 0x1e1e1e1eu;
+            const int hs = 2 * gp;
+            const uint32_t hi2 = hs <= 5 ? (H[t0 + tt] << (5 - hs)) & 0x60606060u : (H[t0 + tt] >> (hs - 5)) & 0x60606060u;
+            const uint32_t q2 = lo4 | hi2;
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                // bytes (pp, pp+2) -> fp16 512 + q
+                const h2 code = as_h2(byte_pair(0x60606060u, q2, pp ? 0x04030401u : 0x04020400u));
+                o[2 * tt + pp] = as_u(__builtin_elementwise_fma(code, s2[gp], n2[gp]));   // (q-32)*scale, exact
+            }
+        }
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){o[0], o[1], o[2], o[3]}),
+                                                   c, 0, 0, 0);
+    }
+    const float d = h2f(r.d);
+    acc0 = fmaf(f.xs0 * d, c[0] + c[1], acc0);
+    acc1 = fmaf(f.xs1 * d, c[2] + c[3], acc1);
+}
+
+// ------------------------------------------------------------------ kernel --
+// One run of up to two super-blocks (sa, sa+1 if TWO) over cnt tiles from
+// tile0: fragments (if convert), then the tiles with the next tile's bytes in
+// flight; each tile's partial goes to slot[tile][wave][lane] (added to what is
+// there if accumulate).
+template <int T, bool TWO>
+__device__ __forceinline__ void run_piece(const uint8_t *__restrict__ w, int64_t rb, int n, int tile0, int cnt,
+                                          int sa, bool convert, const float *__restrict__ xrow, XFrag (&xf)[GB_C],
+                                          fl2 (*slot)[GB_W][64], bool accumulate)
+{
+    using F = Fmt<T>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, g = lane >> 4;
+    auto off = [&](int tt, int s) -> int64_t {
+        const int row = min((tile0 + tt) * 16 + nl, n - 1);
+        return (int64_t)row * rb + (int64_t)s * F::BB;
+    };
+    WRawB<T> A0, A1, B0, B1;
+    if (convert) {
+        // activations first: the wait for them then leaves the weight loads
+        // below in flight (loads complete in order)
+        fl4 v[16];
+        load_x<T>(xrow + 256 * sa, g, v);
+        load_b<T>(w, off(0, sa), g, A0);
+        if (TWO)
+            load_b<T>(w, off(0, sa + 1), g, A1);
+        convert_x<T>(v, xf[0]);
+        if (TWO) {
+            load_x<T>(xrow + 256 * (sa + 1), g, v);
+            convert_x<T>(v, xf[1]);
+        }
+    } else {
+        load_b<T>(w, off(0, sa), g, A0);
+        if (TWO)
+            load_b<T>(w, off(0, sa + 1), g, A1);
+    }
+    auto tile = [&](const WRawB<T> &r0, const WRawB<T> &r1, int tt) {
+        float a0 = 0.f, a1 = 0.f;
+        sb_dot<T>(r0, xf[0], g, a0, a1);
+        if (TWO)
+            sb_dot<T>(r1, xf[1], g, a0, a1);
+        fl2 part = {a0, a1};
+        if (accumulate)
+            part += slot[tt][wave][lane];
+        slot[tt][wave][lane] = part;
+    };
+    int tt = 0;
+    for (; tt + 2 <= cnt; tt += 2) {
+        load_b<T>(w, off(tt + 1, sa), g, B0);
+        if (TWO)
+            load_b<T>(w, off(tt + 1, sa + 1), g, B1);
+        tile(A0, A1, tt);
+        const int tn = min(tt + 2, cnt - 1);   // past the end: a harmless re-read
+        load_b<T>(w, off(tn, sa), g, A0);
+        if (TWO)
+            load_b<T>(w, off(tn, sa + 1), g, A1);
+        tile(B0, B1, tt + 1);
+    }
+    if (tt < cnt)
+        tile(A0, A1, tt);
+}
+
+template <int T>
+__global__ void __launch_bounds__(64 * GB_W)
+gemvb_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x, int batch,
+             float *__restrict__ y)
+{
+    __shared__ fl2 red[2][GB_TC][GB_W][64];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int S = k / 256;
+    const int s_begin = wave * S / GB_W, s_end = (wave + 1) * S / GB_W;
+    const int npc = (s_end - s_begin + GB_C - 1) / GB_C;
+    const bool multi = S > GB_C * GB_W;       // the same for every wave
+    const int ntiles = (n + 15) >> 4;
+    const int per = ntiles / (int)gridDim.x, rem = ntiles - per * (int)gridDim.x;
+    const int t_begin = (int)blockIdx.x * per + min((int)blockIdx.x, rem);
+    const int t_count = per + ((int)blockIdx.x < rem ? 1 : 0);
+    // activation row of this lane's A rows (rows past the batch repeat the
+    // last one; their outputs are never stored)
+    const float *xrow = x + (int64_t)min((lane & 15) >> 1, batch - 1) * k;
+
+    XFrag xf[GB_C];
+    int buf = 0;
+    for (int c0 = 0; c0 < t_count; c0 += GB_TC, buf ^= 1) {
+        const int cnt = min(GB_TC, t_count - c0);
+        const int tile0 = t_begin + c0;
+        for (int p = 0; p < npc; ++p) {
+            const int sa = s_begin + GB_C * p;
+            const bool convert = multi || c0 == 0;
+            if (sa + 1 < s_end)
+                run_piece<T, true>(w, rb, n, tile0, cnt, sa, convert, xrow, xf, red[buf], p > 0);
+            else
+                run_piece<T, false>(w, rb, n, tile0, cnt, sa, convert, xrow, xf, red[buf], p > 0);
+        }
+        if (npc == 0) {
+            for (int tt = 0; tt < cnt; ++tt)
+                red[buf][tt][wave][lane] = (fl2){0.f, 0.f};
+        }
+        __syncthreads();
+        // fixed-order sum over the waves, one (tile, lane) pair per thread
+        for (int j = threadIdx.x; j < cnt * 64; j += 64 * GB_W) {
+            const int tt = j >> 6, ln = j & 63;
+            fl2 s = red[buf][tt][0][ln];
+#pragma unroll
+            for (int ww = 1; ww < GB_W; ++ww)
+                s += red[buf][tt][ww][ln];
+            const int row = (tile0 + tt) * 16 + (ln & 15), b0 = 2 * (ln >> 4);
+            if (row < n) {
+                if (b0 < batch)
+                    y[(int64_t)b0 * n + row] = s[0];
+                if (b0 + 1 < batch)
+                    y[(int64_t)(b0 + 1) * n + row] = s[1];
+            }
+        }
+        // red is double-buffered: the next chunk writes the other half, and
+        // this half is written again only after the next chunk's barrier
+    }
+}
+
+int cu_count_cached()
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+template <int T>
+hipError_t launch_b(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, int batch, float *y,
+                    hipStream_t s)
+{
+    const int64_t ntiles = (n + 15) / 16;
+    const int grid = (int)(ntiles < cu_count_cached() ? ntiles : cu_count_cached());
+    hipLaunchKernelGGL(gemvb_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, w, (int)n, (int)k, (int64_t)rb, x,
+                       batch, y);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemv_mfma_supported(int type, int batch)
+{
+    return batch >= 2 && batch <= 8 && (type == T_Q4_K || type == T_Q6_K);
+}
+
+hipError_t launch_gemv_mfma(int type, const void *w, int64_t n, int64_t k, size_t rb, const float *x, int batch,
+                            float *y, hipStream_t s)
+{
+    const uint8_t *wb = (const uint8_t *)w;
+    switch (type) {
+    case T_Q4_K: return launch_b<T_Q4_K>(wb, n, k, rb, x, batch, y, s);
+    case T_Q6_K: return launch_b<T_Q6_K>(wb, n, k, rb, x, batch, y, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace qmm

@@ -20,6 +20,12 @@ hipError_t launch_gemv(int type, const void *w, int64_t n, int64_t k, size_t rb,
 hipError_t launch_gemv_multi(int type, int np, const void *const *w, const int64_t *n, int64_t k, size_t rb,
                              const float *const *x, int batch, float *const *y, hipStream_t s);
 
+// Batch 2..8 GEMV on the matrix cores (Q4_K, Q6_K); launch_gemv uses it for
+// the batches and types that gemv_mfma_supported accepts.
+bool gemv_mfma_supported(int type, int batch);
+hipError_t launch_gemv_mfma(int type, const void *w, int64_t n, int64_t k, size_t rb, const float *x, int batch,
+                            float *y, hipStream_t s);
+
 hipError_t launch_gemm(int type, const void *w, int64_t n, int64_t k, size_t rb, const uint16_t *x,
                        int64_t m, float *y, hipStream_t s);
 

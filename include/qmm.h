@@ -102,10 +102,16 @@ QMM_API int qmm_dequant(int type, const void *w, int64_t n, int64_t k, float *ou
 /*
  * Decode GEMV: y[b][j] = sum_i w[j][i] * x[b][i] for b < batch, j < n.
  * x: fp32 [batch][k], y: fp32 [batch][n], 1 <= batch <= 8 (batch 0 = empty).
- * Weights are read once from the quantized bytes and decoded in registers;
- * products and sums are fp32.  (dotLLM "GPU Inference", Custom Kernels
- * table: quantized_gemv_* operating directly on quantized weights; the
- * decode path is memory-bandwidth bound.)
+ * Weights are read once from the quantized bytes and decoded in registers.
+ * Batch 1 (all types) and batch 2..8 of Q8_0 / Q4_0: fp32 products and sums.
+ * Batch 2..8 of Q4_K / Q6_K run on the fp16 matrix cores: per 256-element
+ * block and activation row, x is scaled by a power of two and split into
+ * two fp16 parts (about 22 significant bits), the weights enter as exact
+ * fp16 integers (code x sub-block scale), sums are fp32 and the block
+ * scales are applied in fp32; x must be finite.  All paths are
+ * deterministic.  (dotLLM "GPU Inference", Custom Kernels table:
+ * quantized_gemv_* operating directly on quantized weights; the decode path
+ * is memory-bandwidth bound.)
  */
 QMM_API int qmm_gemv(int type, const void *w, int64_t n, int64_t k,
              const float *x, int64_t batch, float *y, void *stream);

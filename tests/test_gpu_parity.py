@@ -150,6 +150,57 @@ def test_gemv_special_inputs(t):
         check_tol(y8[b:b + 1], ref, absum, GEMV_TOL, "batch-8 column")
 
 
+@pytest.mark.parametrize("t", TYPES)
+def test_gemv_batch_one_hot_exact(t):
+    """Batch 8 with one-hot rows: every output is a single product w * 1,
+    so each row of y must equal a column of the exact dequantized weights."""
+    n, k = 70, 8 * G.BLOCK_ELEMS[t]
+    w = G.gen_weights(t, n, k, seed=15)
+    W = oracle.dequant(t, w, n, k)
+    cols = [0, 5, 31, 32, k // 2 + 3, k - 256 + 17, k - 2, k - 1]
+    x = np.zeros((8, k), np.float32)
+    for b, c in enumerate(cols):
+        x[b, c] = 1.0
+    got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+    for b, c in enumerate(cols):
+        assert np.array_equal(got[b], W[:, c]), (G.NAMES[t], b, c)
+
+
+@pytest.mark.parametrize("t", [G.Q4_K, G.Q6_K])
+def test_gemv_batch_dynamic_range(t):
+    """Activation rows of very different magnitudes, tiny elements next to
+    large ones in the same block, and an all-zero block: batch > 1 splits x
+    into two fp16 parts per 256-element block after a power-of-two scaling,
+    which must keep the 2e-5 bound over the whole fp32 range."""
+    n, k = 45, 6 * 256
+    w = G.gen_weights(t, n, k, seed=21)
+    x = G.gen_x(k, 7, seed=22).astype(np.float64)
+    mags = [1e-30, 1e-6, 1e-2, 1.0, 3e3, 1e20, 1e-38]
+    x *= np.array(mags)[:, None]
+    x[:, ::3] *= 1e-9          # tiny elements inside every block
+    x[2, 256:512] = 0.0        # one empty block
+    x[4, 1000] = 6e4 * 1e4     # one element far above the rest of its block
+    x = x.astype(np.float32)
+    ref, absum = oracle.gemv(t, w, n, k, x)
+    got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+    say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "dynamic range %s" % G.NAMES[t]))
+
+
+@pytest.mark.parametrize("t,n,k,batch", [(G.Q4_K, 33000, 4608, 5), (G.Q6_K, 40000, 1024, 8),
+                                         (G.Q6_K, 2100, 4864, 3)])
+def test_gemv_batch_many_tiles(t, n, k, batch):
+    """More 16-row tiles than 8 per compute unit (several reduction rounds
+    per workgroup), K runs longer than two blocks per wave, waves with no
+    block (k = 1024), and an odd super-block count per row (Q6_K rows then
+    alternate their 4-byte alignment)."""
+    say("gemv many tiles", G.NAMES[t], n, k, batch)
+    w = G.gen_weights(t, n, k, seed=31)
+    x = G.gen_x(k, batch, seed=32)
+    ref, absum = oracle.gemv(t, w, n, k, x)
+    got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+    say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "gemv %s %dx%d B%d" % (G.NAMES[t], n, k, batch)))
+
+
 def test_gemv_unaligned_rows():
     """Row sizes that are not a multiple of 16 bytes take the 2-byte staging
     path."""
