@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
@@ -457,6 +459,180 @@ gemvb_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
     }
 }
 
+// ----------------------------------------------------- single-run kernel --
+// K of at most 16 super-blocks (every wave owns at most two): the A fragments
+// are converted once per workgroup and the weight stream runs through a ring
+// of GB_D tiles per wave (GB_D - 1 tiles of bytes in flight while one is
+// decoded).  The activations reach LDS by direct global->LDS loads, issued
+// before the first weight loads: waiting for them (the memory counter
+// completes in order) leaves those weight loads in flight, and they take no
+// registers while the fragments are built.
+template <int T> struct RingDepth { static constexpr int D = 3; };
+template <> struct RingDepth<T_Q4_K> { static constexpr int D = 4; };
+
+constexpr int XROW = 256 + 4;    // floats per staged activation row (16-byte pad: fewer bank conflicts)
+
+// Loads per WRawB<T> (each counts once in the vector memory counter).
+template <int T> struct RawLoads { static constexpr int N = 3; };
+template <> struct RawLoads<T_Q6_K> { static constexpr int N = 9; };
+
+// s_waitcnt with only the vector memory counter limited to n (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+#define QMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+// LDS operations of this wave complete (vmcnt and expcnt untouched).
+#define QMM_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xc07f)
+
+template <int T, bool TWO, int D>
+__device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n, int k, int64_t rb,
+                                           const float *__restrict__ x, int batch, float *__restrict__ y,
+                                           int t_begin, int t_count, int sa, float (*xs)[8][XROW],
+                                           fl2 (*red)[GB_W][64])
+{
+    using F = Fmt<T>;
+    constexpr int NC = TWO ? 2 : 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, g = lane >> 4;
+    // this wave's activations, 1 KB per (row, super-block), 16 bytes per lane;
+    // rows past the batch repeat the last one (never stored)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(x + (int64_t)min(b, batch - 1) * k + 256 * (sa + c) + 4 * lane),
+                (__attribute__((address_space(3))) void *)&xs[c][b][0], 16, 0, 0);
+
+    struct Slot {
+        WRawB<T> r[NC];
+    };
+    Slot ring[D];
+    auto load_tile = [&](Slot &sl, int t) {
+        t = min(t, t_count - 1);
+        const int row = min((t_begin + t) * 16 + nl, n - 1);
+        const int64_t base = (int64_t)row * rb + (int64_t)sa * F::BB;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            load_b<T>(w, base + c * F::BB, g, sl.r[c]);
+    };
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        load_tile(ring[d], d);
+    __builtin_amdgcn_sched_barrier(0);
+    // the activation loads were issued before the ring: wait for them only
+    QMM_WAIT_VMCNT((D - 1) * NC * RawLoads<T>::N);
+    __builtin_amdgcn_sched_barrier(0);
+    XFrag xf[NC];
+    {
+        const int r = lane & 15, b = min(r >> 1, batch - 1);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            fl4 v[16];
+            load_x<T>(xs[c][b], g, v);   // b: this lane's row (min(r/2, batch - 1))
+            convert_x<T>(v, xf[c]);
+        }
+    }
+    for (int t = 0; t < t_count; t += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            load_tile(ring[(j + D - 1) % D], t + j + D - 1);   // past the end: a harmless re-read
+            if (t + j < t_count) {
+                float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    sb_dot<T>(ring[j].r[c], xf[c], g, a0, a1);
+                red[j][wave][lane] = (fl2){a0, a1};
+            }
+        }
+        // cross-wave sum of these D tiles (raw barriers: no wait for the
+        // weight loads in flight)
+        QMM_WAIT_LGKM0();
+        __builtin_amdgcn_s_barrier();
+        const int nt = min(D, t_count - t);
+        if ((int)threadIdx.x < nt * 64) {
+            const int j = threadIdx.x >> 6, ln = threadIdx.x & 63;
+            fl2 s = red[j][0][ln];
+#pragma unroll
+            for (int ww = 1; ww < GB_W; ++ww)
+                s += red[j][ww][ln];
+            const int row = (t_begin + t + j) * 16 + (ln & 15), b0 = 2 * (ln >> 4);
+            if (row < n) {
+                if (b0 < batch)
+                    y[(int64_t)b0 * n + row] = s[0];
+                if (b0 + 1 < batch)
+                    y[(int64_t)(b0 + 1) * n + row] = s[1];
+            }
+        }
+        QMM_WAIT_LGKM0();
+        __builtin_amdgcn_s_barrier();
+    }
+}
+
+template <int T>
+__global__ void __launch_bounds__(64 * GB_W)
+gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x, int batch,
+              float *__restrict__ y)
+{
+    constexpr int DM = RingDepth<T>::D;
+    __shared__ __attribute__((aligned(16))) float xs[GB_W][2][8][XROW];
+    __shared__ __attribute__((aligned(16))) fl2 red[DM][GB_W][64];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int S = k / 256;
+    const int sa = wave * S / GB_W, ns = (wave + 1) * S / GB_W - sa;   // 0, 1 or 2 super-blocks
+    const int ntiles = (n + 15) >> 4;
+    const int per = ntiles / (int)gridDim.x, rem = ntiles - per * (int)gridDim.x;
+    const int t_begin = (int)blockIdx.x * per + min((int)blockIdx.x, rem);
+    const int t_count = per + ((int)blockIdx.x < rem ? 1 : 0);
+
+    // ring depth: one tile per lane group of loads in flight per tile the
+    // workgroup still has (no prefetch of tiles that do not exist)
+    auto run = [&](auto two_c, auto d_c) {
+        single_run<T, decltype(two_c)::value, decltype(d_c)::value>(w, n, k, rb, x, batch, y, t_begin, t_count, sa,
+                                                                      xs[wave], red);
+    };
+    using std_true = std::integral_constant<bool, true>;
+    using std_false = std::integral_constant<bool, false>;
+    if (ns > 0) {
+        const int dsel = min(t_count, DM);
+        if (ns == 2) {
+            if (dsel >= DM) run(std_true{}, std::integral_constant<int, DM>{});
+            else if (dsel == 3) run(std_true{}, std::integral_constant<int, 3>{});
+            else if (dsel == 2) run(std_true{}, std::integral_constant<int, 2>{});
+            else run(std_true{}, std::integral_constant<int, 1>{});
+        } else {
+            if (dsel >= DM) run(std_false{}, std::integral_constant<int, DM>{});
+            else if (dsel == 3) run(std_false{}, std::integral_constant<int, 3>{});
+            else if (dsel == 2) run(std_false{}, std::integral_constant<int, 2>{});
+            else run(std_false{}, std::integral_constant<int, 1>{});
+        }
+    }
+    else {
+        // no super-block: zero partials, same barriers as the others
+        const int D = min(t_count, DM);
+        for (int t = 0; t < t_count; t += D) {
+            for (int j = 0; j < D; ++j)
+                red[j][wave][lane] = (fl2){0.f, 0.f};
+            QMM_WAIT_LGKM0();
+            __builtin_amdgcn_s_barrier();
+            const int nt = min(D, t_count - t);
+            if ((int)threadIdx.x < nt * 64) {
+                const int j = threadIdx.x >> 6, ln = threadIdx.x & 63;
+                fl2 s = red[j][0][ln];
+                for (int ww = 1; ww < GB_W; ++ww)
+                    s += red[j][ww][ln];
+                const int row = (t_begin + t + j) * 16 + (ln & 15), b0 = 2 * (ln >> 4);
+                if (row < n) {
+                    if (b0 < batch)
+                        y[(int64_t)b0 * n + row] = s[0];
+                    if (b0 + 1 < batch)
+                        y[(int64_t)(b0 + 1) * n + row] = s[1];
+                }
+            }
+            QMM_WAIT_LGKM0();
+            __builtin_amdgcn_s_barrier();
+        }
+    }
+}
+
 int cu_count_cached()
 {
     static int cus = 0;
@@ -477,6 +653,11 @@ hipError_t launch_b(const uint8_t *w, int64_t n, int64_t k, size_t rb, const flo
 {
     const int64_t ntiles = (n + 15) / 16;
     const int grid = (int)(ntiles < cu_count_cached() ? ntiles : cu_count_cached());
+    if (k <= 256 * 2 * GB_W) {
+        hipLaunchKernelGGL(gemvb1_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, w, (int)n, (int)k, (int64_t)rb, x,
+                           batch, y);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(gemvb_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, w, (int)n, (int)k, (int64_t)rb, x,
                        batch, y);
     return hipGetLastError();
