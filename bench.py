@@ -186,14 +186,16 @@ def time_eager(torch, q, probs, steps, warmup):
 
 def cpu_baseline(cfg_probs_host, target_s):
     """The oracle (plain C, fp64, OpenMP over rows) on a bounded sample of the
-    same workload: whole layers of the decode stream, as many as fit in
-    about target_s seconds."""
+    same workload: whole layers of the decode stream, taken in order (and
+    again from the first layer once all are done) until about target_s
+    seconds of CPU time are spent."""
     import oracle
     nthreads = oracle.max_threads()
     done_bytes, t_used, layers = 0, 0.0, 0
     per_layer = 7
-    i = 0
-    while i < len(cfg_probs_host) and (t_used < target_s or layers == 0):
+    nl = len(cfg_probs_host) // per_layer
+    while t_used < target_s or layers == 0:
+        i = (layers % nl) * per_layer
         chunk = cfg_probs_host[i:i + per_layer]
         t0 = time.perf_counter()
         for (t, n, k, w, x) in chunk:
@@ -201,10 +203,9 @@ def cpu_baseline(cfg_probs_host, target_s):
         t_used += time.perf_counter() - t0
         done_bytes += sum(n * G.row_bytes(t, k) + 4 * k + 4 * n for (t, n, k, w, x) in chunk)
         layers += 1
-        i += per_layer
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-            "sample": "%d of 22 layers (%d GEMVs, %.1f MB of weights) of the same Q4_0 stream, %.1f s"
-                      % (layers, layers * per_layer, done_bytes / 1e6, t_used)}
+            "sample": "%d layers (%d GEMVs, %.1f MB of weights; the 22-layer Q4_0 stream repeated %.1f times), %.1f s"
+                      % (layers, layers * per_layer, done_bytes / 1e6, layers / nl, t_used)}
 
 
 # ------------------------------------------------------------- secondaries --

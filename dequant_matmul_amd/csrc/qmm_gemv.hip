@@ -33,10 +33,15 @@
 //                 registers, waves are independent and persistent, and the
 //                 weight bytes of the next row group are in flight while the
 //                 current one is decoded.
+//   gemv3_kernel  batch 1, Q4_K with n >= 2048: x in LDS (padded against
+//                 bank conflicts), 8 waves per compute unit, one row per item.
+//   gemv2m_kernel gemv2 over a table of up to 8 problems sharing k (the
+//                 grouped entry point): one launch instead of one per matrix.
 //   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
 //                 once per workgroup; otherwise as gemv2.
-//   gemv_kernel   batch 2..8 (and unaligned rows): x segment and weight
-//                 segments staged in LDS per workgroup.
+//   gemv_kernel   batch 2..8 of Q8_0 / Q4_0 (and unaligned batch-1 rows): x
+//                 segment and weight segments staged in LDS per workgroup.
+//   Batch 2..8 of Q4_K / Q6_K runs on the matrix cores (qmm_gemv_mfma.hip).
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
