@@ -14,7 +14,9 @@
 //   VALU work co-issues with MFMA only up to ~3-4 wave instructions per MFMA
 //   before it becomes the limit, and LDS delivers ~128 B/clk per CU.  So:
 //   - Workgroup tile BM (m) x BN (n) = 256 x 128 with 8 wavefronts stacked
-//     along m, each owning 32 x 128 = 2 x 8 MFMA blocks.  Every wave loads
+//     along m, each owning 32 x 128 = 2 x 8 MFMA blocks (128 x 64 with 4
+//     waves of 32 x 64 when 256 x 128 tiles would leave half the CUs idle,
+//     128 x 128 for m <= 128).  Every wave loads
 //     only its own X rows (two waves loading the same X lines doubled the L2
 //     traffic and was 2.5x slower); all share the weight tile.  The decode of
 //     a weight element is shared by BM rows of X.
@@ -525,6 +527,12 @@ static int cu_count()
 
 hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s);
 
+template <int BM, int BN>
+static int64_t tile_count(int64_t m, int64_t n)
+{
+    return ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+}
+
 template <int T, int FM, int FN, int WM, int WN, int XD>
 hipError_t launch_cfg(const uint8_t *w, int64_t n, int64_t k, size_t rb, const uint16_t *x, int64_t m, float *y,
                       hipStream_t s)
@@ -554,11 +562,17 @@ template <int T>
 hipError_t launch_gemm_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, const uint16_t *x, int64_t m,
                          float *y, hipStream_t s)
 {
-    // 8 wavefronts stacked along m, each 16 FM x 128: every wave reads its own
-    // X rows (no wave loads X another wave loads), all share the weight tile
+    // Wavefronts stacked along m, each 16 FM x 16 FN: every wave reads its own
+    // X rows (no wave loads X another wave loads), all share the weight tile.
+    // 256 x 128 tiles (8 waves) when they fill at least half the CUs; else
+    // 128 x 64 tiles (4 waves) before splitting K: on 512 x 4096 these give
+    // 256 tiles and ran 25% faster than 64 tiles split 4 ways, whose fp32
+    // atomics and zero fill cost more than the smaller tiles' extra decode.
     if (m <= 128)
         return launch_cfg<T, 1, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);   // 128 x 128
-    return launch_cfg<T, 2, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);       // 256 x 128
+    if (2 * tile_count<256, 128>(m, n) > cu_count())
+        return launch_cfg<T, 2, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);   // 256 x 128
+    return launch_cfg<T, 2, 4, 4, 1, 4>(w, n, k, rb, x, m, y, s);       // 128 x 64
 }
 
 hipError_t launch_gemm(int type, const void *w, int64_t n, int64_t k, size_t rb, const uint16_t *x, int64_t m,

@@ -139,12 +139,14 @@ QMM_API int qmm_gemv_multi(int type, int nprob, const void *const *w, const int6
  * fused quantized GEMM replacing dequant-to-scratch + FP16 GEMM for
  * prefill; shimmy "Airframe GPU pipeline": prompts are prefilled in
  * 512-token chunks.)
- * When m and n give too few output tiles to fill the GPU (e.g. m = 512,
- * n = 4096), K is split into up to 4 chunks whose partial sums are added
- * into y with fp32 atomics after y is zeroed on the same stream (two
- * launches); the order of those additions varies, so such results may
- * differ between calls in the last bits (always within the fp32 rounding
- * of the sum).
+ * When m and n give too few output tiles to fill the GPU even with the
+ * smaller tiles (e.g. m <= 128 with n = 4096, or m = 512 with n <= 2048 on
+ * 256 compute units), K is split into up to 4
+ * chunks whose partial sums are added into y with fp32 atomics after y is
+ * zeroed on the same stream (two launches); the order of those additions
+ * varies, so such results may differ between calls in the last bits
+ * (always within the fp32 rounding of the sum).  512-token chunks with
+ * n >= 4096 are not split and are deterministic.
  */
 QMM_API int qmm_gemm_prefill(int type, const void *w, int64_t n, int64_t k,
                      const uint16_t *x, int64_t m, float *y, void *stream);
