@@ -22,8 +22,8 @@ _LIB = os.path.join(_HERE, "libqmm_oracle.so")
 
 # Type ids (same numeric values as the public C-ABI; defined here on purpose,
 # not imported, so the oracle stays independent of the product package).
-Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
-TYPES = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K}
+Q4_0, Q8_0, Q4_K, Q6_K, Q5_0, Q5_K = 0, 1, 2, 3, 4, 5
+TYPES = {"Q4_0": Q4_0, "Q8_0": Q8_0, "Q4_K": Q4_K, "Q6_K": Q6_K, "Q5_0": Q5_0, "Q5_K": Q5_K}
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
              "-Wall", "-Wextra", "-shared", "-fPIC"]

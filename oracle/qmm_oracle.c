@@ -35,6 +35,12 @@
  *     the Q6_K ql/qh bit planes) this follows the public GGUF convention; that
  *     mapping is "parity unpinned" against real files (none are available) and
  *     is pinned only by encoder/decoder self-consistency tests.
+ *   - Q5_0 and Q5_K: shimmy "Architecture", Quantization table names a
+ *     5-bit super-block with a high-bit plane, and dotLLM "GPU Inference",
+ *     Quantization on GPU table lists Q5_0 and Q5_K (dequant-only there);
+ *     neither prints a layout.  Theirs here (GGUF convention, parity
+ *     unpinned) is the 4-bit layout of Q4_0 / Q4_K plus one high bit per
+ *     element in a separate bit plane.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -fopenmp -shared -fPIC.
  * Parallelism is an OpenMP loop over independent output rows only; it does not
@@ -50,7 +56,7 @@
 #endif
 
 /* Type ids, mirrored by value (not by header) from the public ABI. */
-enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3 };
+enum { OR_Q4_0 = 0, OR_Q8_0 = 1, OR_Q4_K = 2, OR_Q6_K = 3, OR_Q5_0 = 4, OR_Q5_K = 5 };
 
 /* Return codes: 0 = ok, -1 = bad type, -2 = bad shape, -3 = out of memory. */
 
@@ -61,6 +67,8 @@ int oracle_block_elems(int t)
     case OR_Q8_0: return 32;
     case OR_Q4_K: return 256;
     case OR_Q6_K: return 256;
+    case OR_Q5_0: return 32;
+    case OR_Q5_K: return 256;
     default: return 0;
     }
 }
@@ -72,6 +80,8 @@ int oracle_block_bytes(int t)
     case OR_Q8_0: return 2 + 32;            /* d, 32 int8 codes              */
     case OR_Q4_K: return 2 + 2 + 12 + 128;  /* d, dmin, scales, nibbles      */
     case OR_Q6_K: return 128 + 64 + 16 + 2; /* ql, qh, int8 scales, d        */
+    case OR_Q5_0: return 2 + 4 + 16;        /* d, 32 high bits, nibbles      */
+    case OR_Q5_K: return 2 + 2 + 12 + 32 + 128; /* d, dmin, scales, qh, nibbles */
     default: return 0;
     }
 }
@@ -186,6 +196,37 @@ static double elem_value(int t, const uint8_t *blk, int e)
         int hi = (qh[32 * h + l] >> (2 * g)) & 3;
         int q = lo | (hi << 4);
         return d * (double)sc[e / 16] * (double)(q - 32);
+    }
+    case OR_Q5_0: {
+        /* 5-bit codes: the low 4 bits as in Q4_0 (16 bytes of nibbles at
+         * byte 6, low nibbles elements 0-15, high nibbles 16-31), bit 4 of
+         * element e is bit e of the little-endian 32-bit word at byte 2;
+         * w = d * (q - 16).  (Layout: GGUF convention, parity unpinned.) */
+        double d = oracle_half_to_double(rd16(blk));
+        uint32_t qh = (uint32_t)blk[2] | ((uint32_t)blk[3] << 8) | ((uint32_t)blk[4] << 16) |
+                      ((uint32_t)blk[5] << 24);
+        const uint8_t *qs = blk + 6;
+        int lo = (e < 16) ? (qs[e] & 15) : (qs[e - 16] >> 4);
+        int q = lo | (int)(((qh >> e) & 1u) << 4);
+        return d * (double)(q - 16);
+    }
+    case OR_Q5_K: {
+        /* w = d * sc_j * q - dmin * m_j as Q4_K (same scale/min packing),
+         * q a 5-bit code: the low 4 bits placed as in Q4_K (code bytes at
+         * byte 48), bit 4 is bit j of qh[l], the 32 bytes at byte 16, for
+         * element l of sub-block j.  (Layout: GGUF convention, parity
+         * unpinned.) */
+        double d = oracle_half_to_double(rd16(blk));
+        double dmin = oracle_half_to_double(rd16(blk + 2));
+        const uint8_t *s = blk + 4;
+        const uint8_t *qh = blk + 16;
+        const uint8_t *qs = blk + 48;
+        int j = e / 32, l = e % 32, sc, m;
+        oracle_q4k_scale_min(s, j, &sc, &m);
+        uint8_t byte = qs[32 * (j / 2) + l];
+        int lo = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
+        int q = lo | (((qh[l] >> j) & 1) << 4);
+        return d * (double)sc * (double)q - dmin * (double)m;
     }
     default:
         return NAN;

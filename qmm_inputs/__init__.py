@@ -13,6 +13,9 @@ Block layouts written here (byte offsets inside one block, little-endian fp16):
                                6-bit scale/min fields, [16:144] 4-bit codes
   Q6_K  (256 elements, 210 B): [0:128] ql, [128:192] qh, [192:208] 16 x int8
                                scales, [208:210] d
+  Q5_0  (32 elements, 22 B):  [0:2] d, [2:6] 32 high bits, [6:22] 4-bit codes
+  Q5_K  (256 elements, 176 B): [0:2] d, [2:4] dmin, [4:16] scale/min bytes,
+                               [16:48] high bits, [48:176] 4-bit codes
 
 Distributions (the workload definitions that go with the pages):
   Q8_0: d ~ U[1e-3, 1e-2] rounded to fp16 (RNE), q ~ U{-127..127}
@@ -21,6 +24,8 @@ Distributions (the workload definitions that go with the pages):
         bijection between 96 bits and 16 six-bit fields, so every field is
         ~ U{0..63}); code bytes uniform
   Q6_K: ql, qh uniform (so q ~ U{0..63}); scales ~ U{-64..63}; d ~ U[1e-4,1e-3]
+  Q5_0 / Q5_K (no workload names them; the Q4_0 / Q4_K recipes): d (and
+        dmin) as for Q4_0 / Q4_K, every other byte uniform (q ~ U{0..31})
   activations: fp32 (decode) or fp16 (prefill) ~ N(0, 1)
 
 Seeds: matrix i of workload c uses seed 1000*c + i; its activation uses
@@ -33,12 +38,13 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
-NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
-BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210}
+Q4_0, Q8_0, Q4_K, Q6_K, Q5_0, Q5_K = 0, 1, 2, 3, 4, 5
+NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_0: "Q5_0", Q5_K: "Q5_K"}
+BLOCK_ELEMS = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256, Q5_0: 32, Q5_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210, Q5_0: 22, Q5_K: 176}
 
-DEFAULT_D_RANGE = {Q8_0: (1e-3, 1e-2), Q4_0: (1e-3, 1e-2), Q4_K: (1e-4, 1e-3), Q6_K: (1e-4, 1e-3)}
+DEFAULT_D_RANGE = {Q8_0: (1e-3, 1e-2), Q4_0: (1e-3, 1e-2), Q4_K: (1e-4, 1e-3), Q6_K: (1e-4, 1e-3),
+                   Q5_0: (1e-3, 1e-2), Q5_K: (1e-4, 1e-3)}
 
 
 def row_bytes(qtype: int, k: int) -> int:
@@ -96,6 +102,11 @@ def gen_weights(qtype: int, n: int, k: int, seed: int, d_range=None) -> np.ndarr
         blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
     elif qtype == Q4_K:
         # scale bytes and code bytes stay uniform
+        blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
+        blk[:, :, 2:4] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
+    elif qtype == Q5_0:
+        blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
+    elif qtype == Q5_K:
         blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
         blk[:, :, 2:4] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
     elif qtype == Q6_K:
@@ -159,6 +170,21 @@ def workload(cfg: int):
             mats += [("l%d.%s" % (layer, nm), t, n, k)
                      for nm, t, n, k in _llama_layer(4096, 14336, 1024, Q4_K, t_v=Q6_K, t_down=Q6_K)]
         mats.append(("lm_head", Q6_K, 128256, 4096))
+    elif cfg == 6:
+        # the 5-bit types (named by the pages, not by a workload): the
+        # Llama-3-8B shapes of workload 3 in Q5_K
+        for layer in range(32):
+            mats += [("l%d.%s" % (layer, nm), t, n, k)
+                     for nm, t, n, k in _llama_layer(4096, 14336, 1024, Q5_K)]
+    elif cfg == 7:
+        # the TinyLlama stream of workload 2 in Q5_0
+        for layer in range(22):
+            mats += [("l%d.%s" % (layer, nm), t, n, k)
+                     for nm, t, n, k in _llama_layer(2048, 5632, 256, Q5_0)]
+    elif cfg == 8:
+        # the prefill chunk GEMMs of workload 4 in Q5_0 and Q5_K
+        mats = [("gate_q5_0", Q5_0, 14336, 4096), ("q_q5_0", Q5_0, 4096, 4096),
+                ("gate_q5_k", Q5_K, 14336, 4096), ("q_q5_k", Q5_K, 4096, 4096)]
     else:
         raise ValueError("unknown workload %r" % (cfg,))
     return [(nm, t, n, k, 1000 * cfg + i) for i, (nm, t, n, k) in enumerate(mats)]

@@ -4,7 +4,7 @@ from __future__ import annotations
 import os
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-TYPE_IDS = {"Q4_0": 0, "Q8_0": 1, "Q4_K": 2, "Q6_K": 3}
+TYPE_IDS = {"Q4_0": 0, "Q8_0": 1, "Q4_K": 2, "Q6_K": 3, "Q5_0": 4, "Q5_K": 5}
 
 
 def load(fname: str) -> list[dict]:

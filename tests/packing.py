@@ -16,14 +16,19 @@ header for the page citations):
         element e: h = e // 128, r = e % 128, g = r // 32, l = r % 32;
         low 4 bits in ql[64 h + 32 (g % 2) + l] (low nibble if g < 2),
         high 2 bits at bit 2g of qh[32 h + l] (reading R8)
+  Q5_0: fp16 d | 4 B high bits | 16 B nibbles as Q4_0; bit 4 of element i is
+        bit i of the little-endian word              w = d (q - 16)
+  Q5_K: fp16 d | fp16 dmin | 12 B scales | 32 B qh | 128 B codes as Q4_K;
+        bit 4 of element (j, l) is bit j of qh[l]    w = d sc_j q - dmin m_j
+        (both 5-bit layouts: GGUF convention, a reading; parity unpinned)
 """
 from __future__ import annotations
 
 import numpy as np
 
-Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
-BE = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BB = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210}
+Q4_0, Q8_0, Q4_K, Q6_K, Q5_0, Q5_K = 0, 1, 2, 3, 4, 5
+BE = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q6_K: 256, Q5_0: 32, Q5_K: 256}
+BB = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q6_K: 210, Q5_0: 22, Q5_K: 176}
 
 
 def f16(v) -> np.uint16:
@@ -90,6 +95,28 @@ def pack_q6_k(d16: int, sc, q) -> bytes:
     return bytes(ql) + bytes(qh) + bytes(int(v) & 0xFF for v in sc) + _h(d16)
 
 
+def pack_q5_0(d16: int, q) -> bytes:
+    q = np.asarray(q, dtype=np.int64)
+    assert q.shape == (32,) and q.min() >= 0 and q.max() <= 31
+    hbits = sum((int(q[i]) >> 4) << i for i in range(32))
+    lo = [int(v) & 15 for v in q]
+    return _h(d16) + hbits.to_bytes(4, "little") + bytes(lo[i] | (lo[i + 16] << 4) for i in range(16))
+
+
+def pack_q5_k(d16: int, dmin16: int, sc, m, q) -> bytes:
+    q = np.asarray(q, dtype=np.int64)
+    assert q.shape == (256,) and q.min() >= 0 and q.max() <= 31
+    qh = bytearray(32)
+    qs = bytearray(128)
+    for j in range(8):
+        for l in range(32):
+            v = int(q[32 * j + l])
+            qh[l] |= (v >> 4) << j
+            byte = 32 * (j // 2) + l
+            qs[byte] |= (v & 15) if j % 2 == 0 else ((v & 15) << 4)
+    return _h(d16) + _h(dmin16) + pack_q4k_scales(sc, m) + bytes(qh) + bytes(qs)
+
+
 # ---------------------------------------------------------------- readers ---
 
 def read_fields(t: int, blk: bytes) -> dict:
@@ -127,6 +154,18 @@ def read_fields(t: int, blk: bytes) -> dict:
             lo = (lb & 15) if g < 2 else (lb >> 4)
             q[e] = lo | (((qh[32 * h + l] >> (2 * g)) & 3) << 4)
         return {"d": int(b[208]) | int(b[209]) << 8, "sc": b[192:208].view(np.int8).astype(np.int64), "q": q}
+    if t == Q5_0:
+        hb = int.from_bytes(bytes(b[2:6]), "little")
+        qs = b[6:22].astype(np.int64)
+        lo = np.concatenate([qs & 15, qs >> 4])
+        hi = np.array([(hb >> i) & 1 for i in range(32)], dtype=np.int64)
+        return {"d": int(b[0]) | int(b[1]) << 8, "q": lo | (hi << 4)}
+    if t == Q5_K:
+        f = read_fields(Q4_K, bytes(b[0:16]) + bytes(b[48:176]))
+        qh = b[16:48].astype(np.int64)
+        for j in range(8):
+            f["q"][32 * j: 32 * j + 32] |= ((qh >> j) & 1) << 4
+        return f
     raise ValueError(t)
 
 
@@ -198,4 +237,33 @@ def quant_q6_k(w) -> tuple[bytes, np.ndarray]:
     return pack_q6_k(d16, sc, q.reshape(-1)), step.reshape(-1)
 
 
-QUANT = {Q8_0: quant_q8_0, Q4_0: quant_q4_0, Q4_K: quant_q4_k, Q6_K: quant_q6_k}
+def quant_q5_0(w) -> tuple[bytes, np.ndarray]:
+    w = np.asarray(w, dtype=np.float64)
+    d16 = _f16_up(max(np.abs(w).max(), 1e-4) / 15.0)
+    d = _hval(d16)
+    q = np.clip(np.rint(w / d) + 16, 0, 31).astype(np.int64)
+    return pack_q5_0(d16, q), np.full(32, d)
+
+
+def quant_q5_k(w) -> tuple[bytes, np.ndarray]:
+    w = np.asarray(w, dtype=np.float64).reshape(8, 32)
+    mn = np.minimum(w.min(axis=1), 0.0)
+    mx = w.max(axis=1)
+    off = -mn
+    dmin16 = _f16_up(max(off.max(), 1e-4) / 63.0)
+    dmin = _hval(dmin16)
+    m = np.minimum(np.ceil(off / dmin), 63).astype(np.int64)
+    span = (mx - mn) + dmin
+    d16 = _f16_up(max(span.max(), 1e-4) / (31.0 * 63.0))
+    d = _hval(d16)
+    sc = np.clip(np.ceil(span / (31.0 * d)), 1, 63).astype(np.int64)
+    q = np.zeros((8, 32), dtype=np.int64)
+    step = np.zeros((8, 32))
+    for j in range(8):
+        q[j] = np.clip(np.rint((w[j] + dmin * m[j]) / (d * sc[j])), 0, 31)
+        step[j] = d * sc[j]
+    return pack_q5_k(d16, dmin16, sc, m, q.reshape(-1)), step.reshape(-1)
+
+
+QUANT = {Q8_0: quant_q8_0, Q4_0: quant_q4_0, Q4_K: quant_q4_k, Q6_K: quant_q6_k,
+         Q5_0: quant_q5_0, Q5_K: quant_q5_k}

@@ -28,7 +28,8 @@ def test_deterministic_and_seed_sensitive():
     assert a.shape == (8, 2 * 144)
 
 
-@pytest.mark.parametrize("t,lo,hi", [(G.Q8_0, 1e-3, 1e-2), (G.Q4_0, 1e-3, 1e-2), (G.Q4_K, 1e-4, 1e-3), (G.Q6_K, 1e-4, 1e-3)])
+@pytest.mark.parametrize("t,lo,hi", [(G.Q8_0, 1e-3, 1e-2), (G.Q4_0, 1e-3, 1e-2), (G.Q4_K, 1e-4, 1e-3), (G.Q6_K, 1e-4, 1e-3),
+                                     (G.Q5_0, 1e-3, 1e-2), (G.Q5_K, 1e-4, 1e-3)])
 def test_field_ranges(t, lo, hi):
     w = G.gen_weights(t, 64, 4 * G.BLOCK_ELEMS[t], seed=3)
     fs = _fields(t, w)
@@ -40,11 +41,13 @@ def test_field_ranges(t, lo, hi):
         assert q.min() >= -127 and q.max() <= 127 and q.min() < -100 and q.max() > 100
     elif t == G.Q4_0 or t == G.Q4_K:
         assert q.min() == 0 and q.max() == 15
+    elif t == G.Q5_0 or t == G.Q5_K:
+        assert q.min() == 0 and q.max() == 31
     else:
         assert q.min() == 0 and q.max() == 63
         sc = np.concatenate([f["sc"] for f in fs])
         assert sc.min() == -64 and sc.max() == 63
-    if t == G.Q4_K:
+    if t in (G.Q4_K, G.Q5_K):
         dmin = np.array([_h(f["dmin"]) for f in fs])
         assert dmin.min() >= np.float16(lo) * (1 - 2 ** -10) and dmin.max() <= np.float16(hi) * (1 + 2 ** -10)
         sc = np.concatenate([f["sc"] for f in fs])

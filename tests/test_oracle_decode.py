@@ -13,7 +13,7 @@ import oracle
 import packing as P
 from golden_io import load
 
-TYPES = [P.Q4_0, P.Q8_0, P.Q4_K, P.Q6_K]
+TYPES = [P.Q4_0, P.Q8_0, P.Q4_K, P.Q6_K, P.Q5_0, P.Q5_K]
 
 
 # --- fp16 unpack (shimmy "Architecture", Quantization table: fp16 unpack) ---
@@ -40,8 +40,9 @@ def test_fp16_special_values():
 # --- sizes (dotLLM "GPU Inference", Weight Strategy: Q4_K ~4.5 bits/param) ---
 
 def test_block_sizes_and_bits_per_weight():
-    assert [oracle.block_elems(t) for t in TYPES] == [32, 32, 256, 256]
-    assert [oracle.block_bytes(t) for t in TYPES] == [18, 34, 144, 210]
+    assert [oracle.block_elems(t) for t in TYPES] == [32, 32, 256, 256, 32, 256]
+    assert [oracle.block_bytes(t) for t in TYPES] == [18, 34, 144, 210, 22, 176]
+    assert oracle.block_bytes(P.Q5_K) * 8 / 256 == 5.5
     assert oracle.block_bytes(P.Q4_K) * 8 / 256 == 4.5
     assert oracle.row_bytes(P.Q4_K, 4096) == 2304
     assert oracle.row_bytes(P.Q6_K, 14336) == 11760
@@ -55,7 +56,7 @@ def _signed_zero_equal(a, b):
     return np.array_equal(np.asarray(a, np.float64), np.asarray(b, np.float64))
 
 
-@pytest.mark.parametrize("fname", ["q8_0.txt", "q4_0.txt"])
+@pytest.mark.parametrize("fname", ["q8_0.txt", "q4_0.txt", "q5_0.txt"])
 def test_golden_simple_blocks(fname):
     for blk in load(fname):
         t = blk["type"]
@@ -82,6 +83,24 @@ def test_golden_q4_k():
         q = np.where(j % 2 == 0, l % 16, 15 - l % 16)
         exp = np.array(blk["sc"])[j] * q - 0.5 * np.array(blk["m"])[j]
         assert np.array_equal(got, exp.astype(np.float32)), blk["name"]
+
+
+def test_golden_q5_k():
+    for blk in load("q5_k.txt"):
+        w = np.frombuffer(blk["bytes"], dtype=np.uint8)
+        got = oracle.dequant(P.Q5_K, w, 1, 256)[0]
+        for e, v in blk["spot"].items():
+            assert got[e] == v, (blk["name"], e)
+        for j in range(8):
+            assert oracle.q4k_scale_min(blk["bytes"][4:16], j) == (blk["sc"][j], blk["m"][j])
+    # block A element by element: q = l % 16 (even j), 31 - l % 16 (odd j)
+    blk = load("q5_k.txt")[0]
+    got = oracle.dequant(P.Q5_K, np.frombuffer(blk["bytes"], dtype=np.uint8), 1, 256)[0]
+    e = np.arange(256)
+    j, l = e // 32, e % 32
+    q = np.where(j % 2 == 0, l % 16, 31 - l % 16)
+    exp = np.array(blk["sc"])[j] * q - 0.5 * np.array(blk["m"])[j]
+    assert np.array_equal(got, exp.astype(np.float32))
 
 
 def test_golden_q6_k():
@@ -199,6 +218,38 @@ def test_q6_k_one_hot_codes():
         assert np.array_equal(w, 5.0 * (np.arange(256) // 16 == i))
 
 
+def test_q5_0_one_hot_codes_and_bits():
+    for e in range(32):
+        q = np.full(32, 16, np.int64)   # code 16 -> weight 0
+        q[e] = 16 + 11 if e % 2 else 16 - 13   # both sides of the offset, high bit set / clear
+        w = oracle.dequant(P.Q5_0, np.frombuffer(P.pack_q5_0(0x3C00, q), np.uint8), 1, 32)[0]
+        assert np.array_equal(w, (11.0 if e % 2 else -13.0) * (np.arange(32) == e)), e
+    # one-hot bits of the high-bit word move exactly one element by 16 d
+    for bit in range(32):
+        raw = bytearray(P.pack_q5_0(0x3C00, np.zeros(32, np.int64)))
+        raw[2 + bit // 8] |= 1 << (bit % 8)
+        w = oracle.dequant(P.Q5_0, np.frombuffer(bytes(raw), np.uint8), 1, 32)[0]
+        assert np.array_equal(w, -16.0 + 16.0 * (np.arange(32) == bit)), bit
+
+
+def test_q5_k_one_hot_codes_and_bits():
+    sc = [1] * 8
+    m = [0] * 8
+    for e in range(0, 256, 3):
+        q = np.zeros(256, np.int64)
+        q[e] = 19          # low nibble 3, high bit set
+        blk = P.pack_q5_k(0x3C00, 0x3C00, sc, m, q)
+        w = oracle.dequant(P.Q5_K, np.frombuffer(blk, np.uint8), 1, 256)[0]
+        assert np.array_equal(w, 19.0 * (np.arange(256) == e)), e
+    # one-hot bits of the 32 qh bytes land on exactly one element (j = bit, l = byte)
+    for byte in range(32):
+        for bit in range(8):
+            raw = bytearray(P.pack_q5_k(0x3C00, 0x3C00, sc, m, np.zeros(256, np.int64)))
+            raw[16 + byte] = 1 << bit
+            w = oracle.dequant(P.Q5_K, np.frombuffer(bytes(raw), np.uint8), 1, 256)[0]
+            assert np.flatnonzero(w).tolist() == [32 * bit + byte] and w.max() == 16.0
+
+
 # --- independent encoder vs decoder ----------------------------------------
 
 @pytest.mark.parametrize("t", TYPES)
@@ -220,10 +271,14 @@ def test_encode_with_own_scales_round_trip(t):
         elif t == P.Q4_0:
             again = P.pack_q4_0(f["d"], f["q"])
             imp = h(f["d"]) * (f["q"] - 8)
-        elif t == P.Q4_K:
-            again = P.pack_q4_k(f["d"], f["dmin"], f["sc"], f["m"], f["q"])
+        elif t in (P.Q4_K, P.Q5_K):
+            pack = P.pack_q4_k if t == P.Q4_K else P.pack_q5_k
+            again = pack(f["d"], f["dmin"], f["sc"], f["m"], f["q"])
             j = np.arange(256) // 32
             imp = h(f["d"]) * f["sc"][j] * f["q"] - h(f["dmin"]) * f["m"][j]
+        elif t == P.Q5_0:
+            again = P.pack_q5_0(f["d"], f["q"])
+            imp = h(f["d"]) * (f["q"] - 16)
         else:
             again = P.pack_q6_k(f["d"], f["sc"], f["q"])
             imp = h(f["d"]) * f["sc"][np.arange(256) // 16] * (f["q"] - 32)

@@ -18,7 +18,7 @@ import oracle
 import qmm_inputs
 import packing as P
 
-TYPES = [P.Q4_0, P.Q8_0, P.Q4_K, P.Q6_K]
+TYPES = [P.Q4_0, P.Q8_0, P.Q4_K, P.Q6_K, P.Q5_0, P.Q5_K]
 
 
 def _exact_dot(wrow, xrow):
@@ -31,7 +31,7 @@ def _exact_dot(wrow, xrow):
     return s, sa
 
 
-@pytest.mark.parametrize("t,n,k", [(P.Q8_0, 1, 32), (P.Q4_0, 1, 32)] + [(t, 4, 256) for t in TYPES])
+@pytest.mark.parametrize("t,n,k", [(P.Q8_0, 1, 32), (P.Q4_0, 1, 32), (P.Q5_0, 1, 32)] + [(t, 4, 256) for t in TYPES])
 def test_gemv_exact_rationals(t, n, k):
     w = qmm_inputs.gen_weights(t, n, k, seed=21 + t)
     x = qmm_inputs.gen_x(k, 2, seed=22 + t)

@@ -31,6 +31,11 @@ MUTANTS = {
                          "return d * (double)sc[e / 32] * (double)(q - 32);"),
     "q6_k d position": ("double d = oracle_half_to_double(rd16(blk + 208));",
                         "double d = oracle_half_to_double(rd16(blk + 192));"),
+    "q5_0 offset": ("return d * (double)(q - 16);", "return d * (double)(q - 15);"),
+    "q5_0 high bit of the wrong element": ("int q = lo | (int)(((qh >> e) & 1u) << 4);",
+                                           "int q = lo | (int)(((qh >> (e % 16)) & 1u) << 4);"),
+    "q5_k high-bit plane": ("int q = lo | (((qh[l] >> j) & 1) << 4);", "int q = lo | (((qh[l] >> (j / 2)) & 1) << 4);"),
+    "q5_k qh offset": ("const uint8_t *qh = blk + 16;", "const uint8_t *qh = blk + 17;"),
     "fp16 exponent bias": ("v = ldexp((double)(1024 + f), e - 25);", "v = ldexp((double)(1024 + f), e - 24);"),
     "gemv batch index": ("double p = (double)wrow[i] * (double)x[b * k + i];",
                          "double p = (double)wrow[i] * (double)x[i];"),
