@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized-weight matmul on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix|q5]
 
 A step is one decode pass over the TinyLlama-shaped Q4_0 weight stream:
 22 layers x (q, k, v, o, gate, up, down) = 154 GEMVs at batch 1 on one
@@ -15,7 +15,8 @@ of the 8 TB/s peak, the decode-equivalent tokens/s, the roofline of the
 dominant kernel (the Q4_0 GEMV) from per-launch HIP-event timings, the CPU
 oracle timed on a bounded sample of the same workload, and secondary figures
 for the other workloads (Q8_0 single matrix, Llama-3-8B Q4_K set, 512-token
-prefill GEMMs, Q4_K_M-style mix with a Q6_K LM head at batch 1/4/8).
+prefill GEMMs, Q4_K_M-style mix with a Q6_K LM head at batch 1/4/8, and the
+same shapes in the 5-bit types Q5_K / Q5_0).
 """
 from __future__ import annotations
 
@@ -52,7 +53,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix"], default="all",
+    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix", "q5"], default="all",
                    help="which secondary workloads to run after the primary line's (all by default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU oracle sample")
@@ -265,14 +266,14 @@ def sec_stream(torch, q, cfg, weights, batch, steps, warmup, dev, label, with_ge
     return out
 
 
-def sec_prefill(torch, q, steps, warmup, dev):
+def sec_prefill(torch, q, steps, warmup, dev, cfg=4):
     res = {}
     m = G.PREFILL_M
-    for name, t, n, k, seed in G.workload(4):
+    for name, t, n, k, seed in G.workload(cfg):
         w = torch.from_numpy(G.gen_weights(t, n, k, seed)).to(dev)
         probs = []
         for c in range(G.PREFILL_CHUNKS):
-            X = torch.from_numpy(G.gen_x_f16(m, k, G.x_seed(4, 10 * c + len(res)))).to(dev)
+            X = torch.from_numpy(G.gen_x_f16(m, k, G.x_seed(cfg, 10 * c + len(res)))).to(dev)
             Y = torch.empty((m, n), dtype=torch.float32, device=dev)
             probs.append(Problem(torch, "%s.c%d" % (name, c), t, n, k, w, X, Y, kind="gemm"))
         g = capture(torch, q, probs)
@@ -410,6 +411,19 @@ def main():
                     "Q4_K_M-style mix (v, down, LM head 128256x4096 in Q6_K), 225 GEMVs, batch %d" % b,
                     with_gemm=True)
             del wts
+        if want("q5"):
+            log("secondary: 5-bit types")
+            wts = build_weights(torch, 6, dev)
+            sec["llama3_8b_q5_k"] = sec_stream(torch, q, 6, wts, 1, args.steps, args.warmup, dev,
+                                               "Llama-3-8B-shaped Q5_K, 224 GEMVs, batch 1")
+            del wts
+            torch.cuda.empty_cache()
+            wts = build_weights(torch, 7, dev)
+            sec["tinyllama_q5_0"] = sec_stream(torch, q, 7, wts, 1, args.steps, args.warmup, dev,
+                                               "TinyLlama-shaped Q5_0 stream, 154 GEMVs, batch 1")
+            del wts
+            torch.cuda.empty_cache()
+            sec["prefill_512_q5"] = sec_prefill(torch, q, args.steps, args.warmup, dev, cfg=8)
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 

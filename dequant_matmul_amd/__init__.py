@@ -22,8 +22,8 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
-Q4_0, Q8_0, Q4_K, Q6_K = 0, 1, 2, 3
-TYPE_NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K"}
+Q4_0, Q8_0, Q4_K, Q6_K, Q5_0, Q5_K = 0, 1, 2, 3, 4, 5
+TYPE_NAMES = {Q4_0: "Q4_0", Q8_0: "Q8_0", Q4_K: "Q4_K", Q6_K: "Q6_K", Q5_0: "Q5_0", Q5_K: "Q5_K"}
 OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_ALIGN, ERR_HIP = range(6)
 
 # C-ABI entry points and their ctypes signatures (mirrors include/qmm.h).

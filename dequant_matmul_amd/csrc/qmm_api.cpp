@@ -11,8 +11,8 @@ namespace {
 int block_elems(int t)
 {
     switch (t) {
-    case QMM_Q4_0: case QMM_Q8_0: return 32;
-    case QMM_Q4_K: case QMM_Q6_K: return 256;
+    case QMM_Q4_0: case QMM_Q8_0: case QMM_Q5_0: return 32;
+    case QMM_Q4_K: case QMM_Q6_K: case QMM_Q5_K: return 256;
     default: return 0;
     }
 }
@@ -24,6 +24,8 @@ int block_bytes(int t)
     case QMM_Q8_0: return 34;
     case QMM_Q4_K: return 144;
     case QMM_Q6_K: return 210;
+    case QMM_Q5_0: return 22;
+    case QMM_Q5_K: return 176;
     default: return 0;
     }
 }

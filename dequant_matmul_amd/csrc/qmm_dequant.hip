@@ -8,12 +8,14 @@
 //   Q4_K  fma(q, d sc, -dmin m): d sc and dmin m are exact products, so the
 //         single rounding of the fma is the rounding of the exact weight
 //   Q6_K  (d sc) (q - 32)     (at most 23 significant bits, exact)
+//   Q5_0  d (q - 16)          (exact)
+//   Q5_K  fma(q, d sc, -dmin m) as Q4_K
 // No division, reciprocal or fp16 intermediate is involved.
 //
 // Work split: one thread per 8 consecutive outputs of a row, so a wavefront
 // stores 2 KB of contiguous fp32 (the kernel is bound by these writes: the
 // output is 3.8x-7.1x the input bytes).  Inputs are read with naturally
-// aligned 2- or 4-byte loads (blocks of 34, 18 and 210 bytes are only 2-byte
+// aligned 2- or 4-byte loads (blocks of 34, 18, 22 and 210 bytes are only 2-byte
 // aligned); the reads hit in cache because neighbouring threads share blocks.
 #include "qmm_device.h"
 #include "qmm_launch.h"
@@ -90,6 +92,45 @@ dequant_kernel(const uint8_t *__restrict__ w, int64_t n, int64_t k, int64_t rb, 
         v[2] = __builtin_fmaf(ub2(c0), dsc, -dm); v[3] = __builtin_fmaf(ub3(c0), dsc, -dm);
         v[4] = __builtin_fmaf(ub0(c1), dsc, -dm); v[5] = __builtin_fmaf(ub1(c1), dsc, -dm);
         v[6] = __builtin_fmaf(ub2(c1), dsc, -dm); v[7] = __builtin_fmaf(ub3(c1), dsc, -dm);
+    } else if constexpr (T == T_Q5_0) {
+        // 22-byte blocks: 2-byte aligned loads only
+        const float d = h2f(ld16(blk));
+        const uint32_t hbits = ld16(blk + 2) | (ld16(blk + 4) << 16);
+        uint32_t c0, c1;
+        ld8_u16(blk + 6 + (eb & 15), c0, c1);
+        if (eb >= 16) {
+            c0 >>= 4;
+            c1 >>= 4;
+        }
+        const uint32_t hb = hbits >> eb;   // bits of elements eb .. eb+7
+        c0 = (c0 & 0x0f0f0f0fu) | bits_to_byte_bit4(hb);
+        c1 = (c1 & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> 4);
+        v[0] = d * (ub0(c0) - 16.f); v[1] = d * (ub1(c0) - 16.f);
+        v[2] = d * (ub2(c0) - 16.f); v[3] = d * (ub3(c0) - 16.f);
+        v[4] = d * (ub0(c1) - 16.f); v[5] = d * (ub1(c1) - 16.f);
+        v[6] = d * (ub2(c1) - 16.f); v[7] = d * (ub3(c1) - 16.f);
+    } else if constexpr (T == T_Q5_K) {
+        // 176-byte blocks keep 16-byte alignment
+        const uint32_t *hd = (const uint32_t *)blk;
+        const uint32_t dd = hd[0], s0 = hd[1], s1 = hd[2], s2 = hd[3];
+        const int j = eb >> 5, l0 = eb & 31;
+        uint32_t sc, m;
+        q4k_scale_min(s0, s1, s2, j, sc, m);
+        const float dsc = h2f(dd & 0xffffu) * (float)sc;
+        const float dm = h2f(dd >> 16) * (float)m;
+        const uint32_t *qh = (const uint32_t *)(blk + 16 + l0);
+        const uint32_t *cs = (const uint32_t *)(blk + 48 + 32 * (j >> 1) + l0);
+        uint32_t c0 = cs[0], c1 = cs[1];
+        if (j & 1) {
+            c0 >>= 4;
+            c1 >>= 4;
+        }
+        c0 = (c0 & 0x0f0f0f0fu) | (((qh[0] >> j) & 0x01010101u) << 4);
+        c1 = (c1 & 0x0f0f0f0fu) | (((qh[1] >> j) & 0x01010101u) << 4);
+        v[0] = __builtin_fmaf(ub0(c0), dsc, -dm); v[1] = __builtin_fmaf(ub1(c0), dsc, -dm);
+        v[2] = __builtin_fmaf(ub2(c0), dsc, -dm); v[3] = __builtin_fmaf(ub3(c0), dsc, -dm);
+        v[4] = __builtin_fmaf(ub0(c1), dsc, -dm); v[5] = __builtin_fmaf(ub1(c1), dsc, -dm);
+        v[6] = __builtin_fmaf(ub2(c1), dsc, -dm); v[7] = __builtin_fmaf(ub3(c1), dsc, -dm);
     } else {  // Q6_K
         const int h = eb >> 7, r = eb & 127, gq = r >> 5, l0 = r & 31;
         uint32_t l_lo, l_hi, h_lo, h_hi;
@@ -127,6 +168,8 @@ hipError_t launch_dequant(int type, const void *w, int64_t n, int64_t k, size_t 
     case T_Q8_0: hipLaunchKernelGGL(dequant_kernel<T_Q8_0>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
     case T_Q4_K: hipLaunchKernelGGL(dequant_kernel<T_Q4_K>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
     case T_Q6_K: hipLaunchKernelGGL(dequant_kernel<T_Q6_K>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
+    case T_Q5_0: hipLaunchKernelGGL(dequant_kernel<T_Q5_0>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
+    case T_Q5_K: hipLaunchKernelGGL(dequant_kernel<T_Q5_K>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -9,6 +9,10 @@
 //                        128 B codes; w = d sc_j q - dmin m_j, j = e / 32
 //   Q6_K 256 el / 210 B: 128 B ql | 64 B qh | 16 int8 scales | fp16 d;
 //                        w = d scale[e/16] (q - 32)
+//   Q5_0  32 el / 22 B : fp16 d | 32 high bits | 16 B codes as Q4_0;
+//                        w = d (q - 16)
+//   Q5_K 256 el / 176 B: as Q4_K with 32 B qh between the scales and the
+//                        codes (bit j of qh[l]: bit 4 of element (j, l))
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -16,7 +20,7 @@
 
 namespace qmm {
 
-enum : int { T_Q4_0 = 0, T_Q8_0 = 1, T_Q4_K = 2, T_Q6_K = 3 };
+enum : int { T_Q4_0 = 0, T_Q8_0 = 1, T_Q4_K = 2, T_Q6_K = 3, T_Q5_0 = 4, T_Q5_K = 5 };
 
 // Native 128-bit vectors.  (HIP's uint4 / float4 are structs whose copies
 // lower to memcpy, which can keep arrays of them in scratch memory.)
@@ -28,6 +32,8 @@ template <> struct Fmt<T_Q4_0> { static constexpr int BE = 32, BB = 18; };
 template <> struct Fmt<T_Q8_0> { static constexpr int BE = 32, BB = 34; };
 template <> struct Fmt<T_Q4_K> { static constexpr int BE = 256, BB = 144; };
 template <> struct Fmt<T_Q6_K> { static constexpr int BE = 256, BB = 210; };
+template <> struct Fmt<T_Q5_0> { static constexpr int BE = 32, BB = 22; };
+template <> struct Fmt<T_Q5_K> { static constexpr int BE = 256, BB = 176; };
 
 // IEEE binary16 bits -> fp32 (exact; v_cvt_f32_f16).
 __device__ __forceinline__ float h2f(uint32_t bits16)
@@ -58,6 +64,14 @@ __device__ __forceinline__ float sb0(uint32_t v) { return (float)(int8_t)(v); }
 __device__ __forceinline__ float sb1(uint32_t v) { return (float)(int8_t)(v >> 8); }
 __device__ __forceinline__ float sb2(uint32_t v) { return (float)(int8_t)(v >> 16); }
 __device__ __forceinline__ float sb3(uint32_t v) { return (float)(int8_t)(v >> 24); }
+
+// Bits 0..3 of h moved to bit 4 of bytes 0..3 (the four partial products of
+// the multiply land on disjoint bit ranges, so nothing carries): the high
+// code bit of four consecutive Q5_0 elements.
+__device__ __forceinline__ uint32_t bits_to_byte_bit4(uint32_t h)
+{
+    return ((h & 15u) * 0x02040810u) & 0x10101010u;
+}
 
 // Make this wave's LDS writes visible to the other lanes of the same wave.
 __device__ __forceinline__ void wave_lds_sync()

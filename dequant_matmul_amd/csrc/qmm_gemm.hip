@@ -29,16 +29,16 @@
 //     a rolling window.  The raw weight bytes of tile t+2 are requested at the
 //     start of tile t, right after the first X load of the next tile, so the
 //     in-order vmcnt waits for X cover them only a tile later.
-//   - Weight decode to fp16: Q8_0 / Q4_0 codes become exact fp16 integers
+//   - Weight decode to fp16: Q8_0 / Q4_0 / Q5_0 codes become exact fp16 integers
 //     (byte permute into 0x64xx = 1024 + byte, then subtract the bias) and one
 //     v_pk_mul_f16 by d rounds d*q exactly once: d*q is exact in fp32, so this
-//     equals fp16_RNE(fp32 w).  Q4_K / Q6_K values are formed in fp32 with one
+//     equals fp16_RNE(fp32 w).  Q4_K / Q5_K / Q6_K values are formed in fp32 with one
 //     fma (the exact dequantized fp32 value) and packed with v_cvt_pk_f16_f32.
 //   - Workgroups are remapped so that each XCD (dispatched round-robin) owns a
 //     contiguous run of tiles along n with one X slice, which stays in its L2.
 //   - Ragged m / n: loads clamp to the last valid row, stores are masked (row
 //     r of Y depends only on row r of X and column j only on row j of W).
-//     Ragged K (Q8_0 / Q4_0, K a multiple of 32): 32-wide K sub-steps past K
+//     Ragged K (32-element blocks, K a multiple of 32): 32-wide K sub-steps past K
 //     are skipped.
 #include "qmm_device.h"
 #include "qmm_launch.h"
@@ -96,10 +96,12 @@ __device__ __forceinline__ void realign(const URun<NDW> &r, uint32_t sh, uint32_
 
 // ------------------------------------------------------- decode units --
 // A unit is 32 weights of one row inside K step t, quarter q (0..3):
-//   Q8_0 / Q4_0  block 4 t + q of the row (one run of 32 elements at 32 q);
+//   Q8_0 / Q4_0 / Q5_0  block 4 t + q of the row (one run of 32 elements at
+//                32 q; Q5_0 reads its high-bit word with the codes);
 //   Q4_K         16 code bytes of super-block t / 2: low nibbles are 16
 //                elements of sub-block 2p, high nibbles the same 16 of
 //                sub-block 2p + 1 (p = 2 (t % 2) + q / 2);
+//   Q5_K         as Q4_K, plus the 16 qh bytes of the same elements l;
 //   Q6_K         16 ql bytes and 16 qh bytes of super-block t / 2, half
 //                h = t % 2: 16 elements (l = 16 (q % 2) + i) of each of the
 //                groups g = q / 2 (low nibble) and g + 2 (high nibble).
@@ -108,6 +110,8 @@ template <> struct WRaw<T_Q8_0> { uint32_t d; URun<8> c; uint32_t sh; };
 template <> struct WRaw<T_Q4_0> { uint32_t d; URun<4> c; uint32_t sh; };
 template <> struct WRaw<T_Q4_K> { u32x4 hd; u32x4 c; };
 template <> struct WRaw<T_Q6_K> { URun<4> ql; URun<4> qh; uint32_t sc; uint32_t d; uint32_t sh; };
+template <> struct WRaw<T_Q5_0> { uint32_t d; URun<5> c; uint32_t sh; };   // c: high-bit word, 4 code dwords
+template <> struct WRaw<T_Q5_K> { u32x4 hd; u32x4 c; u32x4 h; };
 
 template <int T>
 __device__ __forceinline__ void load_unit(const uint8_t *row, int t, int q, WRaw<T> &r)
@@ -120,6 +124,15 @@ __device__ __forceinline__ void load_unit(const uint8_t *row, int t, int q, WRaw
         const uint8_t *blk = row + (int64_t)(4 * t + q) * 18;
         r.d = *(const uint16_t *)blk;
         r.sh = gload_run<4>(blk + 2, r.c);
+    } else if constexpr (T == T_Q5_0) {
+        const uint8_t *blk = row + (int64_t)(4 * t + q) * 22;
+        r.d = *(const uint16_t *)blk;
+        r.sh = gload_run<5>(blk + 2, r.c);
+    } else if constexpr (T == T_Q5_K) {
+        const uint8_t *blk = row + (int64_t)(t >> 1) * 176;    // 16-byte aligned
+        r.hd = *(const u32x4 *)blk;
+        r.h = *(const u32x4 *)(blk + 16 + 16 * (q & 1));      // qh of the unit's 16 elements l
+        r.c = *(const u32x4 *)(blk + 48 + 64 * (t & 1) + 16 * q);
     } else if constexpr (T == T_Q4_K) {
         const uint8_t *blk = row + (int64_t)(t >> 1) * 144;    // 16-byte aligned
         r.hd = *(const u32x4 *)blk;
@@ -251,6 +264,68 @@ template <> struct Dec<T_Q4_K> {
     {
         const uint32_t c = i == 0 ? r.c.x : i == 1 ? r.c.y : i == 2 ? r.c.z : r.c.w;
         const uint32_t lo = opaque(c & 0x0f0f0f0fu), hi = opaque(c & 0xf0f0f0f0u);
+        st64(ws + base + 4 * i,
+             pack_rne(__builtin_fmaf(ub0(lo), dsc0, -dm0), __builtin_fmaf(ub1(lo), dsc0, -dm0)),
+             pack_rne(__builtin_fmaf(ub2(lo), dsc0, -dm0), __builtin_fmaf(ub3(lo), dsc0, -dm0)));
+        st64(ws + base + 32 + 4 * i,
+             pack_rne(__builtin_fmaf(ub0(hi), dsc1, -dm1), __builtin_fmaf(ub1(hi), dsc1, -dm1)),
+             pack_rne(__builtin_fmaf(ub2(hi), dsc1, -dm1), __builtin_fmaf(ub3(hi), dsc1, -dm1)));
+    }
+};
+
+template <> struct Dec<T_Q5_0> {
+    half2v d2;
+    int off;
+    __device__ __forceinline__ void setup(const WRaw<T_Q5_0> &r, int, int q)
+    {
+        keep_raw(r);
+        d2 = bits_h2(r.d | (r.d << 16));
+        off = 32 * q;
+    }
+    __device__ __forceinline__ void part(const WRaw<T_Q5_0> &r, int i, _Float16 *ws) const
+    {
+        const half2v bias = {(_Float16)1040.f, (_Float16)1040.f};
+        const uint32_t hb = align_bytes(r.c.d[1], r.c.d[0], r.sh);
+        const uint32_t c = align_bytes(r.c.d[i + 2], r.c.d[i + 1], r.sh);
+        const uint32_t q5lo = (c & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (4 * i));
+        const uint32_t q5hi = ((c >> 4) & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (16 + 4 * i));
+        uint32_t lo[2], hi[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            // 1024 + q exactly, minus the bias 1040: q - 16, then one rounding of d (q - 16)
+            lo[j] = h2_bits((bits_h2(bytes_1024(q5lo, j)) - bias) * d2);
+            hi[j] = h2_bits((bits_h2(bytes_1024(q5hi, j)) - bias) * d2);
+        }
+        st64(ws + off + 4 * i, lo[0], lo[1]);          // elements 4i .. 4i+3
+        st64(ws + off + 16 + 4 * i, hi[0], hi[1]);     // elements 16+4i .. 16+4i+3
+    }
+};
+
+template <> struct Dec<T_Q5_K> {
+    float dsc0, dm0, dsc1, dm1;
+    uint32_t hs;
+    int base;
+    __device__ __forceinline__ void setup(const WRaw<T_Q5_K> &r, int t, int q)
+    {
+        keep_raw(r);
+        const int p = 2 * (t & 1) + (q >> 1);
+        uint32_t sc0, m0, sc1, m1;
+        q4k_scale_min(r.hd.y, r.hd.z, r.hd.w, 2 * p, sc0, m0);
+        q4k_scale_min(r.hd.y, r.hd.z, r.hd.w, 2 * p + 1, sc1, m1);
+        const float d = h2f(r.hd.x & 0xffffu), dmin = h2f(r.hd.x >> 16);
+        dsc0 = d * (float)sc0;
+        dm0 = dmin * (float)m0;
+        dsc1 = d * (float)sc1;
+        dm1 = dmin * (float)m1;
+        hs = 2u * (uint32_t)p;      // qh bit of sub-block 2p; 2p + 1 for the high nibbles
+        base = 64 * (q >> 1) + 16 * (q & 1);
+    }
+    __device__ __forceinline__ void part(const WRaw<T_Q5_K> &r, int i, _Float16 *ws) const
+    {
+        const uint32_t c = i == 0 ? r.c.x : i == 1 ? r.c.y : i == 2 ? r.c.z : r.c.w;
+        const uint32_t h = i == 0 ? r.h.x : i == 1 ? r.h.y : i == 2 ? r.h.z : r.h.w;
+        const uint32_t lo = opaque((c & 0x0f0f0f0fu) | (((h >> hs) & 0x01010101u) << 4));
+        const uint32_t hi = opaque(((c >> 4) & 0x0f0f0f0fu) | (((h >> (hs + 1u)) & 0x01010101u) << 4));
         st64(ws + base + 4 * i,
              pack_rne(__builtin_fmaf(ub0(lo), dsc0, -dm0), __builtin_fmaf(ub1(lo), dsc0, -dm0)),
              pack_rne(__builtin_fmaf(ub2(lo), dsc0, -dm0), __builtin_fmaf(ub3(lo), dsc0, -dm0)));
@@ -584,6 +659,8 @@ hipError_t launch_gemm(int type, const void *w, int64_t n, int64_t k, size_t rb,
     case T_Q8_0: return launch_gemm_t<T_Q8_0>(wb, n, k, rb, x, m, y, s);
     case T_Q4_K: return launch_gemm_t<T_Q4_K>(wb, n, k, rb, x, m, y, s);
     case T_Q6_K: return launch_gemm_t<T_Q6_K>(wb, n, k, rb, x, m, y, s);
+    case T_Q5_0: return launch_gemm_t<T_Q5_0>(wb, n, k, rb, x, m, y, s);
+    case T_Q5_K: return launch_gemm_t<T_Q5_K>(wb, n, k, rb, x, m, y, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -11,7 +11,8 @@
 //     consecutive units of a row, i.e. one unit per lane of a wavefront.
 //   - Weights are read with 16-byte loads.  Q4_K blocks (144 B) keep 16-byte
 //     alignment, so each lane loads its unit straight into registers.  Blocks
-//     of 34, 18 and 210 bytes are only 2-byte aligned: the wavefront copies the
+//     of 34, 18, 22 and 210 bytes are only 2-byte aligned (and the 176-byte
+//     Q5_K blocks take the same path): the wavefront copies the
 //     row segment into LDS with fully coalesced loads (64 lanes x 16 B
 //     contiguous) and each lane reads its unit back with aligned dword reads,
 //     realigned in registers with v_alignbyte_b32.
@@ -39,7 +40,8 @@
 //                 grouped entry point): one launch instead of one per matrix.
 //   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
 //                 once per workgroup; otherwise as gemv2.
-//   gemv_kernel   batch 2..8 of Q8_0 / Q4_0 (and unaligned batch-1 rows): x
+//   gemv_kernel   batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K (and unaligned
+//                 batch-1 rows): x
 //                 segment and weight segments staged in LDS per workgroup.
 //   Batch 2..8 of Q4_K / Q6_K runs on the matrix cores (qmm_gemv_mfma.hip).
 #include "qmm_device.h"
@@ -57,6 +59,8 @@ template <> struct GemvUnit<T_Q4_0> { static constexpr int UE = 32, NRUN = 8; };
 template <> struct GemvUnit<T_Q8_0> { static constexpr int UE = 32, NRUN = 8; };
 template <> struct GemvUnit<T_Q4_K> { static constexpr int UE = 64, NRUN = 16; };
 template <> struct GemvUnit<T_Q6_K> { static constexpr int UE = 64, NRUN = 16; };
+template <> struct GemvUnit<T_Q5_0> { static constexpr int UE = 32, NRUN = 8; };
+template <> struct GemvUnit<T_Q5_K> { static constexpr int UE = 64, NRUN = 16; };
 
 // Element (relative to the segment start) of the first element of run j of
 // lane-unit u.  The run order is the order in which unit_dot consumes x.
@@ -65,9 +69,9 @@ __device__ __forceinline__ int run_elem(int u, int j)
 {
     if constexpr (T == T_Q8_0) {
         return 32 * u + 4 * j;                                // codes 4j..4j+3
-    } else if constexpr (T == T_Q4_0) {
+    } else if constexpr (T == T_Q4_0 || T == T_Q5_0) {
         return 32 * u + (j < 4 ? 4 * j : 16 + 4 * (j - 4));   // low nibbles, then high
-    } else if constexpr (T == T_Q4_K) {
+    } else if constexpr (T == T_Q4_K || T == T_Q5_K) {
         return 64 * u + (j < 8 ? 4 * j : 32 + 4 * (j - 8));   // sub-block 2p, then 2p+1
     } else {
         // u = 4 sb + 2 h + hf: elements 128h + 32g + 16hf + i of super-block sb,
@@ -91,6 +95,8 @@ template <> struct URaw<T_Q8_0> { uint32_t d; uint32_t c[8]; };
 template <> struct URaw<T_Q4_0> { uint32_t d; uint32_t c[4]; };
 template <> struct URaw<T_Q4_K> { u32x4 hd; uint32_t c[8]; };
 template <> struct URaw<T_Q6_K> { uint32_t qa[4], qb[4], qh[4], sc[2], d; };
+template <> struct URaw<T_Q5_0> { uint32_t d; uint32_t qh; uint32_t c[4]; };
+template <> struct URaw<T_Q5_K> { u32x4 hd; uint32_t h[8]; uint32_t c[8]; };
 
 // Read NDW dwords starting at an even byte offset of an LDS byte buffer
 // (addressed as dwords), realigning in registers.
@@ -124,6 +130,23 @@ __device__ __forceinline__ void raw_from_lds(const uint32_t *seg, int u, URaw<T>
         const uint32_t off = 18u * u;               // fp16 d, then 16 code bytes
         r.d = lds_read_u16(seg, off);
         lds_read_bytes<4>(seg, off + 2, r.c);
+    } else if constexpr (T == T_Q5_0) {
+        const uint32_t off = 22u * u;               // fp16 d, 32 high bits, 16 code bytes
+        uint32_t t[5];
+        r.d = lds_read_u16(seg, off);
+        lds_read_bytes<5>(seg, off + 2, t);
+        r.qh = t[0];
+        r.c[0] = t[1]; r.c[1] = t[2]; r.c[2] = t[3]; r.c[3] = t[4];
+    } else if constexpr (T == T_Q5_K) {
+        const int p = u & 3;
+        const uint32_t *blk = seg + 44 * (u >> 2);  // 176 B = 44 dwords
+        r.hd = *(const u32x4 *)blk;
+        const u32x4 h0 = *(const u32x4 *)(blk + 4), h1 = *(const u32x4 *)(blk + 8);
+        const u32x4 c0 = *(const u32x4 *)(blk + 12 + 8 * p), c1 = *(const u32x4 *)(blk + 16 + 8 * p);
+        r.h[0] = h0.x; r.h[1] = h0.y; r.h[2] = h0.z; r.h[3] = h0.w;
+        r.h[4] = h1.x; r.h[5] = h1.y; r.h[6] = h1.z; r.h[7] = h1.w;
+        r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
+        r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
     } else if constexpr (T == T_Q4_K) {
         const int p = u & 3;
         const uint32_t *blk = seg + 36 * (u >> 2);  // 144 B = 36 dwords
@@ -223,7 +246,9 @@ struct XFromLds {
 // Sums of x over the groups of a unit that share a constant code offset:
 // Q4_0 the block (1), Q4_K the two sub-blocks (2), Q6_K the four 16-element
 // scale groups (4); Q8_0 has no offset.
-template <int T> struct XSumCount { static constexpr int N = T == T_Q4_0 ? 1 : T == T_Q4_K ? 2 : T == T_Q6_K ? 4 : 1; };
+template <int T> struct XSumCount {
+    static constexpr int N = (T == T_Q4_0 || T == T_Q5_0) ? 1 : (T == T_Q4_K || T == T_Q5_K) ? 2 : T == T_Q6_K ? 4 : 1;
+};
 
 // ... or from registers (batch 1): the lane's unit is the same for every row,
 // so its offset sums are computed once (sums()) and reused.
@@ -239,12 +264,12 @@ struct XFromRegs {
 template <int T>
 __device__ __forceinline__ void unit_x_sums(const f32x4 *xr, float *xs)
 {
-    if constexpr (T == T_Q4_0) {
+    if constexpr (T == T_Q4_0 || T == T_Q5_0) {
         float a = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) a += sum4(xr[i]) + sum4(xr[4 + i]);
         xs[0] = a;
-    } else if constexpr (T == T_Q4_K) {
+    } else if constexpr (T == T_Q4_K || T == T_Q5_K) {
         float a = 0.f, b = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -336,6 +361,116 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
                 acc[r][b] = __builtin_fmaf(d, __builtin_fmaf(-8.f, xsum[b], t), acc[r][b]);
             }
         }
+    } else if constexpr (T == T_Q5_0) {
+        // as Q4_0, with bit 4 of each code from the block's 32-bit word
+        AccT slo[R][B], shi[R][B];
+        float xsum[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            xsum[b] = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) slo[r][b] = shi[r][b] = zero_acc<AccT>();
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 xl[B], xh[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                xl[b] = xg(i, b);
+                xh[b] = xg(4 + i, b);
+                if constexpr (!XG::PRE)
+                    xsum[b] += sum4(xl[b]) + sum4(xh[b]);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t c = raw[r].c[i], hb = raw[r].qh;
+                const uint32_t lo = opaque((c & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (4 * i)));
+                const uint32_t hi = opaque(((c >> 4) & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (16 + 4 * i)));
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    slo[r][b] = dot4_u(lo, xl[b], slo[r][b]);
+                    shi[r][b] = dot4_u(hi, xh[b], shi[r][b]);
+                }
+            }
+        }
+        if constexpr (XG::PRE)
+#pragma unroll
+            for (int b = 0; b < B; ++b) xsum[b] = xg.sum(b, 0);
+        // d * sum (q - 16) x = d * (slo + shi - 16 sum x)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float d = h2f(raw[r].d);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float t = fin(slo[r][b]) + fin(shi[r][b]);
+                acc[r][b] = __builtin_fmaf(d, __builtin_fmaf(-16.f, xsum[b], t), acc[r][b]);
+            }
+        }
+    } else if constexpr (T == T_Q5_K) {
+        // as Q4_K, with bit 4 of each code at bit 2p (low nibbles, sub-block
+        // 2p) or 2p + 1 (high nibbles) of the qh byte of its element
+        const int p = u & 3;
+        float dsc0[R], dsc1[R], dm0[R], dm1[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            uint32_t sc0, m0, sc1, m1;
+            q4k_scale_min(raw[r].hd.y, raw[r].hd.z, raw[r].hd.w, 2 * p, sc0, m0);
+            q4k_scale_min(raw[r].hd.y, raw[r].hd.z, raw[r].hd.w, 2 * p + 1, sc1, m1);
+            const float d = h2f(raw[r].hd.x & 0xffffu), dmin = h2f(raw[r].hd.x >> 16);
+            dsc0[r] = d * (float)sc0;
+            dsc1[r] = d * (float)sc1;
+            dm0[r] = dmin * (float)m0;
+            dm1[r] = dmin * (float)m1;
+        }
+        AccT s0[R][B], s1[R][B];
+        float x0[B], x1[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            x0[b] = x1[b] = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) s0[r][b] = s1[r][b] = zero_acc<AccT>();
+        }
+        const uint32_t sh0 = 2u * (uint32_t)p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            f32x4 xl[B], xh[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                xl[b] = xg(i, b);
+                xh[b] = xg(8 + i, b);
+                if constexpr (!XG::PRE) {
+                    x0[b] += sum4(xl[b]);
+                    x1[b] += sum4(xh[b]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t c = raw[r].c[i], hb = raw[r].h[i];
+                const uint32_t lo = opaque((c & 0x0f0f0f0fu) | (((hb >> sh0) & 0x01010101u) << 4));
+                const uint32_t hi = opaque(((c >> 4) & 0x0f0f0f0fu) | (((hb >> (sh0 + 1u)) & 0x01010101u) << 4));
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    s0[r][b] = dot4_u(lo, xl[b], s0[r][b]);
+                    s1[r][b] = dot4_u(hi, xh[b], s1[r][b]);
+                }
+            }
+        }
+        if constexpr (XG::PRE)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                x0[b] = xg.sum(b, 0);
+                x1[b] = xg.sum(b, 1);
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                float t = dsc0[r] * fin(s0[r][b]);
+                t = __builtin_fmaf(dsc1[r], fin(s1[r][b]), t);
+                t = __builtin_fmaf(-dm0[r], x0[b], t);
+                t = __builtin_fmaf(-dm1[r], x1[b], t);
+                acc[r][b] += t;
+            }
     } else if constexpr (T == T_Q4_K) {
         // unit = (super-block, code group p = u % 4): sub-block 2p in the low
         // nibbles, 2p+1 in the high nibbles
@@ -1085,6 +1220,8 @@ hipError_t launch_gemv(int type, const void *w, int64_t n, int64_t k, size_t rb,
     case T_Q8_0: return launch_t<T_Q8_0>(wb, n, k, rb, x, batch, y, s);
     case T_Q4_K: return launch_t<T_Q4_K>(wb, n, k, rb, x, batch, y, s);
     case T_Q6_K: return launch_t<T_Q6_K>(wb, n, k, rb, x, batch, y, s);
+    case T_Q5_0: return launch_t<T_Q5_0>(wb, n, k, rb, x, batch, y, s);
+    case T_Q5_K: return launch_t<T_Q5_K>(wb, n, k, rb, x, batch, y, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1130,6 +1267,8 @@ hipError_t launch_gemv_multi(int type, int np, const void *const *w, const int64
     case T_Q8_0: return launch_multi_t<T_Q8_0>(np, w, n, k, rb, x, batch, y, s);
     case T_Q4_K: return launch_multi_t<T_Q4_K>(np, w, n, k, rb, x, batch, y, s);
     case T_Q6_K: return launch_multi_t<T_Q6_K>(np, w, n, k, rb, x, batch, y, s);
+    case T_Q5_0: return launch_multi_t<T_Q5_0>(np, w, n, k, rb, x, batch, y, s);
+    case T_Q5_K: return launch_multi_t<T_Q5_K>(np, w, n, k, rb, x, batch, y, s);
     default: return hipErrorInvalidValue;
     }
 }

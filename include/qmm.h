@@ -29,6 +29,17 @@
  *             w = d scale[e / 16] (q - 32); element e = 128 h + 32 g + l has
  *             its low 4 bits in nibble (g / 2) of ql[64 h + 32 (g % 2) + l]
  *             and its high 2 bits at bit 2 g of qh[32 h + l]
+ *   QMM_Q5_0  32 elements, 22 B:  d | 4 B high bits | 16 B codes
+ *             w = d (q - 16); low 4 bits of element i as in Q4_0, bit 4 is
+ *             bit i of the little-endian 32-bit word
+ *   QMM_Q5_K  256 elements, 176 B: d | dmin | 12 B scales | 32 B qh |
+ *             128 B codes; w = d sc_j q - dmin m_j as in Q4_K (same scale
+ *             packing and low-4-bit placement); bit 4 of element (j, l) is
+ *             bit j of qh[l]
+ *   (shimmy "Architecture", Quantization table names the 5-bit super-block
+ *   with a high-bit plane and dotLLM "GPU Inference", Quantization on GPU
+ *   table lists Q5_0 / Q5_K; neither prints their layout, which here is the
+ *   public GGUF one.)
  *
  * Common conventions
  *   - Weight matrix w: n rows (output features) of qmm_row_bytes(t, k)
@@ -68,7 +79,9 @@ typedef enum qmm_type {
     QMM_Q4_0 = 0,
     QMM_Q8_0 = 1,
     QMM_Q4_K = 2,
-    QMM_Q6_K = 3
+    QMM_Q6_K = 3,
+    QMM_Q5_0 = 4,
+    QMM_Q5_K = 5
 } qmm_type;
 
 typedef enum qmm_status {
@@ -83,7 +96,7 @@ typedef enum qmm_status {
 /* Elements per block (32 or 256); 0 for an unknown type. */
 QMM_API int qmm_block_elems(int type);
 
-/* Bytes per block (18, 34, 144, 210); 0 for an unknown type. */
+/* Bytes per block (18, 34, 144, 210, 22, 176); 0 for an unknown type. */
 QMM_API int qmm_block_bytes(int type);
 
 /* Bytes of one row of k weights; 0 if the type is unknown, k < 0 or k is not

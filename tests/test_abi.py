@@ -49,8 +49,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_sizes_and_strings():
     q = _lib()
-    assert [q.block_elems(t) for t in (q.Q4_0, q.Q8_0, q.Q4_K, q.Q6_K)] == [32, 32, 256, 256]
-    assert [q.block_bytes(t) for t in (q.Q4_0, q.Q8_0, q.Q4_K, q.Q6_K)] == [18, 34, 144, 210]
+    assert [q.block_elems(t) for t in (q.Q4_0, q.Q8_0, q.Q4_K, q.Q6_K, q.Q5_0, q.Q5_K)] == [32, 32, 256, 256, 32, 256]
+    assert [q.block_bytes(t) for t in (q.Q4_0, q.Q8_0, q.Q4_K, q.Q6_K, q.Q5_0, q.Q5_K)] == [18, 34, 144, 210, 22, 176]
+    assert q.block_elems(6) == 0 and q.block_bytes(6) == 0
     assert q.row_bytes(q.Q4_K, 4096) == 2304 and q.row_bytes(q.Q6_K, 14336) == 11760
     assert q.row_bytes(q.Q8_0, 48) == 0 and q.row_bytes(q.Q8_0, -32) == 0 and q.row_bytes(9, 32) == 0
     assert q.block_elems(-1) == 0
@@ -90,14 +91,14 @@ def test_validation_errors_gemv():
 def test_validation_errors_dequant_and_gemm():
     q = _lib()
     L = q.lib
-    assert L.qmm_dequant(5, A, 4, 32, A, None) == q.ERR_TYPE
+    assert L.qmm_dequant(6, A, 4, 32, A, None) == q.ERR_TYPE
     assert L.qmm_dequant(q.Q6_K, A, 4, 200, A, None) == q.ERR_SHAPE
     assert L.qmm_dequant(q.Q6_K, None, 4, 256, A, None) == q.ERR_NULL
     assert L.qmm_dequant(q.Q6_K, A, 4, 256, None, None) == q.ERR_NULL
     assert L.qmm_dequant(q.Q6_K, A, 4, 256, MIS, None) == q.ERR_ALIGN
     assert L.qmm_dequant(q.Q6_K, None, 0, 256, None, None) == q.OK
     assert L.qmm_dequant(q.Q6_K, None, 4, 0, None, None) == q.OK
-    assert L.qmm_gemm_prefill(4, A, 4, 32, A, 8, A, None) == q.ERR_TYPE
+    assert L.qmm_gemm_prefill(6, A, 4, 32, A, 8, A, None) == q.ERR_TYPE
     assert L.qmm_gemm_prefill(q.Q4_0, A, 4, 16, A, 8, A, None) == q.ERR_SHAPE
     assert L.qmm_gemm_prefill(q.Q4_0, A, 4, 32, A, -8, A, None) == q.ERR_SHAPE
     assert L.qmm_gemm_prefill(q.Q4_0, A, 4, 32, None, 8, A, None) == q.ERR_NULL

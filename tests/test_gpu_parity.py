@@ -25,7 +25,7 @@ if not torch.cuda.is_available():
 import dequant_matmul_amd as q  # noqa: E402
 
 DEV = "cuda:0"
-TYPES = [G.Q4_0, G.Q8_0, G.Q4_K, G.Q6_K]
+TYPES = [G.Q4_0, G.Q8_0, G.Q4_K, G.Q6_K, G.Q5_0, G.Q5_K]
 GEMV_TOL = 2e-5
 GEMM_TOL = 1e-3
 
@@ -114,7 +114,8 @@ def test_gemv_small_and_ragged(t, batch):
 
 @pytest.mark.parametrize("t,n,k", [(G.Q8_0, 2048, 2048), (G.Q4_0, 2048, 5632), (G.Q4_0, 256, 2048),
                                    (G.Q4_K, 14336, 4096), (G.Q4_K, 4096, 14336), (G.Q6_K, 4096, 14336),
-                                   (G.Q6_K, 1024, 4096)])
+                                   (G.Q6_K, 1024, 4096), (G.Q5_0, 4096, 4096), (G.Q5_K, 14336, 4096),
+                                   (G.Q5_K, 4096, 14336)])
 @pytest.mark.parametrize("batch", [1, 8])
 def test_gemv_workload_shapes(t, n, k, batch):
     say("gemv full", G.NAMES[t], n, k, batch)
@@ -204,7 +205,7 @@ def test_gemv_batch_many_tiles(t, n, k, batch):
 def test_gemv_unaligned_rows():
     """Row sizes that are not a multiple of 16 bytes take the 2-byte staging
     path."""
-    for t, nb in ((G.Q8_0, 3), (G.Q4_0, 5), (G.Q6_K, 3)):
+    for t, nb in ((G.Q8_0, 3), (G.Q4_0, 5), (G.Q6_K, 3), (G.Q5_0, 3)):
         k = G.BLOCK_ELEMS[t] * nb
         assert G.row_bytes(t, k) % 16 != 0
         for batch in (1, 5):
@@ -261,13 +262,13 @@ def test_gemm_one_hot_rows_give_fp16_weights(t):
 
 
 def _tiny_scales(t, w, n, k, rng):
-    """Overwrite every fp16 scale field (d, and dmin for Q4_K) with a random
+    """Overwrite every fp16 scale field (d, and dmin for Q4_K / Q5_K) with a random
     subnormal fp16 (bits 0x0001..0x03ff), so that many dequantized weights are
     fp16 subnormals or need rounding near the subnormal range."""
     w = w.copy().reshape(n, -1)
     bb, be = G.BLOCK_BYTES[t], G.BLOCK_ELEMS[t]
     nb = k // be
-    offs = {G.Q8_0: [0], G.Q4_0: [0], G.Q4_K: [0, 2], G.Q6_K: [208]}[t]
+    offs = {G.Q8_0: [0], G.Q4_0: [0], G.Q4_K: [0, 2], G.Q6_K: [208], G.Q5_0: [0], G.Q5_K: [0, 2]}[t]
     for b in range(nb):
         for o in offs:
             bits = rng.integers(1, 0x400, size=n).astype(np.uint16)
@@ -295,7 +296,7 @@ def test_gemm_one_hot_subnormal_scales(t):
 
 
 @pytest.mark.parametrize("t,n", [(G.Q8_0, 14336), (G.Q8_0, 4096), (G.Q4_K, 14336), (G.Q4_K, 4096),
-                                 (G.Q4_0, 4096), (G.Q6_K, 4096)])
+                                 (G.Q4_0, 4096), (G.Q6_K, 4096), (G.Q5_0, 4096), (G.Q5_K, 14336)])
 def test_gemm_prefill_workload_shapes(t, n):
     m, k = G.PREFILL_M, 4096
     say("gemm full", G.NAMES[t], m, n, k)
