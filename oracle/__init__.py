@@ -60,6 +60,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_dequant_f64.argtypes = [ctypes.c_int, P, I64, I64, P]
         L.oracle_gemv.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P, P]
         L.oracle_gemm.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P, I64, P, P]
+        L.oracle_double_to_half.argtypes = [ctypes.c_double]
+        L.oracle_double_to_half.restype = ctypes.c_uint16
+        L.oracle_float_to_half_array.argtypes = [P, I64, P]
+        L.oracle_float_to_half_array.restype = None
+        L.oracle_embed.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P]
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_set_threads.restype = None
         L.oracle_max_threads.argtypes = []
@@ -95,6 +100,19 @@ def half_to_float(h: np.ndarray) -> np.ndarray:
     return out
 
 
+def to_half_bits(x) -> np.ndarray:
+    """fp32 values -> IEEE binary16 bit patterns (uint16), nearest-even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().oracle_float_to_half_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def double_to_half_bits(v: float) -> int:
+    """One fp64 value -> binary16 bits, nearest-even."""
+    return int(lib().oracle_double_to_half(float(v)))
+
+
 def q4k_scale_min(s12: bytes | np.ndarray, j: int) -> tuple[int, int]:
     s = np.ascontiguousarray(np.frombuffer(bytes(s12), dtype=np.uint8))
     assert s.size == 12
@@ -125,6 +143,22 @@ def dequant_f64(t: int, w: np.ndarray, n: int, k: int) -> np.ndarray:
     out = np.empty((n, k), dtype=np.float64)
     _check(lib().oracle_dequant_f64(t, _ptr(w), n, k, _ptr(out)), "dequant_f64")
     return out
+
+
+def dequant_f16(t: int, w: np.ndarray, n: int, k: int) -> np.ndarray:
+    """fp16 dequant (bits, uint16 [n, k]): the fp32 dequant rounded to
+    binary16, nearest-even."""
+    return to_half_bits(dequant(t, w, n, k))
+
+
+def embed(t: int, table: np.ndarray, vocab: int, k: int, ids, f16: bool = False) -> np.ndarray:
+    """Embedding gather: row i = fp32 dequant of table row ids[i] (zeros for
+    an id outside [0, vocab)); ``f16`` returns binary16 bits instead."""
+    table = _wbytes(table, t, vocab, k)
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+    out = np.empty((ids.size, k), dtype=np.float32)
+    _check(lib().oracle_embed(t, _ptr(table), vocab, k, _ptr(ids), ids.size, _ptr(out)), "embed")
+    return to_half_bits(out) if f16 else out
 
 
 def gemv(t: int, w: np.ndarray, n: int, k: int, x: np.ndarray):

@@ -16,6 +16,10 @@
  *   - gemm:     Y[m][n] = sum_k X[m][k] * w[n][k] with X given as IEEE fp16
  *               bits, w the exact fp32 dequant (not rounded to fp16), fp64
  *               accumulation in ascending k, plus the same |.| sum.
+ *   - embed:    out[i] = dequant of table row ids[i] (zeros for an id out of
+ *               range);
+ *   - fp16:     any fp32 result rounded to binary16, nearest-even (the FP16
+ *               outputs of the dequant and the embedding gather).
  *
  * Sources (page / section):
  *   - shimmy "Airframe GPU pipeline", per-layer ops: dequantization happens
@@ -119,6 +123,47 @@ void oracle_half_to_float_array(const uint16_t *h, int64_t n, float *out)
 {
     for (int64_t i = 0; i < n; i++)
         out[i] = oracle_half_to_float(h[i]);
+}
+
+/*
+ * value -> IEEE 754 binary16 bits, round to nearest with ties to even,
+ * written from the format definition.  A finite nonzero |v| is rounded to a
+ * multiple of the quantum 2^(E - 10) of its binade, E = floor(log2 |v|),
+ * with E raised to -14 below the normal range (the subnormal quantum
+ * 2^-24):  m = rint(|v| / 2^(E - 10)) (ties to even in the default rounding
+ * mode), bits = ((E + 15) << 10) + m - 1024.  The formula also covers the
+ * subnormals (E = -14, m < 1024 gives bits = m) and the carry into the next
+ * binade (m = 2048); a result at or above the Inf pattern 0x7c00 is Inf.
+ * NaN -> quiet NaN 0x7e00 with the sign kept.
+ * (dotLLM "GPU Inference", Forward Pass: the hidden state is FP16; Custom
+ * Kernels table: dequant_* kernels write FP16.)
+ */
+uint16_t oracle_double_to_half(double v)
+{
+    uint16_t s = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(s | 0x7e00);
+    if (isinf(a))
+        return (uint16_t)(s | 0x7c00);
+    if (a == 0.0)
+        return s;
+    int E;
+    frexp(a, &E); /* a = f 2^E with 0.5 <= f < 1 */
+    E -= 1;       /* now 1 <= a / 2^E < 2 */
+    if (E < -14)
+        E = -14;
+    double m = rint(ldexp(a, 10 - E)); /* scaling by a power of two is exact */
+    long bits = ((long)(E + 15) << 10) + (long)m - 1024;
+    if (bits >= 0x7c00)
+        return (uint16_t)(s | 0x7c00);
+    return (uint16_t)(s | bits);
+}
+
+void oracle_float_to_half_array(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_double_to_half((double)x[i]);
 }
 
 static uint16_t rd16(const uint8_t *p)
@@ -283,6 +328,34 @@ int oracle_dequant_f64(int t, const uint8_t *w, int64_t n, int64_t k, double *ou
     for (int64_t r = 0; r < n; r++)
         for (int64_t i = 0; i < k; i++)
             out[r * k + i] = elem_value(t, w + r * rb + (i / be) * bb, (int)(i % be));
+    return 0;
+}
+
+/*
+ * Embedding row gather: out[i][:] = the fp32 dequant of row ids[i] of the
+ * table [vocab][k]; an id outside [0, vocab) gives a row of zeros (a choice
+ * of this library: the pages do not say what an invalid id does).
+ * (dotLLM "GPU Inference", Forward Pass step 2 and Weight Loading Pipeline:
+ * the token embeddings stay quantized on the GPU and the lookup kernel
+ * dequantizes the rows of the given token ids into the hidden state.)
+ */
+int oracle_embed(int t, const uint8_t *table, int64_t vocab, int64_t k,
+                 const int32_t *ids, int64_t seq, float *out)
+{
+    int rc = check(t, vocab, k);
+    if (rc)
+        return rc;
+    if (seq < 0)
+        return -2;
+    size_t rb = oracle_row_bytes(t, k);
+    for (int64_t i = 0; i < seq; i++) {
+        int64_t id = ids[i];
+        float *dst = out + (size_t)i * k;
+        if (id >= 0 && id < vocab)
+            dequant_row(t, table + (size_t)id * rb, k, dst);
+        else
+            memset(dst, 0, (size_t)k * sizeof(float));
+    }
     return 0;
 }
 

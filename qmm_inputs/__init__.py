@@ -27,6 +27,7 @@ Distributions (the workload definitions that go with the pages):
   Q5_0 / Q5_K (no workload names them; the Q4_0 / Q4_K recipes): d (and
         dmin) as for Q4_0 / Q4_K, every other byte uniform (q ~ U{0..31})
   activations: fp32 (decode) or fp16 (prefill) ~ N(0, 1)
+  token ids: int32 ~ U{0..vocab-1}
 
 Seeds: matrix i of workload c uses seed 1000*c + i; its activation uses
 1000*c + 500 + i.
@@ -125,6 +126,12 @@ def gen_x(k: int, batch: int, seed: int) -> np.ndarray:
     return rng.standard_normal((batch, k), dtype=np.float32)
 
 
+def gen_ids(vocab: int, seq: int, seed: int) -> np.ndarray:
+    """int32 token ids [seq] ~ U{0..vocab-1}."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, vocab, size=seq, dtype=np.int64).astype(np.int32)
+
+
 def gen_x_f16(m: int, k: int, seed: int) -> np.ndarray:
     """fp16 activations [m, k] ~ N(0, 1) (drawn in fp32, rounded RNE)."""
     rng = np.random.default_rng(seed)
@@ -185,6 +192,11 @@ def workload(cfg: int):
         # the prefill chunk GEMMs of workload 4 in Q5_0 and Q5_K
         mats = [("gate_q5_0", Q5_0, 14336, 4096), ("q_q5_0", Q5_0, 4096, 4096),
                 ("gate_q5_k", Q5_K, 14336, 4096), ("q_q5_k", Q5_K, 4096, 4096)]
+    elif cfg == 9:
+        # quantized token-embedding tables for the row gather: the Llama 3.2
+        # 1B table in Q8_0 (the type the pages' embedding kernel reads) and
+        # the Llama-3-8B table in Q4_K; ids ~ U{0..vocab-1}, 1 or 512 tokens
+        mats = [("embd_q8_0", Q8_0, 128256, 2048), ("embd_q4_k", Q4_K, 128256, 4096)]
     else:
         raise ValueError("unknown workload %r" % (cfg,))
     return [(nm, t, n, k, 1000 * cfg + i) for i, (nm, t, n, k) in enumerate(mats)]

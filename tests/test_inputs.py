@@ -79,3 +79,13 @@ def test_workload_shapes_and_byte_totals():
     assert head[2] * G.row_bytes(head[1], head[3]) == 430940160
     seeds = [s for *_, s in G.workload(3)]
     assert len(set(seeds)) == len(seeds) and seeds[0] == 3000
+
+
+def test_token_ids():
+    ids = G.gen_ids(128256, 4096, seed=9500)
+    assert ids.dtype == np.int32 and ids.min() >= 0 and ids.max() < 128256
+    assert np.array_equal(ids, G.gen_ids(128256, 4096, seed=9500))
+    assert len(np.unique(ids)) > 4000       # nearly all distinct rows
+    embd = G.workload(9)
+    # Llama 3.2 1B Q8_0 token table: 128256 x 2048 at 34 B per 32 weights
+    assert embd[0][1:4] == (G.Q8_0, 128256, 2048) and 128256 * G.row_bytes(G.Q8_0, 2048) == 279085056

@@ -11,7 +11,7 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_dot.py"]
+PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_dot.py", "tests/test_oracle_embed.py"]
 
 MUTANTS = {
     "q4_0 offset": ("return d * (double)(q - 8);", "return d * (double)(q - 7);"),
@@ -40,6 +40,11 @@ MUTANTS = {
     "gemv batch index": ("double p = (double)wrow[i] * (double)x[b * k + i];",
                          "double p = (double)wrow[i] * (double)x[i];"),
     "gemv abs as sum": ("acc += p;", "acc += fabs(p);"),
+    "fp16 ties away from zero": ("double m = rint(ldexp(a, 10 - E));", "double m = floor(ldexp(a, 10 - E) + 0.5);"),
+    "fp16 subnormal binade": ("if (E < -14)", "if (E < -15)"),
+    "fp16 overflow threshold": ("if (bits >= 0x7c00)", "if (bits >= 0x7bff)"),
+    "embed invalid id reads row 0": ("memset(dst, 0, (size_t)k * sizeof(float));", "dequant_row(t, table, k, dst);"),
+    "embed id order": ("int64_t id = ids[i];", "int64_t id = ids[seq - 1 - i];"),
     "gemm row index": ("double p = oracle_half_to_double(x[mm * k + i]) * (double)wrow[i];",
                        "double p = oracle_half_to_double(x[ii * k + i]) * (double)wrow[i];"),
 }
