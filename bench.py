@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized-weight matmul on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix|q5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix|q5|embed]
 
 A step is one decode pass over the TinyLlama-shaped Q4_0 weight stream:
 22 layers x (q, k, v, o, gate, up, down) = 154 GEMVs at batch 1 on one
@@ -15,8 +15,9 @@ of the 8 TB/s peak, the decode-equivalent tokens/s, the roofline of the
 dominant kernel (the Q4_0 GEMV) from per-launch HIP-event timings, the CPU
 oracle timed on a bounded sample of the same workload, and secondary figures
 for the other workloads (Q8_0 single matrix, Llama-3-8B Q4_K set, 512-token
-prefill GEMMs, Q4_K_M-style mix with a Q6_K LM head at batch 1/4/8, and the
-same shapes in the 5-bit types Q5_K / Q5_0).
+prefill GEMMs, Q4_K_M-style mix with a Q6_K LM head at batch 1/4/8, the
+same shapes in the 5-bit types Q5_K / Q5_0, and the quantized embedding
+gather for one decode token and a 512-token chunk).
 """
 from __future__ import annotations
 
@@ -53,7 +54,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix", "q5"], default="all",
+    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix", "q5", "embed"], default="all",
                    help="which secondary workloads to run after the primary line's (all by default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU oracle sample")
@@ -90,6 +91,25 @@ class Problem:
                                         self.batch, self.y.data_ptr(), stream)
         if st != 0:
             raise RuntimeError("%s %s: %s" % (self.kind, self.name, q.status_str(st)))
+
+
+class Embed:
+    """One embedding gather (qmm_embed / qmm_embed_f16) with its buffers."""
+
+    def __init__(self, torch, name, t, vocab, k, table, ids, out):
+        self.name, self.t, self.vocab, self.k = name, t, vocab, k
+        self.table, self.ids, self.out = table, ids, out
+        self.seq = ids.shape[0]
+        self.f16 = out.dtype == torch.float16
+        # algorithmic bytes: ids + the rows read + the output written
+        self.bytes = 4 * self.seq + self.seq * G.row_bytes(t, k) + self.seq * k * (2 if self.f16 else 4)
+
+    def launch(self, q, stream):
+        f = q.lib.qmm_embed_f16 if self.f16 else q.lib.qmm_embed
+        st = f(self.t, self.table.data_ptr(), self.vocab, self.k, self.ids.data_ptr(), self.seq,
+               self.out.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError("embed %s: %s" % (self.name, q.status_str(st)))
 
 
 class Group:
@@ -286,6 +306,33 @@ def sec_prefill(torch, q, steps, warmup, dev, cfg=4):
     return res
 
 
+def sec_embed(torch, q, steps, warmup, dev, rotate=32):
+    """Embedding gathers from the Llama 3.2 1B Q8_0 and Llama-3-8B Q4_K token
+    tables: one decode token and one 512-token chunk, fp32 and fp16 outputs;
+    each graph issues `rotate` gathers with distinct ids and outputs."""
+    res = {}
+    for name, t, vocab, k, seed in G.workload(9):
+        table = torch.from_numpy(G.gen_weights(t, vocab, k, seed)).to(dev)
+        for seq in (1, 512):
+            for dt, dn in ((torch.float32, "f32"), (torch.float16, "f16")):
+                probs = []
+                for r in range(rotate):
+                    ids = torch.from_numpy(G.gen_ids(vocab, seq, G.x_seed(9, 1000 * r + seq))).to(dev)
+                    probs.append(Embed(torch, name, t, vocab, k, table, ids,
+                                       torch.empty((seq, k), dtype=dt, device=dev)))
+                g = capture(torch, q, probs)
+                tg = time_graph(torch, g, steps, warmup) / rotate
+                b = probs[0].bytes
+                res["%s_seq%d_%s" % (name, seq, dn)] = {
+                    "table": "%d x %d %s" % (vocab, k, G.NAMES[t]), "tokens": seq, "out": dn,
+                    "us_per_call": round(tg * 1e6, 3), "GB_s": round(b / tg / 1e9, 1),
+                    "pct_hbm_peak": round(100 * b / tg / 1e9 / HBM_PEAK_GBS, 2)}
+                del g, probs
+        del table
+        torch.cuda.empty_cache()
+    return res
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -424,6 +471,9 @@ def main():
             del wts
             torch.cuda.empty_cache()
             sec["prefill_512_q5"] = sec_prefill(torch, q, args.steps, args.warmup, dev, cfg=8)
+        if want("embed"):
+            log("secondary: embedding gathers")
+            sec["embed"] = sec_embed(torch, q, args.steps, args.warmup, dev)
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 

@@ -10,6 +10,7 @@ CPU fallback: if the library is missing, importing this package fails.
     y = qmm.gemv(w_bytes, qmm.Q4_K, n, k, x)          # x fp32 [B, k] -> y fp32 [B, n]
     Y = qmm.gemm_prefill(w_bytes, qmm.Q4_K, n, k, X)  # X fp16 [m, k] -> Y fp32 [m, n]
     W = qmm.dequant(w_bytes, qmm.Q4_K, n, k)          # -> fp32 [n, k]
+    H = qmm.embed(table, qmm.Q8_0, vocab, k, ids)      # ids int32 [seq] -> fp32 [seq, k]
 
 Block types and layouts follow shimmy "Architecture" (Quantization table) and
 dotLLM "GPU Inference" (Quantization on GPU table); see include/qmm.h.
@@ -33,6 +34,9 @@ SIGNATURES = {
     "qmm_block_bytes": (_I, [_I]),
     "qmm_row_bytes": (_SZ, [_I, _I64]),
     "qmm_dequant": (_I, [_I, _P, _I64, _I64, _P, _P]),
+    "qmm_dequant_f16": (_I, [_I, _P, _I64, _I64, _P, _P]),
+    "qmm_embed": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "qmm_embed_f16": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
     "qmm_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
     "qmm_gemv_multi": (_I, [_I, _I, _P, _P, _I64, _P, _I64, _P, _P]),
     "qmm_gemm_prefill": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
@@ -115,6 +119,40 @@ def dequant(w, qtype: int, n: int, k: int, out=None):
     if out is None:
         out = torch.empty((n, k), dtype=torch.float32, device=w.device)
     _call(lib.qmm_dequant(qtype, w.data_ptr(), n, k, out.data_ptr(), _stream_ptr(w.device)), "qmm_dequant")
+    return out
+
+
+def dequant_f16(w, qtype: int, n: int, k: int, out=None):
+    """fp16 [n, k] dequantized weights (the fp32 values rounded to nearest-even)."""
+    torch = _torch()
+    _check_w(w, qtype, n, k)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float16, device=w.device)
+    _call(lib.qmm_dequant_f16(qtype, w.data_ptr(), n, k, out.data_ptr(), _stream_ptr(w.device)),
+          "qmm_dequant_f16")
+    return out
+
+
+def embed(table, qtype: int, vocab: int, k: int, ids, dtype=None, out=None):
+    """Embedding gather: row r = dequantized table row ids[r] (zeros for an id
+    outside [0, vocab)).  ids: int32 device tensor [seq]; dtype float32
+    (default, exact) or float16."""
+    torch = _torch()
+    _check_w(table, qtype, vocab, k)
+    dtype = torch.float32 if dtype is None else dtype
+    if ids.dtype != torch.int32 or not ids.is_cuda or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 device tensor [seq]")
+    seq = ids.shape[0]
+    if out is None:
+        out = torch.empty((seq, k), dtype=dtype, device=table.device)
+    if dtype == torch.float32:
+        f = lib.qmm_embed
+    elif dtype == torch.float16:
+        f = lib.qmm_embed_f16
+    else:
+        raise ValueError("dtype must be torch.float32 or torch.float16")
+    _call(f(qtype, table.data_ptr(), vocab, k, ids.data_ptr(), seq, out.data_ptr(), _stream_ptr(table.device)),
+          "qmm_embed")
     return out
 
 

@@ -86,6 +86,60 @@ int qmm_dequant(int type, const void *w, int64_t n, int64_t k, float *out, void 
     return hip_status(qmm::launch_dequant(type, w, n, k, rb, out, (hipStream_t)stream));
 }
 
+int qmm_dequant_f16(int type, const void *w, int64_t n, int64_t k, uint16_t *out, void *stream)
+{
+    size_t rb = 0;
+    int st = check_common(type, w, n, k, &rb);
+    if (st != QMM_OK)
+        return st;
+    if (n == 0 || k == 0)
+        return QMM_OK;
+    if (out == nullptr)
+        return QMM_ERR_NULL;
+    if (!aligned16(out))
+        return QMM_ERR_ALIGN;
+    return hip_status(qmm::launch_dequant_f16(type, w, n, k, rb, out, (hipStream_t)stream));
+}
+
+// Shared checks of the two embedding gathers (the table is checked like a
+// weight matrix of vocab rows).
+static int check_embed(int type, const void *table, int64_t vocab, int64_t k, const int32_t *ids, int64_t seq,
+                const void *out, size_t *rb)
+{
+    int st = check_common(type, table, vocab, k, rb);
+    if (st != QMM_OK)
+        return st;
+    if (seq < 0 || seq > 0x7fffffff)
+        return QMM_ERR_SHAPE;
+    if (seq == 0 || k == 0)
+        return QMM_OK;
+    if (ids == nullptr || out == nullptr)
+        return QMM_ERR_NULL;
+    if (((uintptr_t)ids & 3u) != 0 || !aligned16(out))
+        return QMM_ERR_ALIGN;
+    return QMM_OK;
+}
+
+int qmm_embed(int type, const void *table, int64_t vocab, int64_t k, const int32_t *ids, int64_t seq, float *out,
+              void *stream)
+{
+    size_t rb = 0;
+    int st = check_embed(type, table, vocab, k, ids, seq, out, &rb);
+    if (st != QMM_OK || seq == 0 || k == 0)
+        return st;
+    return hip_status(qmm::launch_embed(type, table, vocab, k, rb, ids, seq, out, (hipStream_t)stream));
+}
+
+int qmm_embed_f16(int type, const void *table, int64_t vocab, int64_t k, const int32_t *ids, int64_t seq,
+                  uint16_t *out, void *stream)
+{
+    size_t rb = 0;
+    int st = check_embed(type, table, vocab, k, ids, seq, out, &rb);
+    if (st != QMM_OK || seq == 0 || k == 0)
+        return st;
+    return hip_status(qmm::launch_embed_f16(type, table, vocab, k, rb, ids, seq, out, (hipStream_t)stream));
+}
+
 int qmm_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch, float *y,
              void *stream)
 {

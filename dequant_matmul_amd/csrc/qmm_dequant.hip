@@ -12,11 +12,22 @@
 //   Q5_K  fma(q, d sc, -dmin m) as Q4_K
 // No division, reciprocal or fp16 intermediate is involved.
 //
+// The FP16 outputs (qmm_dequant_f16, qmm_embed_f16) round that fp32 value to
+// nearest-even (v_cvt_pk_f16_f32), as the pages' dequant-to-FP16 kernels and
+// FP16 hidden state do.
+//
+// The embedding gather (dotLLM "GPU Inference", Forward Pass step 2: the
+// lookup kernel dequantizes the rows of the given token ids) is the same
+// kernel with the source row taken from the id list; an id outside the table
+// produces a row of +0.
+//
 // Work split: one thread per 8 consecutive outputs of a row, so a wavefront
-// stores 2 KB of contiguous fp32 (the kernel is bound by these writes: the
-// output is 3.8x-7.1x the input bytes).  Inputs are read with naturally
-// aligned 2- or 4-byte loads (blocks of 34, 18, 22 and 210 bytes are only 2-byte
-// aligned); the reads hit in cache because neighbouring threads share blocks.
+// stores 2 KB of contiguous fp32 (1 KB of fp16); the kernel is bound by these
+// writes (the fp32 output is 3.8x-7.1x the input bytes).  Inputs are read
+// with naturally aligned 2- or 4-byte loads (blocks of 34, 18, 22 and 210
+// bytes are only 2-byte aligned); the reads hit in cache because
+// neighbouring threads share blocks.  The grid is capped and strides over the
+// outputs, so any size stays within the 32-bit dispatch limits.
 #include "qmm_device.h"
 #include "qmm_launch.h"
 
@@ -35,22 +46,10 @@ __device__ __forceinline__ void ld8_u16(const uint8_t *p, uint32_t &lo, uint32_t
     hi = (uint32_t)q[2] | ((uint32_t)q[3] << 16);
 }
 
+// The 8 weights of block blk starting at element eb (a multiple of 8).
 template <int T>
-__global__ void __launch_bounds__(256)
-dequant_kernel(const uint8_t *__restrict__ w, int64_t n, int64_t k, int64_t rb, float *__restrict__ out)
+__device__ __forceinline__ void decode8(const uint8_t *blk, int eb, float v[8])
 {
-    using F = Fmt<T>;
-    const int64_t per_row = k >> 3;
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (g >= n * per_row)
-        return;
-    const int64_t row = g / per_row;
-    const int e0 = (int)(g - row * per_row) * 8;  // first element (row-relative)
-    const int b = e0 / F::BE;
-    const int eb = e0 % F::BE;                     // first element inside the block
-    const uint8_t *blk = w + row * rb + (int64_t)b * F::BB;
-    float v[8];
-
     if constexpr (T == T_Q8_0) {
         const float d = h2f(ld16(blk));
         uint32_t c0, c1;
@@ -152,27 +151,109 @@ dequant_kernel(const uint8_t *__restrict__ w, int64_t n, int64_t k, int64_t rb, 
         v[4] = dsc * (ub0(q1) - 32.f); v[5] = dsc * (ub1(q1) - 32.f);
         v[6] = dsc * (ub2(q1) - 32.f); v[7] = dsc * (ub3(q1) - 32.f);
     }
-    float4 *o = (float4 *)(out + row * k + e0);
-    o[0] = make_float4(v[0], v[1], v[2], v[3]);
-    o[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-hipError_t launch_dequant(int type, const void *w, int64_t n, int64_t k, size_t rb, float *out,
-                          hipStream_t s)
+__device__ __forceinline__ void store8(float *o, const float v[8])
+{
+    float4 *p = (float4 *)o;
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// fp16_RNE of two fp32 values, packed (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_h2(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, h2v));
+}
+
+__device__ __forceinline__ void store8(uint16_t *o, const float v[8])
+{
+    *(uint4 *)o = make_uint4(pack_h2(v[0], v[1]), pack_h2(v[2], v[3]), pack_h2(v[4], v[5]), pack_h2(v[6], v[7]));
+}
+
+// Output row r (r < n) = source row r, or with GATHER source row ids[r]
+// (a row of zeros when that id is outside [0, vocab)).
+template <int T, typename O, bool GATHER>
+__global__ void __launch_bounds__(256)
+dequant_kernel(const uint8_t *__restrict__ w, int64_t n, int64_t k, int64_t rb, const int32_t *__restrict__ ids,
+               int64_t vocab, O *__restrict__ out)
+{
+    using F = Fmt<T>;
+    const int64_t per_row = k >> 3;
+    const int64_t total = n * per_row;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total; g += stride) {
+        const int64_t row = g / per_row;
+        const int e0 = (int)(g - row * per_row) * 8;  // first element (row-relative)
+        float v[8];
+        int64_t src = row;
+        bool valid = true;
+        if constexpr (GATHER) {
+            src = ids[row];
+            valid = src >= 0 && src < vocab;
+        }
+        if (valid) {
+            const uint8_t *blk = w + src * rb + (int64_t)(e0 / F::BE) * F::BB;
+            decode8<T>(blk, e0 % F::BE, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = 0.f;
+        }
+        store8(out + row * k + e0, v);
+    }
+}
+
+namespace {
+
+template <typename O, bool GATHER>
+hipError_t launch_any(int type, const void *w, int64_t n, int64_t k, size_t rb, const int32_t *ids,
+                      int64_t vocab, O *out, hipStream_t s)
 {
     const int64_t threads = n * (k >> 3);
-    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+    const int64_t blocks = (threads + 255) / 256;
+    // at most 2^20 workgroups (2^28 work-items); larger problems stride
+    const dim3 grid((unsigned)(blocks < (1 << 20) ? blocks : (1 << 20))), block(256);
     const uint8_t *wb = (const uint8_t *)w;
+    const int64_t r = (int64_t)rb;
     switch (type) {
-    case T_Q4_0: hipLaunchKernelGGL(dequant_kernel<T_Q4_0>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
-    case T_Q8_0: hipLaunchKernelGGL(dequant_kernel<T_Q8_0>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
-    case T_Q4_K: hipLaunchKernelGGL(dequant_kernel<T_Q4_K>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
-    case T_Q6_K: hipLaunchKernelGGL(dequant_kernel<T_Q6_K>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
-    case T_Q5_0: hipLaunchKernelGGL(dequant_kernel<T_Q5_0>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
-    case T_Q5_K: hipLaunchKernelGGL(dequant_kernel<T_Q5_K>, grid, block, 0, s, wb, n, k, (int64_t)rb, out); break;
+    case T_Q4_0: hipLaunchKernelGGL((dequant_kernel<T_Q4_0, O, GATHER>), grid, block, 0, s, wb, n, k, r, ids, vocab, out); break;
+    case T_Q8_0: hipLaunchKernelGGL((dequant_kernel<T_Q8_0, O, GATHER>), grid, block, 0, s, wb, n, k, r, ids, vocab, out); break;
+    case T_Q4_K: hipLaunchKernelGGL((dequant_kernel<T_Q4_K, O, GATHER>), grid, block, 0, s, wb, n, k, r, ids, vocab, out); break;
+    case T_Q6_K: hipLaunchKernelGGL((dequant_kernel<T_Q6_K, O, GATHER>), grid, block, 0, s, wb, n, k, r, ids, vocab, out); break;
+    case T_Q5_0: hipLaunchKernelGGL((dequant_kernel<T_Q5_0, O, GATHER>), grid, block, 0, s, wb, n, k, r, ids, vocab, out); break;
+    case T_Q5_K: hipLaunchKernelGGL((dequant_kernel<T_Q5_K, O, GATHER>), grid, block, 0, s, wb, n, k, r, ids, vocab, out); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dequant(int type, const void *w, int64_t n, int64_t k, size_t rb, float *out, hipStream_t s)
+{
+    return launch_any<float, false>(type, w, n, k, rb, nullptr, n, out, s);
+}
+
+hipError_t launch_dequant_f16(int type, const void *w, int64_t n, int64_t k, size_t rb, uint16_t *out,
+                              hipStream_t s)
+{
+    return launch_any<uint16_t, false>(type, w, n, k, rb, nullptr, n, out, s);
+}
+
+hipError_t launch_embed(int type, const void *table, int64_t vocab, int64_t k, size_t rb, const int32_t *ids,
+                        int64_t seq, float *out, hipStream_t s)
+{
+    return launch_any<float, true>(type, table, seq, k, rb, ids, vocab, out, s);
+}
+
+hipError_t launch_embed_f16(int type, const void *table, int64_t vocab, int64_t k, size_t rb,
+                            const int32_t *ids, int64_t seq, uint16_t *out, hipStream_t s)
+{
+    return launch_any<uint16_t, true>(type, table, seq, k, rb, ids, vocab, out, s);
 }
 
 }  // namespace qmm

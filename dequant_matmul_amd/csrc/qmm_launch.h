@@ -1,7 +1,7 @@
 // qmm_launch.h -- internal launchers of libqmm (host side).  Arguments are
 // already validated by the C-ABI layer (qmm_api.cpp): known type, k a
-// multiple of the block size, n, k, m/batch > 0, pointers non-null and
-// 16-byte aligned.  Each launcher only enqueues on stream s and returns the
+// multiple of the block size, n, k, m/batch/seq > 0, pointers non-null and
+// 16-byte aligned (token ids: 4-byte aligned).  Each launcher only enqueues on stream s and returns the
 // HIP status of the launch.
 #pragma once
 
@@ -13,6 +13,16 @@ namespace qmm {
 
 hipError_t launch_dequant(int type, const void *w, int64_t n, int64_t k, size_t rb, float *out,
                           hipStream_t s);
+
+hipError_t launch_dequant_f16(int type, const void *w, int64_t n, int64_t k, size_t rb, uint16_t *out,
+                              hipStream_t s);
+
+// Embedding gather: out row r = dequant of table row ids[r] (zeros for an id
+// outside [0, vocab)), r < seq.
+hipError_t launch_embed(int type, const void *table, int64_t vocab, int64_t k, size_t rb, const int32_t *ids,
+                        int64_t seq, float *out, hipStream_t s);
+hipError_t launch_embed_f16(int type, const void *table, int64_t vocab, int64_t k, size_t rb,
+                            const int32_t *ids, int64_t seq, uint16_t *out, hipStream_t s);
 
 hipError_t launch_gemv(int type, const void *w, int64_t n, int64_t k, size_t rb, const float *x,
                        int batch, float *y, hipStream_t s);

@@ -113,6 +113,36 @@ QMM_API size_t qmm_row_bytes(int type, int64_t k);
 QMM_API int qmm_dequant(int type, const void *w, int64_t n, int64_t k, float *out, void *stream);
 
 /*
+ * Dequantize to FP16: out[n][k] holds IEEE fp16 bit patterns, each the fp32
+ * value of qmm_dequant rounded to nearest-even (magnitudes of 65520 and
+ * above become +-Inf).  (dotLLM "GPU Inference", Custom Kernels table: the
+ * dequant_*_f16 kernels write the FP16 scratch of the prefill GEMM.)
+ */
+QMM_API int qmm_dequant_f16(int type, const void *w, int64_t n, int64_t k, uint16_t *out, void *stream);
+
+/*
+ * Embedding gather: out[r][:] = the weights of row ids[r] of the quantized
+ * table [vocab][k], for r < seq, each value as in qmm_dequant (fp32, exact).
+ * An id outside [0, vocab) gives a row of +0 (the pages do not say what an
+ * invalid id does; this library neither reads out of the table nor fails,
+ * since the ids are device data).  table: vocab rows of qmm_row_bytes(type,
+ * k) bytes; ids: int32 [seq], device memory, 4-byte aligned (the one pointer
+ * exempt from 16-byte alignment); out: fp32 [seq][k].  vocab == 0 is allowed
+ * (every row is zero, table may be NULL); seq == 0 or k == 0 is a no-op.
+ * (dotLLM "GPU Inference", Forward Pass step 2 and Weight Loading Pipeline:
+ * the token embeddings stay in their quantized format on the GPU and the
+ * lookup kernel dequantizes the rows of the token ids into the hidden state;
+ * Custom Kernels table: embedding_lookup_* with one workgroup row per token.)
+ */
+QMM_API int qmm_embed(int type, const void *table, int64_t vocab, int64_t k, const int32_t *ids, int64_t seq,
+                      float *out, void *stream);
+
+/* As qmm_embed with an FP16 output (fp16 bit patterns [seq][k], each the
+ * fp32 value rounded to nearest-even): dotLLM's hidden state is FP16. */
+QMM_API int qmm_embed_f16(int type, const void *table, int64_t vocab, int64_t k, const int32_t *ids,
+                          int64_t seq, uint16_t *out, void *stream);
+
+/*
  * Decode GEMV: y[b][j] = sum_i w[j][i] * x[b][i] for b < batch, j < n.
  * x: fp32 [batch][k], y: fp32 [batch][n], 1 <= batch <= 8 (batch 0 = empty).
  * Weights are read once from the quantized bytes and decoded in registers.

@@ -31,8 +31,9 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    assert {"qmm_dequant", "qmm_gemv", "qmm_gemv_multi", "qmm_gemm_prefill", "qmm_row_bytes",
-            "qmm_block_elems", "qmm_block_bytes", "qmm_status_str", "qmm_version"} == set(syms)
+    assert {"qmm_dequant", "qmm_dequant_f16", "qmm_embed", "qmm_embed_f16", "qmm_gemv", "qmm_gemv_multi",
+            "qmm_gemm_prefill", "qmm_row_bytes", "qmm_block_elems", "qmm_block_bytes", "qmm_status_str",
+            "qmm_version"} == set(syms)
 
 
 def test_library_exports_every_declared_symbol():
@@ -107,6 +108,32 @@ def test_validation_errors_dequant_and_gemm():
     assert L.qmm_gemm_prefill(q.Q4_0, A, 4, 32, A + 8, 8, A, None) == q.ERR_ALIGN
     assert L.qmm_gemm_prefill(q.Q4_0, A, 4, 32, A, 0, None, None) == q.OK
     assert L.qmm_gemm_prefill(q.Q4_0, None, 0, 32, None, 8, None, None) == q.OK
+
+
+def test_validation_errors_dequant_f16_and_embed():
+    q = _lib()
+    L = q.lib
+    assert L.qmm_dequant_f16(6, A, 4, 32, A, None) == q.ERR_TYPE
+    assert L.qmm_dequant_f16(q.Q4_K, A, 4, 32, A, None) == q.ERR_SHAPE
+    assert L.qmm_dequant_f16(q.Q4_K, None, 4, 256, A, None) == q.ERR_NULL
+    assert L.qmm_dequant_f16(q.Q4_K, A, 4, 256, None, None) == q.ERR_NULL
+    assert L.qmm_dequant_f16(q.Q4_K, A, 4, 256, A + 8, None) == q.ERR_ALIGN
+    assert L.qmm_dequant_f16(q.Q4_K, None, 0, 256, None, None) == q.OK
+    for f in (L.qmm_embed, L.qmm_embed_f16):
+        assert f(7, A, 100, 32, A, 4, A, None) == q.ERR_TYPE
+        assert f(q.Q8_0, A, 100, 40, A, 4, A, None) == q.ERR_SHAPE
+        assert f(q.Q8_0, A, -1, 32, A, 4, A, None) == q.ERR_SHAPE        # negative vocab
+        assert f(q.Q8_0, A, 100, 32, A, -4, A, None) == q.ERR_SHAPE      # negative seq
+        assert f(q.Q8_0, A, 100, 32, A, 1 << 31, A, None) == q.ERR_SHAPE
+        assert f(q.Q8_0, None, 100, 32, A, 4, A, None) == q.ERR_NULL
+        assert f(q.Q8_0, A, 100, 32, None, 4, A, None) == q.ERR_NULL
+        assert f(q.Q8_0, A, 100, 32, A, 4, None, None) == q.ERR_NULL
+        assert f(q.Q8_0, MIS, 100, 32, A, 4, A, None) == q.ERR_ALIGN     # table
+        assert f(q.Q8_0, A, 100, 32, A + 2, 4, A, None) == q.ERR_ALIGN   # ids need 4-byte alignment
+        assert f(q.Q8_0, A, 100, 32, A, 4, MIS, None) == q.ERR_ALIGN
+        # empty problems succeed without touching the device
+        assert f(q.Q8_0, A, 100, 32, None, 0, None, None) == q.OK
+        assert f(q.Q8_0, A, 100, 0, A, 4, None, None) == q.OK
 
 
 def test_validation_errors_gemv_multi():
