@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_float_to_half_array.argtypes = [P, I64, P]
         L.oracle_float_to_half_array.restype = None
         L.oracle_embed.argtypes = [ctypes.c_int, P, I64, I64, P, I64, P]
+        L.oracle_quantize.argtypes = [ctypes.c_int, P, I64, I64, P]
+        L.oracle_quantize_f16.argtypes = [ctypes.c_int, P, I64, I64, P]
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_set_threads.restype = None
         L.oracle_max_threads.argtypes = []
@@ -159,6 +161,24 @@ def embed(t: int, table: np.ndarray, vocab: int, k: int, ids, f16: bool = False)
     out = np.empty((ids.size, k), dtype=np.float32)
     _check(lib().oracle_embed(t, _ptr(table), vocab, k, _ptr(ids), ids.size, _ptr(out)), "embed")
     return to_half_bits(out) if f16 else out
+
+
+def quantize(t: int, x: np.ndarray) -> np.ndarray:
+    """Q8_0 / Q4_0 encoder: x float32 or float16 [n, k] (k a multiple of 32)
+    -> block bytes uint8 [n, row_bytes]."""
+    x = np.ascontiguousarray(x)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    n, k = x.shape
+    out = np.empty((n, row_bytes(t, k) if row_bytes(t, k) else 0), dtype=np.uint8)
+    if x.dtype == np.float16:
+        xb = np.ascontiguousarray(x.view(np.uint16))
+        rc = lib().oracle_quantize_f16(t, _ptr(xb), n, k, _ptr(out))
+    else:
+        xf = np.ascontiguousarray(x, dtype=np.float32)
+        rc = lib().oracle_quantize(t, _ptr(xf), n, k, _ptr(out))
+    _check(rc, "quantize")
+    return out
 
 
 def gemv(t: int, w: np.ndarray, n: int, k: int, x: np.ndarray):

@@ -20,6 +20,8 @@
  *               range);
  *   - fp16:     any fp32 result rounded to binary16, nearest-even (the FP16
  *               outputs of the dequant and the embedding gather).
+ *   - quantize: fp32 (or fp16) values -> Q8_0 / Q4_0 blocks by the GGUF
+ *               rule, in fp32 (the KV-cache encoder).
  *
  * Sources (page / section):
  *   - shimmy "Airframe GPU pipeline", per-layer ops: dequantization happens
@@ -355,6 +357,93 @@ int oracle_embed(int t, const uint8_t *table, int64_t vocab, int64_t k,
             dequant_row(t, table + (size_t)id * rb, k, dst);
         else
             memset(dst, 0, (size_t)k * sizeof(float));
+    }
+    return 0;
+}
+
+/*
+ * Quantize (the KV-cache encoder): each block of 32 fp32 values -> one Q8_0 or
+ * Q4_0 block, by the GGUF rule for these types, every step in fp32 (the
+ * precision in which the codes are decided):
+ *   Q8_0: amax = max |x_i|; d = amax / 127; id = 1 / d (0 when d == 0);
+ *         q_i = x_i * id rounded half away from zero; stored d = fp16(d).
+ *   Q4_0: v = the x_i of largest magnitude (the first one on a tie);
+ *         d = v / -8; id = 1 / d (0 when d == 0);
+ *         q_i = min(15, trunc(x_i * id + 8.5)); stored d = fp16(d).
+ * Codes are computed with the fp32 d, before d is rounded to fp16.
+ * (dotLLM "GPU Inference", Implementation: a GPU KV-cache quantized to Q8_0
+ * or Q4_0 with an FP16 window; the pages do not state the rounding rule.)
+ * x: fp32 [n][k], k a multiple of 32; out: n rows of row-bytes.
+ */
+static void quantize_block(int t, const float *x, uint8_t *blk)
+{
+    if (t == OR_Q8_0) {
+        float amax = 0.0f;
+        for (int i = 0; i < 32; i++)
+            if (fabsf(x[i]) > amax)
+                amax = fabsf(x[i]);
+        float d = amax / 127.0f;
+        float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        uint16_t h = oracle_double_to_half((double)d);
+        blk[0] = (uint8_t)(h & 0xff);
+        blk[1] = (uint8_t)(h >> 8);
+        for (int i = 0; i < 32; i++) {
+            float v = x[i] * id;
+            blk[2 + i] = (uint8_t)(int8_t)(int)roundf(v);
+        }
+    } else { /* Q4_0 */
+        float amax = 0.0f, vmax = 0.0f;
+        for (int i = 0; i < 32; i++)
+            if (fabsf(x[i]) > amax) {
+                amax = fabsf(x[i]);
+                vmax = x[i];
+            }
+        float d = vmax / -8.0f;
+        float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        uint16_t h = oracle_double_to_half((double)d);
+        blk[0] = (uint8_t)(h & 0xff);
+        blk[1] = (uint8_t)(h >> 8);
+        int q[32];
+        for (int i = 0; i < 32; i++) {
+            float v = x[i] * id;
+            float u = v + 8.5f;
+            int c = (int)truncf(u);
+            q[i] = c < 15 ? c : 15;
+        }
+        for (int i = 0; i < 16; i++)
+            blk[2 + i] = (uint8_t)(q[i] | (q[i + 16] << 4));
+    }
+}
+
+int oracle_quantize(int t, const float *x, int64_t n, int64_t k, uint8_t *out)
+{
+    if (t != OR_Q8_0 && t != OR_Q4_0)
+        return -1;
+    int rc = check(t, n, k);
+    if (rc)
+        return rc;
+    int bb = oracle_block_bytes(t);
+    int64_t nblk = n * (k / 32);
+    for (int64_t b = 0; b < nblk; b++)
+        quantize_block(t, x + b * 32, out + b * bb);
+    return 0;
+}
+
+/* The same with fp16 input (IEEE bits), converted exactly to fp32 first. */
+int oracle_quantize_f16(int t, const uint16_t *x, int64_t n, int64_t k, uint8_t *out)
+{
+    if (t != OR_Q8_0 && t != OR_Q4_0)
+        return -1;
+    int rc = check(t, n, k);
+    if (rc)
+        return rc;
+    int bb = oracle_block_bytes(t);
+    int64_t nblk = n * (k / 32);
+    for (int64_t b = 0; b < nblk; b++) {
+        float xf[32];
+        for (int i = 0; i < 32; i++)
+            xf[i] = oracle_half_to_float(x[b * 32 + i]);
+        quantize_block(t, xf, out + b * bb);
     }
     return 0;
 }

@@ -28,6 +28,7 @@ Distributions (the workload definitions that go with the pages):
         dmin) as for Q4_0 / Q4_K, every other byte uniform (q ~ U{0..31})
   activations: fp32 (decode) or fp16 (prefill) ~ N(0, 1)
   token ids: int32 ~ U{0..vocab-1}
+  KV-cache values to encode: fp16 ~ N(0, 1) (the pages give no distribution)
 
 Seeds: matrix i of workload c uses seed 1000*c + i; its activation uses
 1000*c + 500 + i.
@@ -197,6 +198,11 @@ def workload(cfg: int):
         # 1B table in Q8_0 (the type the pages' embedding kernel reads) and
         # the Llama-3-8B table in Q4_K; ids ~ U{0..vocab-1}, 1 or 512 tokens
         mats = [("embd_q8_0", Q8_0, 128256, 2048), ("embd_q4_k", Q4_K, 128256, 4096)]
+    elif cfg == 10:
+        # KV-cache codec: one layer's K (or V) rows of Llama-3-8B (8 KV heads
+        # x 128 = 1024 values per token) over an 8192-token context, encoded
+        # to Q8_0 or Q4_0; the values are fp16 ~ N(0, 1) (gen_x_f16)
+        mats = [("kv_q8_0", Q8_0, 8192, 1024), ("kv_q4_0", Q4_0, 8192, 1024)]
     else:
         raise ValueError("unknown workload %r" % (cfg,))
     return [(nm, t, n, k, 1000 * cfg + i) for i, (nm, t, n, k) in enumerate(mats)]

@@ -11,7 +11,8 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_dot.py", "tests/test_oracle_embed.py"]
+PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_dot.py", "tests/test_oracle_embed.py",
+             "tests/test_oracle_quant.py"]
 
 MUTANTS = {
     "q4_0 offset": ("return d * (double)(q - 8);", "return d * (double)(q - 7);"),
@@ -45,6 +46,14 @@ MUTANTS = {
     "fp16 overflow threshold": ("if (bits >= 0x7c00)", "if (bits >= 0x7bff)"),
     "embed invalid id reads row 0": ("memset(dst, 0, (size_t)k * sizeof(float));", "dequant_row(t, table, k, dst);"),
     "embed id order": ("int64_t id = ids[i];", "int64_t id = ids[seq - 1 - i];"),
+    "q8_0 encode ties to even": ("blk[2 + i] = (uint8_t)(int8_t)(int)roundf(v);",
+                                 "blk[2 + i] = (uint8_t)(int8_t)(int)rintf(v);"),
+    "q8_0 encode scale 1/128": ("float d = amax / 127.0f;", "float d = amax / 128.0f;"),
+    "q4_0 encode offset 8": ("float u = v + 8.5f;", "float u = v + 8.0f;"),
+    "q4_0 encode last max wins": ("if (fabsf(x[i]) > amax) {", "if (fabsf(x[i]) >= amax) {"),
+    "q4_0 encode no clamp": ("q[i] = c < 15 ? c : 15;", "q[i] = c;"),
+    "q4_0 encode nibble pairing": ("blk[2 + i] = (uint8_t)(q[i] | (q[i + 16] << 4));",
+                                   "blk[2 + i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));"),
     "gemm row index": ("double p = oracle_half_to_double(x[mm * k + i]) * (double)wrow[i];",
                        "double p = oracle_half_to_double(x[ii * k + i]) * (double)wrow[i];"),
 }
