@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized-weight matmul on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix|q5|embed]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix|q5|embed|kv]
 
 A step is one decode pass over the TinyLlama-shaped Q4_0 weight stream:
 22 layers x (q, k, v, o, gate, up, down) = 154 GEMVs at batch 1 on one
@@ -16,8 +16,9 @@ dominant kernel (the Q4_0 GEMV) from per-launch HIP-event timings, the CPU
 oracle timed on a bounded sample of the same workload, and secondary figures
 for the other workloads (Q8_0 single matrix, Llama-3-8B Q4_K set, 512-token
 prefill GEMMs, Q4_K_M-style mix with a Q6_K LM head at batch 1/4/8, the
-same shapes in the 5-bit types Q5_K / Q5_0, and the quantized embedding
-gather for one decode token and a 512-token chunk).
+same shapes in the 5-bit types Q5_K / Q5_0, the quantized embedding
+gather for one decode token and a 512-token chunk, and the Q8_0 / Q4_0
+KV-cache codec: encoding and decoding K rows of one Llama-3-8B layer).
 """
 from __future__ import annotations
 
@@ -54,7 +55,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix", "q5", "embed"], default="all",
+    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix", "q5", "embed", "kv"], default="all",
                    help="which secondary workloads to run after the primary line's (all by default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU oracle sample")
@@ -110,6 +111,25 @@ class Embed:
                self.out.data_ptr(), stream)
         if st != 0:
             raise RuntimeError("embed %s: %s" % (self.name, q.status_str(st)))
+
+
+class Codec:
+    """One KV-cache codec call: encode (qmm_quantize_f16, fp16 -> blocks) or
+    decode (qmm_dequant_f16, blocks -> fp16)."""
+
+    def __init__(self, name, t, n, k, x, blocks, back, encode):
+        self.name, self.t, self.n, self.k = name, t, n, k
+        self.x, self.blocks, self.back, self.encode = x, blocks, back, encode
+        # algorithmic bytes: fp16 values on one side, the blocks on the other
+        self.bytes = 2 * n * k + n * G.row_bytes(t, k)
+
+    def launch(self, q, stream):
+        if self.encode:
+            st = q.lib.qmm_quantize_f16(self.t, self.x.data_ptr(), self.n, self.k, self.blocks.data_ptr(), stream)
+        else:
+            st = q.lib.qmm_dequant_f16(self.t, self.blocks.data_ptr(), self.n, self.k, self.back.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError("codec %s: %s" % (self.name, q.status_str(st)))
 
 
 class Group:
@@ -333,6 +353,35 @@ def sec_embed(torch, q, steps, warmup, dev, rotate=32):
     return res
 
 
+def sec_kv(torch, q, steps, warmup, dev):
+    """KV-cache codec on the K rows of one Llama-3-8B layer (1024 fp16 values
+    per token): encode / decode one new token, a 512-token chunk and an
+    8192-token context; the large cases rotate over enough buffers
+    (> 256 MB) that the last-level cache cannot hold them."""
+    res = {}
+    for name, t, n_ctx, k, seed in G.workload(10):
+        for n in (1, 512, n_ctx):
+            rotate = 16 if n == n_ctx else 32
+            probs_e, probs_d = [], []
+            for r in range(rotate):
+                x = torch.from_numpy(G.gen_x_f16(n, k, seed + 17 * r)).to(dev)
+                blocks = torch.empty((n, G.row_bytes(t, k)), dtype=torch.uint8, device=dev)
+                back = torch.empty((n, k), dtype=torch.float16, device=dev)
+                probs_e.append(Codec(name, t, n, k, x, blocks, back, True))
+                probs_d.append(Codec(name, t, n, k, x, blocks, back, False))
+            for kind, probs in (("encode", probs_e), ("decode", probs_d)):
+                g = capture(torch, q, probs)
+                tg = time_graph(torch, g, steps, warmup) / rotate
+                b = probs[0].bytes
+                res["%s_%s_%d" % (name, kind, n)] = {
+                    "rows": "%d x %d" % (n, k), "us_per_call": round(tg * 1e6, 3), "GB_s": round(b / tg / 1e9, 1),
+                    "pct_hbm_peak": round(100 * b / tg / 1e9 / HBM_PEAK_GBS, 2)}
+                del g
+            del probs_e, probs_d
+            torch.cuda.empty_cache()
+    return res
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -474,6 +523,9 @@ def main():
         if want("embed"):
             log("secondary: embedding gathers")
             sec["embed"] = sec_embed(torch, q, args.steps, args.warmup, dev)
+        if want("kv"):
+            log("secondary: KV-cache codec")
+            sec["kv_codec"] = sec_kv(torch, q, args.steps, args.warmup, dev)
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 

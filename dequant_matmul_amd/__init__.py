@@ -11,6 +11,7 @@ CPU fallback: if the library is missing, importing this package fails.
     Y = qmm.gemm_prefill(w_bytes, qmm.Q4_K, n, k, X)  # X fp16 [m, k] -> Y fp32 [m, n]
     W = qmm.dequant(w_bytes, qmm.Q4_K, n, k)          # -> fp32 [n, k]
     H = qmm.embed(table, qmm.Q8_0, vocab, k, ids)      # ids int32 [seq] -> fp32 [seq, k]
+    B = qmm.quantize(kv_f16, qmm.Q8_0)                 # fp16 [n, k] -> Q8_0 blocks
 
 Block types and layouts follow shimmy "Architecture" (Quantization table) and
 dotLLM "GPU Inference" (Quantization on GPU table); see include/qmm.h.
@@ -37,6 +38,8 @@ SIGNATURES = {
     "qmm_dequant_f16": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "qmm_embed": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
     "qmm_embed_f16": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "qmm_quantize": (_I, [_I, _P, _I64, _I64, _P, _P]),
+    "qmm_quantize_f16": (_I, [_I, _P, _I64, _I64, _P, _P]),
     "qmm_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
     "qmm_gemv_multi": (_I, [_I, _I, _P, _P, _I64, _P, _I64, _P, _P]),
     "qmm_gemm_prefill": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
@@ -153,6 +156,28 @@ def embed(table, qtype: int, vocab: int, k: int, ids, dtype=None, out=None):
         raise ValueError("dtype must be torch.float32 or torch.float16")
     _call(f(qtype, table.data_ptr(), vocab, k, ids.data_ptr(), seq, out.data_ptr(), _stream_ptr(table.device)),
           "qmm_embed")
+    return out
+
+
+def quantize(x, qtype: int, out=None):
+    """Encode x (fp32 or fp16 device tensor [n, k], k a multiple of 32) into
+    Q8_0 / Q4_0 blocks: uint8 [n, row_bytes]."""
+    torch = _torch()
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous 2-D device tensor")
+    n, k = x.shape
+    rb = row_bytes(qtype, k)
+    if out is None:
+        out = torch.empty((n, rb), dtype=torch.uint8, device=x.device)
+    if x.dtype == torch.float32:
+        f = lib.qmm_quantize
+    elif x.dtype == torch.float16:
+        f = lib.qmm_quantize_f16
+    else:
+        raise ValueError("x must be float32 or float16")
+    _call(f(qtype, x.data_ptr(), n, k, out.data_ptr(), _stream_ptr(x.device)), "qmm_quantize")
     return out
 
 

@@ -140,6 +140,42 @@ int qmm_embed_f16(int type, const void *table, int64_t vocab, int64_t k, const i
     return hip_status(qmm::launch_embed_f16(type, table, vocab, k, rb, ids, seq, out, (hipStream_t)stream));
 }
 
+// Shared checks of the two encoders (the output is checked like a weight
+// matrix of n rows).
+static int check_quantize(int type, const void *x, int64_t n, int64_t k, void *out, size_t *rb)
+{
+    if (type != QMM_Q8_0 && type != QMM_Q4_0)
+        return QMM_ERR_TYPE;
+    int st = check_common(type, out, n, k, rb);
+    if (st != QMM_OK)
+        return st;
+    if (n == 0 || k == 0)
+        return QMM_OK;
+    if (x == nullptr)
+        return QMM_ERR_NULL;
+    if (!aligned16(x))
+        return QMM_ERR_ALIGN;
+    return QMM_OK;
+}
+
+int qmm_quantize(int type, const float *x, int64_t n, int64_t k, void *out, void *stream)
+{
+    size_t rb = 0;
+    int st = check_quantize(type, x, n, k, out, &rb);
+    if (st != QMM_OK || n == 0 || k == 0)
+        return st;
+    return hip_status(qmm::launch_quantize(type, x, n, k, out, (hipStream_t)stream));
+}
+
+int qmm_quantize_f16(int type, const uint16_t *x, int64_t n, int64_t k, void *out, void *stream)
+{
+    size_t rb = 0;
+    int st = check_quantize(type, x, n, k, out, &rb);
+    if (st != QMM_OK || n == 0 || k == 0)
+        return st;
+    return hip_status(qmm::launch_quantize_f16(type, x, n, k, out, (hipStream_t)stream));
+}
+
 int qmm_gemv(int type, const void *w, int64_t n, int64_t k, const float *x, int64_t batch, float *y,
              void *stream)
 {

@@ -24,6 +24,10 @@ hipError_t launch_embed(int type, const void *table, int64_t vocab, int64_t k, s
 hipError_t launch_embed_f16(int type, const void *table, int64_t vocab, int64_t k, size_t rb,
                             const int32_t *ids, int64_t seq, uint16_t *out, hipStream_t s);
 
+// Encoder (Q8_0 / Q4_0 only): x [n][k] -> n rows of row-bytes.
+hipError_t launch_quantize(int type, const float *x, int64_t n, int64_t k, void *out, hipStream_t s);
+hipError_t launch_quantize_f16(int type, const uint16_t *x, int64_t n, int64_t k, void *out, hipStream_t s);
+
 hipError_t launch_gemv(int type, const void *w, int64_t n, int64_t k, size_t rb, const float *x,
                        int batch, float *y, hipStream_t s);
 

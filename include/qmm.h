@@ -143,6 +143,30 @@ QMM_API int qmm_embed_f16(int type, const void *table, int64_t vocab, int64_t k,
                           int64_t seq, uint16_t *out, void *stream);
 
 /*
+ * Quantize (the encoder of a quantized KV cache): x [n][k] (fp32, k a
+ * multiple of 32) -> out, n rows of qmm_row_bytes(type, k) bytes of Q8_0 or
+ * Q4_0 blocks (other types: QMM_ERR_TYPE).  Each block of 32 values follows
+ * the GGUF rule, every step in fp32:
+ *   Q8_0  d = amax / 127, codes = x / d rounded half away from zero
+ *         (computed as x * (1 / d)); 0 codes and d = 0 for a zero block;
+ *   Q4_0  v = the value of largest magnitude (the first on a tie),
+ *         d = v / -8, codes = min(15, trunc(x * (1 / d) + 8.5)); a zero
+ *         block gets d = -0 and codes 8;
+ * the codes use the fp32 d, which is stored rounded to fp16 (nearest-even).
+ * The divisions are correctly rounded and nothing is fused, so the bytes
+ * are those of any exact fp32 evaluation.  x must be finite (otherwise the
+ * block's bytes are unspecified).  Decoding back: qmm_dequant_f16 /
+ * qmm_dequant.  (dotLLM "GPU Inference", Implementation: a GPU KV-cache
+ * quantized to Q8_0 / Q4_0 with an FP16 window of recent tokens; the pages
+ * state no rounding rule.)
+ */
+QMM_API int qmm_quantize(int type, const float *x, int64_t n, int64_t k, void *out, void *stream);
+
+/* As qmm_quantize with fp16 input (IEEE bit patterns [n][k], converted
+ * exactly): the KV cache holds FP16 keys and values. */
+QMM_API int qmm_quantize_f16(int type, const uint16_t *x, int64_t n, int64_t k, void *out, void *stream);
+
+/*
  * Decode GEMV: y[b][j] = sum_i w[j][i] * x[b][i] for b < batch, j < n.
  * x: fp32 [batch][k], y: fp32 [batch][n], 1 <= batch <= 8 (batch 0 = empty).
  * Weights are read once from the quantized bytes and decoded in registers.

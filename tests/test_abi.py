@@ -31,9 +31,9 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     syms = declared_symbols()
-    assert {"qmm_dequant", "qmm_dequant_f16", "qmm_embed", "qmm_embed_f16", "qmm_gemv", "qmm_gemv_multi",
-            "qmm_gemm_prefill", "qmm_row_bytes", "qmm_block_elems", "qmm_block_bytes", "qmm_status_str",
-            "qmm_version"} == set(syms)
+    assert {"qmm_dequant", "qmm_dequant_f16", "qmm_embed", "qmm_embed_f16", "qmm_quantize", "qmm_quantize_f16",
+            "qmm_gemv", "qmm_gemv_multi", "qmm_gemm_prefill", "qmm_row_bytes", "qmm_block_elems",
+            "qmm_block_bytes", "qmm_status_str", "qmm_version"} == set(syms)
 
 
 def test_library_exports_every_declared_symbol():
@@ -134,6 +134,22 @@ def test_validation_errors_dequant_f16_and_embed():
         # empty problems succeed without touching the device
         assert f(q.Q8_0, A, 100, 32, None, 0, None, None) == q.OK
         assert f(q.Q8_0, A, 100, 0, A, 4, None, None) == q.OK
+
+
+def test_validation_errors_quantize():
+    q = _lib()
+    L = q.lib
+    for f in (L.qmm_quantize, L.qmm_quantize_f16):
+        for t in (q.Q4_K, q.Q6_K, q.Q5_0, q.Q5_K, 6, -1):      # the encoder covers Q8_0 and Q4_0 only
+            assert f(t, A, 4, 256, A, None) == q.ERR_TYPE
+        assert f(q.Q8_0, A, 4, 48, A, None) == q.ERR_SHAPE
+        assert f(q.Q4_0, A, -4, 32, A, None) == q.ERR_SHAPE
+        assert f(q.Q4_0, A, 4, 32, None, None) == q.ERR_NULL
+        assert f(q.Q4_0, None, 4, 32, A, None) == q.ERR_NULL
+        assert f(q.Q4_0, MIS, 4, 32, A, None) == q.ERR_ALIGN
+        assert f(q.Q4_0, A, 4, 32, A + 2, None) == q.ERR_ALIGN
+        assert f(q.Q8_0, None, 0, 32, None, None) == q.OK
+        assert f(q.Q8_0, None, 4, 0, None, None) == q.OK
 
 
 def test_validation_errors_gemv_multi():
