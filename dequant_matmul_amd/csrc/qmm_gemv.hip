@@ -39,7 +39,9 @@
 //   gemv2m_kernel gemv2 over a table of up to 8 problems sharing k (the
 //                 grouped entry point): one launch instead of one per matrix.
 //   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
-//                 once per workgroup; otherwise as gemv2.
+//                 once per workgroup; otherwise as gemv2 (two rows per item,
+//                 one when there are too few rows to give every CU a
+//                 workgroup).
 //   gemv_kernel   batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K (and unaligned
 //                 batch-1 rows): x
 //                 segment and weight segments staged in LDS per workgroup.
@@ -916,9 +918,10 @@ gemv2m_kernel(const GemvProbs Pt, int k, int64_t rb)
 
 // --------------------------------------------------------------- gemv1 --
 // Batch 1, k spanning several segments: x staged in LDS once per workgroup;
-// each wave walks items (R rows x one segment) with the next item's weight
-// bytes in flight.
-template <int T, int R, int NW, int XK>
+// each wave walks items (R rows x one segment) with the weight bytes of the
+// next D items in flight (a ring of D register stages, so a row's segments
+// are fetched together rather than one round trip after another).
+template <int T, int R, int NW, int XK, int D>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 4)))
 gemv1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
              float *__restrict__ y)
@@ -940,15 +943,17 @@ gemv1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
     const int nitems = my_rg * nseg;
     uint32_t *mw = ws + wave * S::LDS_DW;
 
-    S st;
-    auto load = [&](int it) __attribute__((always_inline)) {
+    S st[D];
+    auto load = [&](S &dst, int it) __attribute__((always_inline)) {
         it = min(it, max(nitems - 1, 0));   // past the end: reload the last item
         const int rg = gw + tw * (it / nseg), seg = it % nseg;
         const int segE = min(SEGE, k - seg * SEGE);
-        st.load(w, rb, n, rg * R, seg, segE / F::BE * F::BB / 16, lane);
+        dst.load(w, rb, n, rg * R, seg, segE / F::BE * F::BB / 16, lane);
     };
 
-    load(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+        load(st[i], i);
     {   // stage x; positions >= k hold copies of x[0..3], which no active lane reads
         f32x4 xv[XV];
 #pragma unroll
@@ -967,22 +972,28 @@ gemv1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
     float acc[R][1];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r][0] = 0.f;
-    for (int it = 0; it < nitems; ++it) {
-        st.store(mw, lane);
-        wave_lds_sync();
-        load(it + 1);
-        const int rg = gw + tw * (it / nseg), seg = it % nseg;
-        const int segE = min(SEGE, k - seg * SEGE);
-        if (lane < segE / UE) {
-            URaw<T> cur[R];
+    for (int it0 = 0; it0 < nitems; it0 += D) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
-            const XFromLds<T, XS> xg{xs + xpad<UE>(seg * SEGE), lane};
-            unit_dot<T, 1, R>(cur, lane, xg, acc);
+        for (int i = 0; i < D; ++i) {
+            const int it = it0 + i;
+            st[i].store(mw, lane);
+            wave_lds_sync();
+            load(st[i], it + D);
+            if (it < nitems) {     // the ring runs in whole rounds; the surplus items are reloads
+                const int rg = gw + tw * (it / nseg), seg = it % nseg;
+                const int segE = min(SEGE, k - seg * SEGE);
+                if (lane < segE / UE) {
+                    URaw<T> cur[R];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
+                    const XFromLds<T, XS> xg{xs + xpad<UE>(seg * SEGE), lane};
+                    unit_dot<T, 1, R>(cur, lane, xg, acc);
+                }
+                if (seg == nseg - 1)
+                    reduce_store<R>(acc, rg * R, n, lane, y);
+            }
+            wave_lds_sync();
         }
-        if (seg == nseg - 1)
-            reduce_store<R>(acc, rg * R, n, lane, y);
-        wave_lds_sync();
     }
 }
 
@@ -1155,16 +1166,16 @@ static hipError_t launch_b1_table(const GemvProbs &P, int64_t k, size_t rb, hipS
     return hipGetLastError();
 }
 
-template <int T, int R, int NW, int XK>
+template <int T, int R, int NW, int XK, int D>
 static hipError_t launch_b1_lds(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                                 hipStream_t s)
 {
     static int cap = 0;
-    if (cap == 0 && (cap = resident_wgs(gemv1_kernel<T, R, NW, XK>, 64 * NW)) == 0)
+    if (cap == 0 && (cap = resident_wgs(gemv1_kernel<T, R, NW, XK, D>, 64 * NW)) == 0)
         return hipErrorInvalidValue;
     const int64_t want = ((n + R - 1) / R + NW - 1) / NW;
     const dim3 grid((unsigned)(want < cap ? want : cap)), block(64 * NW);
-    hipLaunchKernelGGL((gemv1_kernel<T, R, NW, XK>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
+    hipLaunchKernelGGL((gemv1_kernel<T, R, NW, XK, D>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
     return hipGetLastError();
 }
 
@@ -1193,8 +1204,21 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
             return n <= 1024 ? launch_b1_regs<T, 1>(w, n, k, rb, x, y, s)
                              : launch_b1_regs<T, 2>(w, n, k, rb, x, y, s);
         }
-        if (k <= 16384)
-            return launch_b1_lds<T, 2, 8, 16384>(w, n, k, rb, x, y, s);
+        if (k <= 16384) {
+            // two rows per item, unless that leaves compute units without a
+            // workgroup (e.g. 2048 rows: 128 workgroups of 8 waves); then one
+            // (measured on MI355X: 2048 x 5632 Q4_0 5.95 -> 5.23 us)
+            static int cus = 0;   // per-process cache (one device model)
+            if (cus == 0) {
+                int dev = 0;
+                if (hipGetDevice(&dev) != hipSuccess ||
+                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+                    return hipErrorInvalidValue;
+            }
+            if (((n + 1) / 2 + 7) / 8 < cus)
+                return launch_b1_lds<T, 1, 8, 16384, 1>(w, n, k, rb, x, y, s);
+            return launch_b1_lds<T, 2, 8, 16384, 1>(w, n, k, rb, x, y, s);
+        }
     }
     if (gemv_mfma_supported(T, batch))
         return launch_gemv_mfma(T, w, n, k, rb, x, batch, y, s);
