@@ -43,7 +43,7 @@ FP16_PEAK_TFLOPS = 2500.0
 # same counters read for a plain 256 MiB device copy (reads x2.0, writes
 # x1.0).  It describes the kernels it was measured on: set it to None when
 # they change, until the counters are taken again.
-TRAFFIC = 3374693   # bytes per launch, averaged over one pass (gemv2_kernel<0,2/1>, gemv1_kernel<0,...>)
+TRAFFIC = 3264571   # bytes per launch, averaged over one pass (gemv2_kernel<0,2/1>, gemv1_kernel<0,1,...>)
 
 
 def log(*a):
