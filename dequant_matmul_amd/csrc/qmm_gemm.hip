@@ -14,12 +14,12 @@
 //   VALU work co-issues with MFMA only up to ~3-4 wave instructions per MFMA
 //   before it becomes the limit, and LDS delivers ~128 B/clk per CU.  So:
 //   - Workgroup tile BM (m) x BN (n) = 256 x 128 with 8 wavefronts stacked
-//     along m, each owning 32 x 128 = 2 x 8 MFMA blocks (128 x 64 with 4
-//     waves of 32 x 64 when 256 x 128 tiles would leave half the CUs idle,
-//     128 x 128 for m <= 128).  Every wave loads
-//     only its own X rows (two waves loading the same X lines doubled the L2
-//     traffic and was 2.5x slower); all share the weight tile.  The decode of
-//     a weight element is shared by BM rows of X.
+//     along m, each owning 32 x 128 = 2 x 8 MFMA blocks (256 x 112 when that
+//     tile count fills the CUs better, 128 x 64 with 4 waves of 32 x 64 when
+//     256 x 128 tiles would leave half the CUs idle, 128 x 128 for
+//     m <= 128).  Every wave loads only its own X rows (two waves loading the
+//     same X lines doubled the L2 traffic and was 2.5x slower); all share the
+//     weight tile.  The decode of a weight element is shared by BM rows of X.
 //   - Only the weight tile goes through LDS: it is decoded once per workgroup
 //     into fp16 [n][k] (row stride padded by 8 halves, conflict-free 128-bit
 //     fragment reads), double buffered, K step 128.  The decode of tile t+1
@@ -374,8 +374,11 @@ struct GemmCfg {
     static constexpr int BM = MW * WM, BN = NW * WN;
     static constexpr int NT = 64 * WM * WN;
     static constexpr int UNITS = 4 * BN;              // decode units per K step
-    static constexpr int UPT = UNITS / NT;            // per thread
-    static_assert(UNITS % NT == 0 && UPT >= 1, "decode units must divide evenly");
+    static constexpr int UPT = (UNITS + NT - 1) / NT; // per thread
+    // units split evenly over the threads, or (e.g. 112-column tiles) the
+    // last wavefronts have none in the last slot
+    static constexpr bool EVEN = UNITS % NT == 0;
+    static_assert(EVEN || (UNITS % 64 == 0 && UNITS > NT * (UPT - 1)), "decode units per wavefront");
     static constexpr int LDS_HALVES = 2 * BN * GLD;
 };
 
@@ -434,13 +437,17 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
         uq[u] = id & 3;
         wrow[u] = w + (int64_t)min(n0 + ucol[u], n - 1) * rb;
     }
+    // slot u of this thread holds a unit (wave-uniform: units come in whole wavefronts)
+    auto has = [&](int u) __attribute__((always_inline)) {
+        return C::EVEN || u < C::UPT - 1 || __builtin_amdgcn_readfirstlane(tid) + C::NT * u < C::UNITS;
+    };
     WRaw<T> wr[2][C::UPT];
     // (full: step t lies wholly inside K, which always holds for 256-element
     // super-blocks since K is then a multiple of 256)
     auto load_w = [&](int par, int t, bool full) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < C::UPT; ++u)
-            if (full || Fmt<T>::BE == 256 || 4 * t + uq[u] < (k >> 5))
+            if (has(u) && (full || Fmt<T>::BE == 256 || 4 * t + uq[u] < (k >> 5)))
                 load_unit<T>(wrow[u], t, uq[u], wr[par][u]);
     };
     // decode of step t in four parts (part i between the MFMAs of sub-step i)
@@ -448,7 +455,7 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
     auto decode_w = [&](int par, int t, _Float16 *dst, bool full, int i) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < C::UPT; ++u)
-            if (full || Fmt<T>::BE == 256 || 4 * t + uq[u] < (k >> 5)) {
+            if (has(u) && (full || Fmt<T>::BE == 256 || 4 * t + uq[u] < (k >> 5))) {
                 if (i == 0)
                     dec[u].setup(wr[par][u], t, uq[u]);
                 dec[u].part(wr[par][u], i, dst + ucol[u] * GLD);
@@ -643,10 +650,21 @@ hipError_t launch_gemm_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, cons
     // 128 x 64 tiles (4 waves) before splitting K: on 512 x 4096 these give
     // 256 tiles and ran 25% faster than 64 tiles split 4 ways, whose fp32
     // atomics and zero fill cost more than the smaller tiles' extra decode.
+    // Of 128- and 112-column tiles, 112 when they keep clearly more CUs busy
+    // in the last round (512 x 14336: 224 tiles of 128 leave 32 of 256 CUs
+    // idle, 256 tiles of 112 none; measured 4-5% faster).
     if (m <= 128)
         return launch_cfg<T, 1, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);   // 128 x 128
-    if (2 * tile_count<256, 128>(m, n) > cu_count())
-        return launch_cfg<T, 2, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);   // 256 x 128
+    const int64_t cus = cu_count();
+    const int64_t t128 = tile_count<256, 128>(m, n);
+    if (2 * t128 > cus) {
+        const int64_t t112 = tile_count<256, 112>(m, n);
+        // busy fraction of the last round, compared as t / rounds (cross-multiplied)
+        const int64_t r128 = (t128 + cus - 1) / cus, r112 = (t112 + cus - 1) / cus;
+        if (100 * t112 * r128 > 105 * t128 * r112)
+            return launch_cfg<T, 2, 7, 8, 1, 4>(w, n, k, rb, x, m, y, s);   // 256 x 112
+        return launch_cfg<T, 2, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);       // 256 x 128
+    }
     return launch_cfg<T, 2, 4, 4, 1, 4>(w, n, k, rb, x, m, y, s);       // 128 x 64
 }
 

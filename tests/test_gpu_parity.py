@@ -296,7 +296,8 @@ def test_gemm_one_hot_subnormal_scales(t):
 
 
 @pytest.mark.parametrize("t,n", [(G.Q8_0, 14336), (G.Q8_0, 4096), (G.Q4_K, 14336), (G.Q4_K, 4096),
-                                 (G.Q4_0, 4096), (G.Q6_K, 4096), (G.Q5_0, 4096), (G.Q5_K, 14336)])
+                                 (G.Q4_0, 4096), (G.Q6_K, 4096), (G.Q5_0, 4096), (G.Q5_K, 14336),
+                                 (G.Q6_K, 14336), (G.Q4_K, 14296), (G.Q8_0, 14200)])   # 112-column tiles, ragged n
 def test_gemm_prefill_workload_shapes(t, n):
     m, k = G.PREFILL_M, 4096
     say("gemm full", G.NAMES[t], m, n, k)
