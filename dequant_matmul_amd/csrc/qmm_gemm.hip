@@ -15,7 +15,7 @@
 //   before it becomes the limit, and LDS delivers ~128 B/clk per CU.  So:
 //   - Workgroup tile BM (m) x BN (n) = 256 x 128 with 8 wavefronts stacked
 //     along m, each owning 32 x 128 = 2 x 8 MFMA blocks (256 x 112 when that
-//     tile count fills the CUs better, 128 x 64 with 4 waves of 32 x 64 when
+//     tile count fills the CUs better, 128 x 64 with 8 waves of 16 x 64 when
 //     256 x 128 tiles would leave half the CUs idle, 128 x 128 for
 //     m <= 128).  Every wave loads only its own X rows (two waves loading the
 //     same X lines doubled the L2 traffic and was 2.5x slower); all share the
@@ -647,9 +647,11 @@ hipError_t launch_gemm_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, cons
     // Wavefronts stacked along m, each 16 FM x 16 FN: every wave reads its own
     // X rows (no wave loads X another wave loads), all share the weight tile.
     // 256 x 128 tiles (8 waves) when they fill at least half the CUs; else
-    // 128 x 64 tiles (4 waves) before splitting K: on 512 x 4096 these give
-    // 256 tiles and ran 25% faster than 64 tiles split 4 ways, whose fp32
-    // atomics and zero fill cost more than the smaller tiles' extra decode.
+    // 128 x 64 tiles before splitting K: on 512 x 4096 these give 256 tiles
+    // and ran 25% faster than 64 tiles split 4 ways, whose fp32 atomics and
+    // zero fill cost more than the smaller tiles' extra decode.  Those tiles
+    // use 8 waves of 16 x 64 (two per SIMD, the first four decode the weight
+    // tile): measured 3-10% faster than 4 waves of 32 x 64.
     // Of 128- and 112-column tiles, 112 when they keep clearly more CUs busy
     // in the last round (512 x 14336: 224 tiles of 128 leave 32 of 256 CUs
     // idle, 256 tiles of 112 none; measured 4-5% faster).
@@ -665,7 +667,7 @@ hipError_t launch_gemm_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, cons
             return launch_cfg<T, 2, 7, 8, 1, 4>(w, n, k, rb, x, m, y, s);   // 256 x 112
         return launch_cfg<T, 2, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);       // 256 x 128
     }
-    return launch_cfg<T, 2, 4, 4, 1, 4>(w, n, k, rb, x, m, y, s);       // 128 x 64
+    return launch_cfg<T, 1, 4, 8, 1, 4>(w, n, k, rb, x, m, y, s);       // 128 x 64, 8 waves
 }
 
 hipError_t launch_gemm(int type, const void *w, int64_t n, int64_t k, size_t rb, const uint16_t *x, int64_t m,
