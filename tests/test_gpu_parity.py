@@ -126,6 +126,19 @@ def test_gemv_workload_shapes(t, n, k, batch):
     say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "gemv %s %dx%d" % (G.NAMES[t], n, k)))
 
 
+@pytest.mark.parametrize("batch", [1, 4, 8])
+def test_gemv_lm_head(batch):
+    """The largest matrix of the workloads: the 128256 x 4096 Q6_K LM head of
+    the Q4_K_M-style mix (431 MB), every output against the oracle."""
+    t, n, k = G.Q6_K, 128256, 4096
+    say("gemv lm head", n, k, batch)
+    w = G.gen_weights(t, n, k, seed=5024)
+    x = G.gen_x(k, batch, seed=5524)
+    ref, absum = oracle.gemv(t, w, n, k, x)
+    got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+    say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "lm head B=%d" % batch))
+
+
 @pytest.mark.parametrize("t", TYPES)
 def test_gemv_special_inputs(t):
     n, k = 70, 8 * G.BLOCK_ELEMS[t]
