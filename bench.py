@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized-weight matmul on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix|q5|embed|kv]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix|q5|embed|kv|dequant]
 
 A step is one decode pass over the TinyLlama-shaped Q4_0 weight stream:
 22 layers x (q, k, v, o, gate, up, down) = 154 GEMVs at batch 1 on one
@@ -18,7 +18,8 @@ for the other workloads (Q8_0 single matrix, Llama-3-8B Q4_K set, 512-token
 prefill GEMMs, Q4_K_M-style mix with a Q6_K LM head at batch 1/4/8, the
 same shapes in the 5-bit types Q5_K / Q5_0, the quantized embedding
 gather for one decode token and a 512-token chunk, and the Q8_0 / Q4_0
-KV-cache codec: encoding and decoding K rows of one Llama-3-8B layer).
+KV-cache codec: encoding and decoding K rows of one Llama-3-8B layer, and
+the dequant-only kernel to fp32 / fp16).
 """
 from __future__ import annotations
 
@@ -55,12 +56,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix", "q5", "embed", "kv"], default="all",
+    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix", "q5", "embed", "kv", "dequant"], default="all",
                    help="which secondary workloads to run after the primary line's (all by default)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU oracle sample")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB 10 times (reference for HBM byte counters)")
+    p.add_argument("--reference-bw", action="store_true",
+                   help="only time plain device fills and copies (torch kernels) of 16 MB and 235 MB, rotating over "
+                        "more than 400 MB: reference bandwidths for the streaming kernels")
     return p.parse_args()
 
 
@@ -130,6 +134,21 @@ class Codec:
             st = q.lib.qmm_dequant_f16(self.t, self.blocks.data_ptr(), self.n, self.k, self.back.data_ptr(), stream)
         if st != 0:
             raise RuntimeError("codec %s: %s" % (self.name, q.status_str(st)))
+
+
+class Dequant:
+    """One dequant-only call (qmm_dequant or qmm_dequant_f16)."""
+
+    def __init__(self, name, t, n, k, w, out, f16):
+        self.name, self.t, self.n, self.k, self.w, self.out, self.f16 = name, t, n, k, w, out, f16
+        # algorithmic bytes: the blocks read + the dense output written
+        self.bytes = n * G.row_bytes(t, k) + n * k * (2 if f16 else 4)
+
+    def launch(self, q, stream):
+        f = q.lib.qmm_dequant_f16 if self.f16 else q.lib.qmm_dequant
+        st = f(self.t, self.w.data_ptr(), self.n, self.k, self.out.data_ptr(), stream)
+        if st != 0:
+            raise RuntimeError("dequant %s: %s" % (self.name, q.status_str(st)))
 
 
 class Group:
@@ -382,6 +401,63 @@ def sec_kv(torch, q, steps, warmup, dev):
     return res
 
 
+def sec_dequant(torch, q, steps, warmup, dev):
+    """Dequant-only: the Q8_0 2048 x 2048 matrix and a Q4_K 14336 x 4096
+    gate projection to fp32 and fp16, rotating over enough weight copies and
+    outputs (> 256 MB per graph) that the last-level cache cannot hold them."""
+    res = {}
+    for name, t, n, k, seed in (("q8_0_2048", G.Q8_0, 2048, 2048, 1000), ("q4_k_gate", G.Q4_K, 14336, 4096, 3004)):
+        w0 = torch.from_numpy(G.gen_weights(t, n, k, seed)).to(dev)
+        for f16, dn in ((False, "f32"), (True, "f16")):
+            per = n * G.row_bytes(t, k) + n * k * (2 if f16 else 4)
+            copies = max(2, int(400e6 // per) + 1)
+            ws = [w0.clone() for _ in range(copies)]
+            probs = [Dequant(name, t, n, k, ws[i], torch.empty((n, k), dtype=torch.float16 if f16 else torch.float32,
+                                                                device=dev), f16) for i in range(copies)]
+            g = capture(torch, q, probs)
+            tg = time_graph(torch, g, max(2, steps // 2), warmup) / copies
+            b = probs[0].bytes
+            res["%s_%s" % (name, dn)] = {"shape": "%d x %d %s" % (n, k, G.NAMES[t]), "out": dn, "copies": copies,
+                                         "us_per_call": round(tg * 1e6, 3), "GB_s": round(b / tg / 1e9, 1),
+                                         "pct_hbm_peak": round(100 * b / tg / 1e9 / HBM_PEAK_GBS, 2)}
+            del g, probs, ws
+            torch.cuda.empty_cache()
+        del w0
+    return res
+
+
+def reference_bw(torch, dev):
+    """Plain fill (write only) and copy (read + write) of fp32 buffers, each
+    rotating over more than 400 MB, timed with events after a warm-up."""
+    res = {}
+    for label, nbytes in (("235MB", 14336 * 4096 * 4), ("16MB", 2048 * 2048 * 4)):
+        n = nbytes // 4
+        cnt = max(2, int(400e6 // nbytes) + 1)
+        dst = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(cnt)]
+        src = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(cnt)]
+        for name, moved in (("fill", nbytes), ("copy", 2 * nbytes)):
+            def once():
+                for i in range(cnt):
+                    if name == "fill":
+                        dst[i].fill_(1.0)
+                    else:
+                        dst[i].copy_(src[i])
+            for _ in range(3):
+                once()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                once()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / (5 * cnt)
+            res["%s_%s" % (name, label)] = {"us": round(t * 1e6, 2), "GB_s": round(moved / t / 1e9, 1)}
+        del dst, src
+        torch.cuda.empty_cache()
+    return res
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -402,6 +478,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes_read": nb, "bytes_written": nb, "launches": 10}))
+        return
+    if args.reference_bw:
+        print(json.dumps(reference_bw(torch, dev)))
         return
     import dequant_matmul_amd as q
     log("device:", torch.cuda.get_device_name(0), "| lib:", q.version())
@@ -523,6 +602,9 @@ def main():
         if want("embed"):
             log("secondary: embedding gathers")
             sec["embed"] = sec_embed(torch, q, args.steps, args.warmup, dev)
+        if want("dequant"):
+            log("secondary: dequant-only")
+            sec["dequant"] = sec_dequant(torch, q, args.steps, args.warmup, dev)
         if want("kv"):
             log("secondary: KV-cache codec")
             sec["kv_codec"] = sec_kv(torch, q, args.steps, args.warmup, dev)
