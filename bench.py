@@ -463,8 +463,8 @@ def reference_bw(torch, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(GEMV rows / GEMM columns would shard across GPUs; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(GEMV rows / GEMM columns would shard across GPUs, one shard per GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     dev = "cuda:0"
