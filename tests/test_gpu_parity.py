@@ -126,6 +126,29 @@ def test_gemv_workload_shapes(t, n, k, batch):
     say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "gemv %s %dx%d" % (G.NAMES[t], n, k)))
 
 
+@pytest.mark.parametrize("t", TYPES)
+def test_gemv_and_gemm_wide_k(t):
+    """k past the widest x staging of the batch-1 kernels (16384), with a
+    partial last segment: batch 1 takes the generic segment-by-segment
+    kernel, batches 3 and 8 their usual paths over many segments; the GEMM
+    runs 161 K steps."""
+    k = 20480 if G.BLOCK_ELEMS[t] == 256 else 16416
+    n = 133
+    w = G.gen_weights(t, n, k, seed=900 + t)
+    wd = upload(w)
+    for batch in (1, 3, 8):
+        say("gemv wide k", G.NAMES[t], n, k, batch)
+        x = G.gen_x(k, batch, seed=910 + batch)
+        ref, absum = oracle.gemv(t, w, n, k, x)
+        got = q.gemv(wd, t, n, k, upload(x)).cpu().numpy()
+        check_tol(got, ref, absum, GEMV_TOL, "gemv wide k %s B=%d" % (G.NAMES[t], batch))
+    say("gemm wide k", G.NAMES[t], 70, n, k)
+    X = G.gen_x_f16(70, k, seed=920)
+    ref, absum = oracle.gemm(t, w, n, k, X)
+    got = q.gemm_prefill(wd, t, n, k, upload(X)).cpu().numpy()
+    check_tol(got, ref, absum, GEMM_TOL, "gemm wide k %s" % G.NAMES[t])
+
+
 @pytest.mark.parametrize("batch", [1, 4, 8])
 def test_gemv_lm_head(batch):
     """The largest matrix of the workloads: the 128256 x 4096 Q6_K LM head of
