@@ -110,6 +110,19 @@ def _check_w(w, qtype: int, n: int, k: int):
         raise ValueError("weight tensor has %d bytes, expected n * row_bytes = %d" % (w.numel(), n * rb))
 
 
+def _out(out, shape, dtype, device):
+    """The caller's output tensor, checked (the library writes exactly
+    prod(shape) elements of dtype there), or a new one."""
+    torch = _torch()
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if (out.dtype != dtype or tuple(out.shape) != tuple(shape) or not out.is_contiguous()
+            or out.device != torch.device(device)):
+        raise ValueError("out must be a contiguous %s tensor of shape %s on %s (got %s %s on %s)"
+                         % (dtype, tuple(shape), device, out.dtype, tuple(out.shape), out.device))
+    return out
+
+
 def _call(status: int, what: str) -> None:
     if status != OK:
         raise QmmError(status, what)
@@ -119,8 +132,7 @@ def dequant(w, qtype: int, n: int, k: int, out=None):
     """fp32 [n, k] dequantized weights (bit-exact)."""
     torch = _torch()
     _check_w(w, qtype, n, k)
-    if out is None:
-        out = torch.empty((n, k), dtype=torch.float32, device=w.device)
+    out = _out(out, (n, k), torch.float32, w.device)
     _call(lib.qmm_dequant(qtype, w.data_ptr(), n, k, out.data_ptr(), _stream_ptr(w.device)), "qmm_dequant")
     return out
 
@@ -129,8 +141,7 @@ def dequant_f16(w, qtype: int, n: int, k: int, out=None):
     """fp16 [n, k] dequantized weights (the fp32 values rounded to nearest-even)."""
     torch = _torch()
     _check_w(w, qtype, n, k)
-    if out is None:
-        out = torch.empty((n, k), dtype=torch.float16, device=w.device)
+    out = _out(out, (n, k), torch.float16, w.device)
     _call(lib.qmm_dequant_f16(qtype, w.data_ptr(), n, k, out.data_ptr(), _stream_ptr(w.device)),
           "qmm_dequant_f16")
     return out
@@ -146,14 +157,12 @@ def embed(table, qtype: int, vocab: int, k: int, ids, dtype=None, out=None):
     if ids.dtype != torch.int32 or not ids.is_cuda or ids.dim() != 1 or not ids.is_contiguous():
         raise ValueError("ids must be a contiguous int32 device tensor [seq]")
     seq = ids.shape[0]
-    if out is None:
-        out = torch.empty((seq, k), dtype=dtype, device=table.device)
-    if dtype == torch.float32:
-        f = lib.qmm_embed
-    elif dtype == torch.float16:
-        f = lib.qmm_embed_f16
-    else:
+    if dtype not in (torch.float32, torch.float16):
         raise ValueError("dtype must be torch.float32 or torch.float16")
+    if ids.device != table.device:
+        raise ValueError("ids and the table must be on the same device")
+    out = _out(out, (seq, k), dtype, table.device)
+    f = lib.qmm_embed if dtype == torch.float32 else lib.qmm_embed_f16
     _call(f(qtype, table.data_ptr(), vocab, k, ids.data_ptr(), seq, out.data_ptr(), _stream_ptr(table.device)),
           "qmm_embed")
     return out
@@ -169,8 +178,9 @@ def quantize(x, qtype: int, out=None):
         raise ValueError("x must be a contiguous 2-D device tensor")
     n, k = x.shape
     rb = row_bytes(qtype, k)
-    if out is None:
-        out = torch.empty((n, rb), dtype=torch.uint8, device=x.device)
+    if rb == 0 and k > 0:
+        raise ValueError("k=%d is not a multiple of the block size of type %d" % (k, qtype))
+    out = _out(out, (n, rb), torch.uint8, x.device)
     if x.dtype == torch.float32:
         f = lib.qmm_quantize
     elif x.dtype == torch.float16:
@@ -191,8 +201,9 @@ def gemv(w, qtype: int, n: int, k: int, x, out=None):
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or x.shape[1] != k:
         raise ValueError("x must be a contiguous fp32 device tensor [B, k]")
     B = x.shape[0]
-    if out is None:
-        out = torch.empty((B, n), dtype=torch.float32, device=w.device)
+    if x.device != w.device:
+        raise ValueError("x and the weights must be on the same device")
+    out = _out(out, (B, n), torch.float32, w.device)
     _call(lib.qmm_gemv(qtype, w.data_ptr(), n, k, x.data_ptr(), B, out.data_ptr(), _stream_ptr(w.device)),
           "qmm_gemv")
     return out[0] if squeeze else out
@@ -212,7 +223,10 @@ def gemv_multi(ws, qtype: int, ns, k: int, xs, outs=None):
         if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or tuple(x.shape) != (B, k):
             raise ValueError("each x must be a contiguous fp32 device tensor [B, k] with the same B")
     if outs is None:
-        outs = [torch.empty((B, n), dtype=torch.float32, device=w.device) for w, n in zip(ws, ns)]
+        outs = [None] * np_
+    if len(outs) != np_:
+        raise ValueError("outs must have one tensor per problem")
+    outs = [_out(o, (B, n), torch.float32, w.device) for o, w, n in zip(outs, ws, ns)]
     wp = (ctypes.c_void_p * max(np_, 1))(*[w.data_ptr() for w in ws])
     xp = (ctypes.c_void_p * max(np_, 1))(*[x.data_ptr() for x in xs])
     yp = (ctypes.c_void_p * max(np_, 1))(*[o.data_ptr() for o in outs])
@@ -230,8 +244,9 @@ def gemm_prefill(w, qtype: int, n: int, k: int, x, out=None):
     if x.dtype != torch.float16 or not x.is_cuda or not x.is_contiguous() or x.shape[1] != k:
         raise ValueError("X must be a contiguous fp16 device tensor [m, k]")
     m = x.shape[0]
-    if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=w.device)
+    if x.device != w.device:
+        raise ValueError("X and the weights must be on the same device")
+    out = _out(out, (m, n), torch.float32, w.device)
     _call(lib.qmm_gemm_prefill(qtype, w.data_ptr(), n, k, x.data_ptr(), m, out.data_ptr(),
                                _stream_ptr(w.device)), "qmm_gemm_prefill")
     return out

@@ -138,3 +138,31 @@ def test_embed_rejects_misaligned_ids_without_launching():
     assert st == q.ERR_ALIGN
     torch.cuda.synchronize()
     assert torch.equal(out.cpu(), torch.full((1, k), 7.0))      # untouched
+
+
+def test_binding_checks_output_tensors():
+    """A caller's out= tensor of the wrong dtype, shape or layout is refused
+    before anything is launched (the library writes exactly the requested
+    elements there)."""
+    t, n, k = G.Q8_0, 8, 64
+    w = upload(G.gen_weights(t, n, k, seed=3))
+    ids = upload(np.array([1, 2], np.int32))
+    x = upload(G.gen_x(k, 2, seed=4))
+    X = upload(G.gen_x_f16(3, k, seed=5))
+    bad = [
+        lambda: q.embed(w, t, n, k, ids, out=torch.empty((2, k), dtype=torch.float16, device=DEV)),
+        lambda: q.embed(w, t, n, k, ids, dtype=torch.float16, out=torch.empty((2, k), device=DEV)),
+        lambda: q.embed(w, t, n, k, ids, out=torch.empty((3, k), device=DEV)),
+        lambda: q.dequant(w, t, n, k, out=torch.empty((n, k - 32), device=DEV)),
+        lambda: q.dequant_f16(w, t, n, k, out=torch.empty((n, k), device=DEV)),
+        lambda: q.gemv(w, t, n, k, x, out=torch.empty((n, 2), device=DEV).t()),
+        lambda: q.gemm_prefill(w, t, n, k, X, out=torch.empty((3, n), dtype=torch.float16, device=DEV)),
+        lambda: q.quantize(X.float(), t, out=torch.empty((3, 60), dtype=torch.uint8, device=DEV)),
+        lambda: q.gemv_multi([w], t, [n], k, [x], outs=[torch.empty((2, n - 1), device=DEV)]),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(ValueError):
+            f()
+    # matching tensors are used in place
+    o = torch.empty((2, k), device=DEV)
+    assert q.embed(w, t, n, k, ids, out=o).data_ptr() == o.data_ptr()
