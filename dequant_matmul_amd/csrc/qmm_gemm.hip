@@ -591,20 +591,12 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
         }
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (256, the MI355X count, if the runtime
+// cannot tell: only the tile choice depends on it).
 static int cu_count()
 {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 256;
-    if (cached[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-            v = 256;
-        cached[dev] = v;
-    }
-    return cached[dev];
+    const int v = device_cu_count();
+    return v > 0 ? v : 256;
 }
 
 hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s);

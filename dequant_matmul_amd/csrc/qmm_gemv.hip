@@ -1122,13 +1122,9 @@ template <int T, int R, int NW>
 static hipError_t launch_b1_xlds(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                                  hipStream_t s)
 {
-    static int cus = 0;   // per-process cache (one device model)
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            return hipErrorInvalidValue;
-    }
+    const int cus = device_cu_count();
+    if (cus == 0)
+        return hipErrorInvalidValue;
     const int64_t want = ((n + R - 1) / R + NW - 1) / NW;
     const dim3 grid((unsigned)(want < cus ? want : cus)), block(64 * NW);
     hipLaunchKernelGGL((gemv3_kernel<T, R, NW>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
@@ -1139,8 +1135,9 @@ template <int T, int R>
 static hipError_t launch_b1_regs(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                                  hipStream_t s)
 {
-    static int cap = 0;   // per-process cache (one device model)
-    if (cap == 0 && (cap = gemv2_cap(gemv2_kernel<T, R>)) == 0)
+    static std::atomic<int> slot[64];
+    const int cap = per_device_cached(slot, [] { return gemv2_cap(gemv2_kernel<T, R>); });
+    if (cap == 0)
         return hipErrorInvalidValue;
     const int64_t nrg = (n + R - 1) / R;
     // mid-size matrices run best with one workgroup per CU (each wave then
@@ -1155,8 +1152,9 @@ static hipError_t launch_b1_regs(const uint8_t *w, int64_t n, int64_t k, size_t 
 template <int T, int R>
 static hipError_t launch_b1_table(const GemvProbs &P, int64_t k, size_t rb, hipStream_t s)
 {
-    static int cap = 0;
-    if (cap == 0 && (cap = gemv2_cap(gemv2m_kernel<T, R>)) == 0)
+    static std::atomic<int> slot[64];
+    const int cap = per_device_cached(slot, [] { return gemv2_cap(gemv2m_kernel<T, R>); });
+    if (cap == 0)
         return hipErrorInvalidValue;
     const int64_t want = ((int64_t)P.rg0[P.np] + 3) / 4;
     if (want == 0)
@@ -1170,8 +1168,9 @@ template <int T, int R, int NW, int XK, int D>
 static hipError_t launch_b1_lds(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                                 hipStream_t s)
 {
-    static int cap = 0;
-    if (cap == 0 && (cap = resident_wgs(gemv1_kernel<T, R, NW, XK, D>, 64 * NW)) == 0)
+    static std::atomic<int> slot[64];
+    const int cap = per_device_cached(slot, [] { return resident_wgs(gemv1_kernel<T, R, NW, XK, D>, 64 * NW); });
+    if (cap == 0)
         return hipErrorInvalidValue;
     const int64_t want = ((n + R - 1) / R + NW - 1) / NW;
     const dim3 grid((unsigned)(want < cap ? want : cap)), block(64 * NW);
@@ -1208,13 +1207,9 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
             // two rows per item, unless that leaves compute units without a
             // workgroup (e.g. 2048 rows: 128 workgroups of 8 waves); then one
             // (measured on MI355X: 2048 x 5632 Q4_0 5.95 -> 5.23 us)
-            static int cus = 0;   // per-process cache (one device model)
-            if (cus == 0) {
-                int dev = 0;
-                if (hipGetDevice(&dev) != hipSuccess ||
-                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-                    return hipErrorInvalidValue;
-            }
+            const int cus = device_cu_count();
+            if (cus == 0)
+                return hipErrorInvalidValue;
             if (((n + 1) / 2 + 7) / 8 < cus)
                 return launch_b1_lds<T, 1, 8, 16384, 1>(w, n, k, rb, x, y, s);
             return launch_b1_lds<T, 2, 8, 16384, 1>(w, n, k, rb, x, y, s);

@@ -635,16 +635,8 @@ gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const flo
 
 int cu_count_cached()
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
-    return cus;
+    const int v = device_cu_count();
+    return v > 0 ? v : 256;
 }
 
 template <int T>

@@ -9,7 +9,41 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qmm {
+
+// A positive per-device value (a CU count, resident workgroups of a kernel)
+// computed on first use for the current device and cached in slot[device].
+// Relaxed atomics: concurrent first calls compute the same value, so a race
+// only repeats the query.  Returns 0 if compute() fails (not cached).
+template <class F>
+inline int per_device_cached(std::atomic<int> (&slot)[64], F compute)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return compute();
+    int v = slot[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        v = compute();
+        if (v > 0)
+            slot[dev].store(v, std::memory_order_relaxed);
+    }
+    return v > 0 ? v : 0;
+}
+
+// Compute units of the current device (0 if the runtime cannot tell).
+inline int device_cu_count()
+{
+    static std::atomic<int> slot[64];
+    return per_device_cached(slot, [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        return v;
+    });
+}
 
 hipError_t launch_dequant(int type, const void *w, int64_t n, int64_t k, size_t rb, float *out,
                           hipStream_t s);

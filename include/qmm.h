@@ -48,8 +48,10 @@
  *     row-major C = A x B).
  *   - All pointers are device pointers (HIP device memory, or memory the
  *     device can access) and must be 16-byte aligned.  The caller owns every
- *     buffer; the library allocates nothing, keeps no state between calls,
- *     and is safe to call from several host threads.
+ *     buffer; the library allocates nothing and keeps no state between calls
+ *     besides device properties it reads once per device (CU count, resident
+ *     workgroups per kernel, cached with atomics), and is safe to call from
+ *     several host threads.
  *   - stream: a hipStream_t passed as void* (NULL = the default stream).
  *     Every call only enqueues work on that stream and never synchronizes
  *     (dotLLM "GPU Inference", Synchronization Model: one stream, all

@@ -100,3 +100,48 @@ def test_graph_replays_match_eager():
         err = np.abs(got["gemm"].cpu().numpy()[rows] - ref)
         assert np.all(err <= 1e-3 * absum), r
         print("replay", r, "ok", flush=True)
+
+
+def test_concurrent_host_threads():
+    """Four host threads, each on its own stream, call the GEMV and the GEMM
+    at the same time (the launch parameters they share are read from
+    per-device atomic caches); every result matches the single-threaded
+    one."""
+    import threading
+    jobs = []
+    for i in range(4):
+        t = [G.Q4_0, G.Q4_K, G.Q6_K, G.Q8_0][i]
+        n, k = 1000 + 37 * i, 4096
+        w = up(G.gen_weights(t, n, k, 60 + i))
+        x = up(G.gen_x(k, 1 + 2 * i, 70 + i))
+        X = up(G.gen_x_f16(33, k, 80 + i))
+        jobs.append((t, n, k, w, x, X))
+    ref = [(q.gemv(w, t, n, k, x).clone(), q.gemm_prefill(w, t, n, k, X).clone()) for t, n, k, w, x, X in jobs]
+    torch.cuda.synchronize()
+    results = [None] * 4
+    errors = []
+    barrier = threading.Barrier(4)
+
+    def work(i):
+        try:
+            t, n, k, w, x, X = jobs[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                barrier.wait()
+                outs = [(q.gemv(w, t, n, k, x), q.gemm_prefill(w, t, n, k, X)) for _ in range(10)]
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:          # reported below
+            errors.append(e)
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for h in th:
+        h.start()
+    for h in th:
+        h.join()
+    assert not errors, errors
+    for i, outs in enumerate(results):
+        for y, Y in outs:
+            assert torch.equal(y, ref[i][0]), i
+            # shapes whose GEMM splits K add in a varying order: compare closely
+            assert torch.allclose(Y, ref[i][1], rtol=0, atol=1e-4 * float(ref[i][1].abs().max())), i
