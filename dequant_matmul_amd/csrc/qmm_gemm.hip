@@ -12,7 +12,8 @@
 // gfx950 design
 //   Measured on MI355X: v_mfma_f32_16x16x32_f16 sustains ~2.0-2.2 PFLOP/s;
 //   VALU work co-issues with MFMA only up to ~3-4 wave instructions per MFMA
-//   before it becomes the limit, and LDS delivers ~128 B/clk per CU.  So:
+//   before it becomes the limit, and LDS delivers 256 B/clk per CU to
+//   conflict-free 128-bit reads and 128 B/clk to stores.  So:
 //   - Workgroup tile BM (m) x BN (n) = 256 x 128 with 8 wavefronts stacked
 //     along m, each owning 32 x 128 = 2 x 8 MFMA blocks (256 x 112 when that
 //     tile count fills the CUs better, 128 x 64 with 8 waves of 16 x 64 when
@@ -21,8 +22,9 @@
 //     same X lines doubled the L2 traffic and was 2.5x slower); all share the
 //     weight tile.  The decode of a weight element is shared by BM rows of X.
 //   - Only the weight tile goes through LDS: it is decoded once per workgroup
-//     into fp16 [n][k] (row stride padded by 8 halves, conflict-free 128-bit
-//     fragment reads), double buffered, K step 128.  The decode of tile t+1
+//     into fp16 [n][k] (16-byte chunks XOR-swizzled within each row so that
+//     the 128-bit fragment reads and decode stores are bank-conflict free),
+//     double buffered, K step 128.  The decode of tile t+1
 //     runs between the MFMAs of tile t; one barrier per K step.
 //   - X fragments are loaded straight from global memory into the MFMA
 //     operand registers (16 bytes per lane; L2-resident), one K step ahead in
@@ -57,7 +59,6 @@ constexpr int GKT = 128;            // K step
 #define QMM_GEMM_SCHED 1
 #endif
 constexpr bool SCHED = QMM_GEMM_SCHED;   // explicit MFMA / VALU interleave
-constexpr int GLD = GKT + 8;        // LDS row stride of the weight tile, halves
 
 // Unaligned byte runs: NDW dwords starting at an even byte address p are
 // fetched as the NDW aligned dwords at or below p plus a 2-byte tail, reading
@@ -181,27 +182,56 @@ __device__ __forceinline__ void keep_raw(const WRaw<T> &r)
         asm volatile("" : : "v"(v[i]));
 }
 
-__device__ __forceinline__ void st64(_Float16 *dst, uint32_t a, uint32_t b)
+// Weight tile layout in LDS: row r holds the 128 K-step weights of output
+// column r as fp16; its 16-byte chunk c (weights 8c .. 8c+7) is stored at
+// chunk c ^ ((c >> 1) & 6) ^ (r % 16) of the row (no padding).  Measured on
+// gfx950 (LDS bank-conflict counters): a 16-byte read serves 16 lanes per
+// cycle from 64 banks, in lane quads grouped by half-wave and by the parity
+// of the quad index, and a 16-byte store serves 8 consecutive lanes from 32
+// banks.  Under this swizzle both the MFMA fragment reads (lane l: row l % 16,
+// chunk 4 s + l / 16) and the decode stores (lane l: row l / 4, the chunk of
+// quarter l % 4 and part i) hit distinct banks; a row pitch padded by 8 halves
+// conflicted 2-way on the reads and 2- to 4-way on the stores.
+__device__ __forceinline__ int tile_off(int r, int c)
 {
-    *(uint32_t __attribute__((ext_vector_type(2))) *)dst = (uint32_t __attribute__((ext_vector_type(2)))){a, b};
+    return r * GKT + 8 * ((c ^ ((c >> 1) & 6) ^ r) & 15);
 }
 
-// Decoder of one unit, in four parts of 8 weights (one code dword pair /
-// dword each), so that the decode can be spread between the MFMAs of the four
-// 32-wide sub-steps of a K step.  setup() prepares the scales; part(i, ws)
-// stores its 8 fp16 weights into weight tile row ws.
+// The swizzle is linear over GF(2): for a chunk c ^ d whose set bits do not
+// meet those of c, tile_off(r, c ^ d) = tile_off(r, c) ^ tile_xor(d).
+__host__ __device__ constexpr int tile_xor(int d)
+{
+    return 8 * ((d ^ ((d >> 1) & 6)) & 15);
+}
+
+// Decoder of one unit, in four parts of 8 consecutive weights (one 16-byte
+// store each), so that the decode can be spread between the MFMAs of the four
+// 32-wide sub-steps of a K step.  setup() prepares the scales; part(i, dst)
+// stores its 8 fp16 weights at dst.  chunk(q, i) = chunk(q, 0) ^ delta(i):
+// the row chunk (8 weights) that part i of quarter q covers (delta(i) shares
+// no set bit with chunk(q, 0)).
 template <int T> struct Dec;
+
+__device__ __forceinline__ uint32_t dw(const u32x4 &v, int k)
+{
+    return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ void st128(_Float16 *dst, const uint32_t (&o)[4])
+{
+    *(u32x4 *)dst = u32x4{o[0], o[1], o[2], o[3]};
+}
 
 template <> struct Dec<T_Q8_0> {
     half2v d2;
-    int off;
-    __device__ __forceinline__ void setup(const WRaw<T_Q8_0> &r, int, int q)
+    static constexpr int delta(int i) { return i; }
+    static __device__ __forceinline__ int chunk(int q, int i) { return 4 * q + delta(i); }
+    __device__ __forceinline__ void setup(const WRaw<T_Q8_0> &r, int, int)
     {
         keep_raw(r);
         d2 = bits_h2(r.d | (r.d << 16));
-        off = 32 * q;
     }
-    __device__ __forceinline__ void part(const WRaw<T_Q8_0> &r, int i, _Float16 *ws) const
+    __device__ __forceinline__ void part(const WRaw<T_Q8_0> &r, int i, _Float16 *dst) const
     {
         const half2v bias = {(_Float16)1152.f, (_Float16)1152.f};
         uint32_t o[4];
@@ -212,38 +242,47 @@ template <> struct Dec<T_Q8_0> {
             for (int j = 0; j < 2; ++j)
                 o[2 * h + j] = h2_bits((bits_h2(bytes_1024(c, j)) - bias) * d2);   // q exact, one rounding
         }
-        *(u32x4 *)(ws + off + 8 * i) = u32x4{o[0], o[1], o[2], o[3]};
+        st128(dst, o);
     }
 };
 
+// Q4_0 / Q5_0 part i: the low (i even: elements 8 (i / 2) + 0..7) or high
+// (i odd: elements 16 + 8 (i / 2) + 0..7) nibbles of code dwords 2 (i / 2) and
+// 2 (i / 2) + 1, so that each code dword is needed by two consecutive parts.
 template <> struct Dec<T_Q4_0> {
     half2v d2;
-    int off;
-    __device__ __forceinline__ void setup(const WRaw<T_Q4_0> &r, int, int q)
+    static constexpr int delta(int i) { return (i >> 1) + 2 * (i & 1); }
+    static __device__ __forceinline__ int chunk(int q, int i) { return 4 * q + delta(i); }
+    __device__ __forceinline__ void setup(const WRaw<T_Q4_0> &r, int, int)
     {
         keep_raw(r);
         d2 = bits_h2(r.d | (r.d << 16));
-        off = 32 * q;
     }
-    __device__ __forceinline__ void part(const WRaw<T_Q4_0> &r, int i, _Float16 *ws) const
+    __device__ __forceinline__ void part(const WRaw<T_Q4_0> &r, int i, _Float16 *dst) const
     {
         const half2v bias = {(_Float16)1032.f, (_Float16)1032.f};
-        const uint32_t c = align_bytes(r.c.d[i + 1], r.c.d[i], r.sh);
-        uint32_t lo[2], hi[2];
+        uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t b = bytes_1024(c, j);                   // [c, 0x64, c', 0x64]
-            lo[j] = h2_bits((bits_h2(b & 0x640f640fu) - bias) * d2);
-            hi[j] = h2_bits((bits_h2(((b >> 4) & 0x000f000fu) | 0x64006400u) - bias) * d2);
+        for (int h = 0; h < 2; ++h) {
+            const int k = 2 * (i >> 1) + h;
+            const uint32_t c = align_bytes(r.c.d[k + 1], r.c.d[k], r.sh);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t b = bytes_1024(c, j);                   // [c, 0x64, c', 0x64]
+                const uint32_t v = (i & 1) == 0 ? (b & 0x640f640fu) : (((b >> 4) & 0x000f000fu) | 0x64006400u);
+                o[2 * h + j] = h2_bits((bits_h2(v) - bias) * d2);
+            }
         }
-        st64(ws + off + 4 * i, lo[0], lo[1]);          // elements 4i .. 4i+3
-        st64(ws + off + 16 + 4 * i, hi[0], hi[1]);     // elements 16+4i .. 16+4i+3
+        st128(dst, o);
     }
 };
 
+// Q4_K / Q5_K part i: the low (i even, sub-block 2p) or high (i odd, sub-block
+// 2p + 1) nibbles of code dwords 2 (i / 2) and 2 (i / 2) + 1 of the unit.
 template <> struct Dec<T_Q4_K> {
     float dsc0, dm0, dsc1, dm1;
-    int base;
+    static constexpr int delta(int i) { return (i >> 1) + 4 * (i & 1); }
+    static __device__ __forceinline__ int chunk(int q, int i) { return 8 * (q >> 1) + 2 * (q & 1) + delta(i); }
     __device__ __forceinline__ void setup(const WRaw<T_Q4_K> &r, int t, int q)
     {
         keep_raw(r);
@@ -258,53 +297,57 @@ template <> struct Dec<T_Q4_K> {
         dm0 = dmin * (float)m0;
         dsc1 = d * (float)sc1 * 0.0625f;
         dm1 = dmin * (float)m1;
-        base = 64 * (q >> 1) + 16 * (q & 1);
     }
-    __device__ __forceinline__ void part(const WRaw<T_Q4_K> &r, int i, _Float16 *ws) const
+    __device__ __forceinline__ void part(const WRaw<T_Q4_K> &r, int i, _Float16 *dst) const
     {
-        const uint32_t c = i == 0 ? r.c.x : i == 1 ? r.c.y : i == 2 ? r.c.z : r.c.w;
-        const uint32_t lo = opaque(c & 0x0f0f0f0fu), hi = opaque(c & 0xf0f0f0f0u);
-        st64(ws + base + 4 * i,
-             pack_rne(__builtin_fmaf(ub0(lo), dsc0, -dm0), __builtin_fmaf(ub1(lo), dsc0, -dm0)),
-             pack_rne(__builtin_fmaf(ub2(lo), dsc0, -dm0), __builtin_fmaf(ub3(lo), dsc0, -dm0)));
-        st64(ws + base + 32 + 4 * i,
-             pack_rne(__builtin_fmaf(ub0(hi), dsc1, -dm1), __builtin_fmaf(ub1(hi), dsc1, -dm1)),
-             pack_rne(__builtin_fmaf(ub2(hi), dsc1, -dm1), __builtin_fmaf(ub3(hi), dsc1, -dm1)));
+        const bool lo = (i & 1) == 0;
+        const float ds = lo ? dsc0 : dsc1, dm = lo ? dm0 : dm1;
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t c = dw(r.c, 2 * (i >> 1) + h);
+            const uint32_t v = opaque(c & (lo ? 0x0f0f0f0fu : 0xf0f0f0f0u));
+            o[2 * h] = pack_rne(__builtin_fmaf(ub0(v), ds, -dm), __builtin_fmaf(ub1(v), ds, -dm));
+            o[2 * h + 1] = pack_rne(__builtin_fmaf(ub2(v), ds, -dm), __builtin_fmaf(ub3(v), ds, -dm));
+        }
+        st128(dst, o);
     }
 };
 
 template <> struct Dec<T_Q5_0> {
     half2v d2;
-    int off;
-    __device__ __forceinline__ void setup(const WRaw<T_Q5_0> &r, int, int q)
+    static constexpr int delta(int i) { return Dec<T_Q4_0>::delta(i); }
+    static __device__ __forceinline__ int chunk(int q, int i) { return 4 * q + delta(i); }
+    __device__ __forceinline__ void setup(const WRaw<T_Q5_0> &r, int, int)
     {
         keep_raw(r);
         d2 = bits_h2(r.d | (r.d << 16));
-        off = 32 * q;
     }
-    __device__ __forceinline__ void part(const WRaw<T_Q5_0> &r, int i, _Float16 *ws) const
+    __device__ __forceinline__ void part(const WRaw<T_Q5_0> &r, int i, _Float16 *dst) const
     {
         const half2v bias = {(_Float16)1040.f, (_Float16)1040.f};
         const uint32_t hb = align_bytes(r.c.d[1], r.c.d[0], r.sh);
-        const uint32_t c = align_bytes(r.c.d[i + 2], r.c.d[i + 1], r.sh);
-        const uint32_t q5lo = (c & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (4 * i));
-        const uint32_t q5hi = ((c >> 4) & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (16 + 4 * i));
-        uint32_t lo[2], hi[2];
+        uint32_t o[4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            // 1024 + q exactly, minus the bias 1040: q - 16, then one rounding of d (q - 16)
-            lo[j] = h2_bits((bits_h2(bytes_1024(q5lo, j)) - bias) * d2);
-            hi[j] = h2_bits((bits_h2(bytes_1024(q5hi, j)) - bias) * d2);
+        for (int h = 0; h < 2; ++h) {
+            const int k = 2 * (i >> 1) + h;
+            const uint32_t c = align_bytes(r.c.d[k + 2], r.c.d[k + 1], r.sh);
+            // element e of the block takes bit e of the high-bit word
+            const uint32_t q5 = (i & 1) == 0 ? (c & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (4 * k))
+                                      : ((c >> 4) & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (16 + 4 * k));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)   // 1024 + q exactly, minus 1040: q - 16, then one rounding of d (q - 16)
+                o[2 * h + j] = h2_bits((bits_h2(bytes_1024(q5, j)) - bias) * d2);
         }
-        st64(ws + off + 4 * i, lo[0], lo[1]);          // elements 4i .. 4i+3
-        st64(ws + off + 16 + 4 * i, hi[0], hi[1]);     // elements 16+4i .. 16+4i+3
+        st128(dst, o);
     }
 };
 
 template <> struct Dec<T_Q5_K> {
     float dsc0, dm0, dsc1, dm1;
     uint32_t hs;
-    int base;
+    static constexpr int delta(int i) { return Dec<T_Q4_K>::delta(i); }
+    static __device__ __forceinline__ int chunk(int q, int i) { return Dec<T_Q4_K>::chunk(q, i); }
     __device__ __forceinline__ void setup(const WRaw<T_Q5_K> &r, int t, int q)
     {
         keep_raw(r);
@@ -318,51 +361,59 @@ template <> struct Dec<T_Q5_K> {
         dsc1 = d * (float)sc1;
         dm1 = dmin * (float)m1;
         hs = 2u * (uint32_t)p;      // qh bit of sub-block 2p; 2p + 1 for the high nibbles
-        base = 64 * (q >> 1) + 16 * (q & 1);
     }
-    __device__ __forceinline__ void part(const WRaw<T_Q5_K> &r, int i, _Float16 *ws) const
+    __device__ __forceinline__ void part(const WRaw<T_Q5_K> &r, int i, _Float16 *dst) const
     {
-        const uint32_t c = i == 0 ? r.c.x : i == 1 ? r.c.y : i == 2 ? r.c.z : r.c.w;
-        const uint32_t h = i == 0 ? r.h.x : i == 1 ? r.h.y : i == 2 ? r.h.z : r.h.w;
-        const uint32_t lo = opaque((c & 0x0f0f0f0fu) | (((h >> hs) & 0x01010101u) << 4));
-        const uint32_t hi = opaque(((c >> 4) & 0x0f0f0f0fu) | (((h >> (hs + 1u)) & 0x01010101u) << 4));
-        st64(ws + base + 4 * i,
-             pack_rne(__builtin_fmaf(ub0(lo), dsc0, -dm0), __builtin_fmaf(ub1(lo), dsc0, -dm0)),
-             pack_rne(__builtin_fmaf(ub2(lo), dsc0, -dm0), __builtin_fmaf(ub3(lo), dsc0, -dm0)));
-        st64(ws + base + 32 + 4 * i,
-             pack_rne(__builtin_fmaf(ub0(hi), dsc1, -dm1), __builtin_fmaf(ub1(hi), dsc1, -dm1)),
-             pack_rne(__builtin_fmaf(ub2(hi), dsc1, -dm1), __builtin_fmaf(ub3(hi), dsc1, -dm1)));
+        const bool lo = (i & 1) == 0;
+        const float ds = lo ? dsc0 : dsc1, dm = lo ? dm0 : dm1;
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = 2 * (i >> 1) + h;
+            const uint32_t c = dw(r.c, k), hq = dw(r.h, k);
+            const uint32_t v = lo ? opaque((c & 0x0f0f0f0fu) | (((hq >> hs) & 0x01010101u) << 4))
+                                     : opaque(((c >> 4) & 0x0f0f0f0fu) | (((hq >> (hs + 1u)) & 0x01010101u) << 4));
+            o[2 * h] = pack_rne(__builtin_fmaf(ub0(v), ds, -dm), __builtin_fmaf(ub1(v), ds, -dm));
+            o[2 * h + 1] = pack_rne(__builtin_fmaf(ub2(v), ds, -dm), __builtin_fmaf(ub3(v), ds, -dm));
+        }
+        st128(dst, o);
     }
 };
 
+// Q6_K part i: group g = q / 2 (low nibbles, i even) or g + 2 (high nibbles,
+// i odd) of ql / qh dwords 2 (i / 2) and 2 (i / 2) + 1 of the unit.
 template <> struct Dec<T_Q6_K> {
     float ds0, nb0, ds1, nb1;
     uint32_t hs0;
-    int base;
+    static constexpr int delta(int i) { return (i >> 1) + 8 * (i & 1); }
+    static __device__ __forceinline__ int chunk(int q, int i) { return 4 * (q >> 1) + 2 * (q & 1) + delta(i); }
     __device__ __forceinline__ void setup(const WRaw<T_Q6_K> &r, int, int q)
     {
         keep_raw(r);
-        const int gp = q >> 1, lq = q & 1;
+        const int gp = q >> 1;
         const float d = h2f(r.d);
         ds0 = d * (float)(int8_t)(r.sc & 0xffu);          // group gp
         ds1 = d * (float)(int8_t)((r.sc >> 8) & 0xffu);   // group gp + 2
         nb0 = -32.f * ds0;                                // fma(q, ds, -32 ds) = ds (q - 32), rounded once
         nb1 = -32.f * ds1;
         hs0 = 2u * (uint32_t)gp;
-        base = 32 * gp + 16 * lq;
     }
-    __device__ __forceinline__ void part(const WRaw<T_Q6_K> &r, int i, _Float16 *ws) const
+    __device__ __forceinline__ void part(const WRaw<T_Q6_K> &r, int i, _Float16 *dst) const
     {
-        const uint32_t ql = align_bytes(r.ql.d[i + 1], r.ql.d[i], r.sh);
-        const uint32_t qh = align_bytes(r.qh.d[i + 1], r.qh.d[i], r.sh);
-        const uint32_t q0 = opaque((ql & 0x0f0f0f0fu) | (((qh >> hs0) & 0x03030303u) << 4));
-        const uint32_t q1 = opaque(((ql >> 4) & 0x0f0f0f0fu) | (((qh >> (hs0 + 4u)) & 0x03030303u) << 4));
-        st64(ws + base + 4 * i,
-             pack_rne(__builtin_fmaf(ub0(q0), ds0, nb0), __builtin_fmaf(ub1(q0), ds0, nb0)),
-             pack_rne(__builtin_fmaf(ub2(q0), ds0, nb0), __builtin_fmaf(ub3(q0), ds0, nb0)));
-        st64(ws + base + 64 + 4 * i,
-             pack_rne(__builtin_fmaf(ub0(q1), ds1, nb1), __builtin_fmaf(ub1(q1), ds1, nb1)),
-             pack_rne(__builtin_fmaf(ub2(q1), ds1, nb1), __builtin_fmaf(ub3(q1), ds1, nb1)));
+        const bool lo = (i & 1) == 0;
+        const float ds = lo ? ds0 : ds1, nb = lo ? nb0 : nb1;
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = 2 * (i >> 1) + h;
+            const uint32_t l = align_bytes(r.ql.d[k + 1], r.ql.d[k], r.sh);
+            const uint32_t hb = align_bytes(r.qh.d[k + 1], r.qh.d[k], r.sh);
+            const uint32_t v = lo ? opaque((l & 0x0f0f0f0fu) | (((hb >> hs0) & 0x03030303u) << 4))
+                                     : opaque(((l >> 4) & 0x0f0f0f0fu) | (((hb >> (hs0 + 4u)) & 0x03030303u) << 4));
+            o[2 * h] = pack_rne(__builtin_fmaf(ub0(v), ds, nb), __builtin_fmaf(ub1(v), ds, nb));
+            o[2 * h + 1] = pack_rne(__builtin_fmaf(ub2(v), ds, nb), __builtin_fmaf(ub3(v), ds, nb));
+        }
+        st128(dst, o);
     }
 };
 
@@ -379,7 +430,7 @@ struct GemmCfg {
     // last wavefronts have none in the last slot
     static constexpr bool EVEN = UNITS % NT == 0;
     static_assert(EVEN || (UNITS % 64 == 0 && UNITS > NT * (UPT - 1)), "decode units per wavefront");
-    static constexpr int LDS_HALVES = 2 * BN * GLD;
+    static constexpr int LDS_HALVES = 2 * BN * GKT;
 };
 
 template <int T, int FM, int FN, int WM, int WN, int XD>
@@ -429,13 +480,14 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
 
     // ---- weight units of this thread
     const uint8_t *wrow[C::UPT];
-    int uq[C::UPT], ucol[C::UPT];
+    int uq[C::UPT], woff[C::UPT];
 #pragma unroll
     for (int u = 0; u < C::UPT; ++u) {
         const int id = tid + C::NT * u;
-        ucol[u] = id >> 2;
+        const int col = id >> 2;
         uq[u] = id & 3;
-        wrow[u] = w + (int64_t)min(n0 + ucol[u], n - 1) * rb;
+        wrow[u] = w + (int64_t)min(n0 + col, n - 1) * rb;
+        woff[u] = tile_off(col, Dec<T>::chunk(uq[u], 0));   // part i: ^ tile_xor(delta(i))
     }
     // slot u of this thread holds a unit (wave-uniform: units come in whole wavefronts)
     auto has = [&](int u) __attribute__((always_inline)) {
@@ -458,7 +510,9 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
             if (has(u) && (full || Fmt<T>::BE == 256 || 4 * t + uq[u] < (k >> 5))) {
                 if (i == 0)
                     dec[u].setup(wr[par][u], t, uq[u]);
-                dec[u].part(wr[par][u], i, dst + ucol[u] * GLD);
+                int wo = woff[u];
+                asm volatile("" : "+v"(wo));   // keep the XOR in the loop: hoisted, the 4 offsets pin 4 VGPRs
+                dec[u].part(wr[par][u], i, dst + (wo ^ tile_xor(Dec<T>::delta(i))));
             }
     };
 
@@ -468,7 +522,9 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    const int bro = (wn * C::NW + (lane & 15)) * GLD + 8 * (lane >> 4);   // B fragment offset
+    // B fragment of sub-step s, block j: row wn NW + 16 j + lane % 16, chunk
+    // 4 s + lane / 16 (the swizzle depends on the row only through lane % 16)
+    const int bro = tile_off(wn * C::NW + (lane & 15), lane >> 4);   // sub-step s: ^ tile_xor(4 s)
 
     // One K step t with compile-time buffer parity PAR (= t % 2).  FULL: t is
     // not among the last three steps, so every step, load and decode of the
@@ -477,16 +533,19 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
     auto tile = [&](auto par_c, auto full_c, int t) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par_c)::value;
         constexpr bool FULL = decltype(full_c)::value;
-        const _Float16 *wcur = Ws + PAR * C::BN * GLD;
-        _Float16 *wnext = Ws + (1 - PAR) * C::BN * GLD;
+        const _Float16 *wcur = Ws + PAR * C::BN * GKT;
+        _Float16 *wnext = Ws + (1 - PAR) * C::BN * GKT;
         const bool nx = FULL || t + 1 < nkt;
         // weight fragments of step s + 1 are read from LDS while the MFMAs of
         // step s run (two register sets)
         half8 bf[2][FN];
         auto read_b = [&](int s, half8 *dst) __attribute__((always_inline)) {
+            int b = bro;
+            asm volatile("" : "+v"(b));        // as for the decode stores
+            const _Float16 *src = wcur + (b ^ tile_xor(4 * s));
 #pragma unroll
             for (int j = 0; j < FN; ++j)
-                dst[j] = *(const half8 *)(wcur + bro + 16 * j * GLD + 32 * s);
+                dst[j] = *(const half8 *)(src + 16 * j * GKT);
         };
         if (FULL || GKT * t < k)
             read_b(0, bf[0]);
@@ -525,7 +584,7 @@ gemm_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const uint1
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x200, C::UPT, 0);
             }
         }
         __syncthreads();
@@ -657,7 +716,8 @@ hipError_t launch_gemm_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, cons
         const int64_t r128 = (t128 + cus - 1) / cus, r112 = (t112 + cus - 1) / cus;
         if (100 * t112 * r128 > 105 * t128 * r112)
             return launch_cfg<T, 2, 7, 8, 1, 4>(w, n, k, rb, x, m, y, s);   // 256 x 112
-        return launch_cfg<T, 2, 8, 8, 1, 4>(w, n, k, rb, x, m, y, s);       // 256 x 128
+        // Q6_K: X two sub-steps ahead, not four (16 VGPRs; four spill)
+        return launch_cfg<T, 2, 8, 8, 1, T == T_Q6_K ? 2 : 4>(w, n, k, rb, x, m, y, s);   // 256 x 128
     }
     return launch_cfg<T, 1, 4, 8, 1, 4>(w, n, k, rb, x, m, y, s);       // 128 x 64, 8 waves
 }
