@@ -34,8 +34,10 @@
 //                 registers, waves are independent and persistent, and the
 //                 weight bytes of the next row group are in flight while the
 //                 current one is decoded.
-//   gemv3_kernel  batch 1, Q4_K with n >= 2048: x in LDS (padded against
-//                 bank conflicts), 8 waves per compute unit, one row per item.
+//   gemv3_kernel  batch 1, Q4_K with n >= 2048, and Q4_0 / Q5_0 with few
+//                 (<= 1024) or many (>= 4096) rows: x in LDS (padded against
+//                 bank conflicts), 8 or 16 waves per compute unit, one row
+//                 per item.
 //   gemv2m_kernel gemv2 over a table of up to 8 problems sharing k (the
 //                 grouped entry point): one launch instead of one per matrix.
 //   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
@@ -1200,6 +1202,17 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
             // per byte): x from LDS, 8 waves per CU, one row per item
             if (T == T_Q4_K && n >= 2048)
                 return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
+            // Q4_0 / Q5_0 with few or many rows: x from LDS as well, one
+            // row per item, which spares each wave its own read of all of x
+            // from L2 (measured on MI355X, Q4_0: 256 x 2048 2.74 -> 2.64 us
+            // with 8 waves per CU, 5632 x 2048 4.78 -> 4.48 us with 16;
+            // 2048 x 2048 is no faster either way)
+            if constexpr (T == T_Q4_0 || T == T_Q5_0) {
+                if (n <= 1024)
+                    return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
+                if (n >= 4096)
+                    return launch_b1_xlds<T, 1, 16>(w, n, k, rb, x, y, s);
+            }
             return n <= 1024 ? launch_b1_regs<T, 1>(w, n, k, rb, x, y, s)
                              : launch_b1_regs<T, 2>(w, n, k, rb, x, y, s);
         }
