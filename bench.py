@@ -427,7 +427,8 @@ def sec_dequant(torch, q, steps, warmup, dev):
 
 
 def reference_bw(torch, dev):
-    """Plain fill (write only) and copy (read + write) of fp32 buffers, each
+    """Plain fill (write only), read (a sum over the buffer: reads it once
+    and writes one number) and copy (read + write) of fp32 buffers, each
     rotating over more than 400 MB, timed with events after a warm-up."""
     res = {}
     for label, nbytes in (("235MB", 14336 * 4096 * 4), ("16MB", 2048 * 2048 * 4)):
@@ -435,11 +436,14 @@ def reference_bw(torch, dev):
         cnt = max(2, int(400e6 // nbytes) + 1)
         dst = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(cnt)]
         src = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(cnt)]
-        for name, moved in (("fill", nbytes), ("copy", 2 * nbytes)):
+        sums = torch.empty(cnt, dtype=torch.float32, device=dev)
+        for name, moved in (("fill", nbytes), ("read", nbytes), ("copy", 2 * nbytes)):
             def once():
                 for i in range(cnt):
                     if name == "fill":
                         dst[i].fill_(1.0)
+                    elif name == "read":
+                        torch.sum(src[i], dim=0, out=sums[i])
                     else:
                         dst[i].copy_(src[i])
             for _ in range(3):
@@ -453,7 +457,7 @@ def reference_bw(torch, dev):
             torch.cuda.synchronize()
             t = e0.elapsed_time(e1) / 1e3 / (5 * cnt)
             res["%s_%s" % (name, label)] = {"us": round(t * 1e6, 2), "GB_s": round(moved / t / 1e9, 1)}
-        del dst, src
+        del dst, src, sums
         torch.cuda.empty_cache()
     return res
 
@@ -513,6 +517,16 @@ def main():
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
     ev_step_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
+    # spread of single passes: 20 replays, each between its own pair of events
+    singles = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        b.synchronize()
+        singles.append(a.elapsed_time(b))
+    singles.sort()
     value = tot_bytes / step_s / 1e9
     # dominant kernel: every launch of the pass is the Q4_0 GEMV; its average
     # launch duration is the event time of the pass divided by the launches
@@ -544,6 +558,8 @@ def main():
         "decode_tok_s": round(1.0 / step_s, 1),
         "eager_ms_per_step": round(eager_s * 1e3, 4),
         "event_ms_per_step": round(ev_step_s * 1e3, 4),
+        "single_pass_ms": {"median": round(0.5 * (singles[9] + singles[10]), 4), "min": round(singles[0], 4),
+                           "max": round(singles[-1], 4), "passes": len(singles)},
         "grouped_launches": grouped,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": TRAFFIC,
