@@ -980,7 +980,11 @@ gemv1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
             const int it = it0 + i;
             st[i].store(mw, lane);
             wave_lds_sync();
-            load(st[i], it + D);
+            // no refill past the wave's last item (wave-uniform): a wave does
+            // not end before its loads land, and the refill's data is unused
+            // (2048 x 5632 Q4_0: 5.55 -> 5.42 us)
+            if (it + D < nitems)
+                load(st[i], it + D);
             if (it < nitems) {     // the ring runs in whole rounds; the surplus items are reloads
                 const int rg = gw + tw * (it / nseg), seg = it % nseg;
                 const int segE = min(SEGE, k - seg * SEGE);
