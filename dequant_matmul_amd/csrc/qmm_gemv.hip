@@ -29,15 +29,15 @@
 //     round trips.
 //
 // Kernels
-//   gemv2_kernel  batch 1, k <= one segment (every projection except the
-//                 wide-k down projections): each lane holds its slice of x in
+//   gemv2_kernel  batch 1, k <= one segment (the projections that neither
+//                 gemv3 nor gemv1 takes): each lane holds its slice of x in
 //                 registers, waves are independent and persistent, and the
 //                 weight bytes of the next row group are in flight while the
 //                 current one is decoded.
-//   gemv3_kernel  batch 1, Q4_K with n >= 2048, and Q4_0 / Q5_0 with few
-//                 (<= 1024) or many (>= 4096) rows: x in LDS (padded against
-//                 bank conflicts), 8 or 16 waves per compute unit, one row
-//                 per item.
+//   gemv3_kernel  batch 1, Q4_K with n <= 1024 or n >= 2048, and Q4_0 /
+//                 Q5_0 with few (<= 1024) or many (>= 4096) rows: x in LDS
+//                 (padded against bank conflicts), 8 or 16 waves per
+//                 compute unit, one row per item.
 //   gemv2m_kernel gemv2 over a table of up to 8 problems sharing k (the
 //                 grouped entry point): one launch instead of one per matrix.
 //   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
@@ -1203,8 +1203,9 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
     if (batch == 1 && rb % 16 == 0) {
         if (k <= 64 * GemvUnit<T>::UE) {
             // Q4_K (the cheapest decode per byte, so the most rows in flight
-            // per byte): x from LDS, 8 waves per CU, one row per item
-            if (T == T_Q4_K && n >= 2048)
+            // per byte): x from LDS, 8 waves per CU, one row per item (also
+            // for 1024 x 4096: 4.38 -> 4.25 us; 2048 rows stay on gemv2)
+            if (T == T_Q4_K && (n >= 2048 || n <= 1024))
                 return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
             // Q4_0 / Q5_0 with few or many rows: x from LDS as well, one
             // row per item, which spares each wave its own read of all of x

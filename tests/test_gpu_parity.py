@@ -115,7 +115,8 @@ def test_gemv_small_and_ragged(t, batch):
 @pytest.mark.parametrize("t,n,k", [(G.Q8_0, 2048, 2048), (G.Q4_0, 2048, 5632), (G.Q4_0, 256, 2048),
                                    (G.Q4_0, 2048, 2048), (G.Q4_0, 5632, 2048), (G.Q4_0, 4099, 1952),
                                    (G.Q4_0, 1023, 96), (G.Q5_0, 5632, 2048), (G.Q5_0, 300, 2048),
-                                   (G.Q4_K, 14336, 4096), (G.Q4_K, 4096, 14336), (G.Q6_K, 4096, 14336),
+                                   (G.Q4_K, 14336, 4096), (G.Q4_K, 4096, 14336), (G.Q4_K, 1024, 4096),
+                                   (G.Q4_K, 1000, 3840), (G.Q6_K, 4096, 14336),
                                    (G.Q6_K, 1024, 4096), (G.Q5_0, 4096, 4096), (G.Q5_K, 14336, 4096),
                                    (G.Q5_K, 4096, 14336)])
 @pytest.mark.parametrize("batch", [1, 8])
