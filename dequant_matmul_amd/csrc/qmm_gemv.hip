@@ -721,15 +721,39 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int gw = blockIdx.x * NW + wave, tw = gridDim.x * NW;
+    // X_LDS: this thread's share of x is loaded into registers first, so
+    // that it is in flight together with the first weight loads (issued
+    // next), and written to LDS after them (stage_x).  Positions past k
+    // read x[0..3] and are not stored.
+    constexpr int XV = X_LDS ? (64 * UE + 4 * 64 * NW - 1) / (4 * 64 * NW) : 1;
+    f32x4 xst[XV];
     if constexpr (X_LDS) {
-        // padded layout (4 floats per unit): lanes read their unit slices at a
-        // stride of UE + 4 floats, which keeps the 128-bit reads off a single
-        // bank group
         const float *x = P.X(0);
-        for (int i = 4 * (int)threadIdx.x; i < k; i += 4 * 64 * NW)
-            *(f32x4 *)(xl + xpad<UE>(i)) = *(const f32x4 *)(x + i);
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < XV; ++j) {
+            const int e = 4 * ((int)threadIdx.x + 64 * NW * j);
+            xst[j] = *(const f32x4 *)(x + (e < k ? e : 0));
+        }
+        // keep these loads ahead of the weight loads: the wait for them
+        // before the LDS writes then leaves the weight loads in flight
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // padded layout (4 floats per unit): lanes read their unit slices at a
+    // stride of UE + 4 floats, which keeps the 128-bit reads off a single
+    // bank group.  The barrier is a raw one after this wave's LDS writes
+    // complete: a full __syncthreads() would also wait for the weight loads.
+    auto stage_x = [&]() __attribute__((always_inline)) {
+        if constexpr (X_LDS) {
+#pragma unroll
+            for (int j = 0; j < XV; ++j) {
+                const int e = 4 * ((int)threadIdx.x + 64 * NW * j);
+                if (e < k)
+                    *(f32x4 *)(xl + xpad<UE>(e)) = xst[j];
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only
+            __builtin_amdgcn_s_barrier();
+        }
+    };
     // each wave takes a contiguous run of row groups (run lengths differ by
     // at most one, so every wave has work when there are enough), so that
     // its results form contiguous runs of y (stored 64 at a time, below)
@@ -768,7 +792,8 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     int p0, r0;
     locate(0, p0, r0);
     int xp = p0;
-    load_x(xp);
+    if constexpr (!X_LDS)
+        load_x(xp);
 
     // Two items of weight bytes in flight while an item computes: three
     // prefetch register sets, the loop unrolled by three so that each has a
@@ -828,6 +853,10 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
         load(0, pr[0]);
         load(1, pr[1]);
         load(2, pr[2]);
+        if constexpr (X_LDS) {
+            stage_x();
+            load_x(xp);
+        }
         auto step = [&](auto bc, int it) __attribute__((always_inline)) {
             constexpr int B = decltype(bc)::value;
             int pp, row0;
@@ -865,6 +894,10 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
             st.load(P.W(pp), rb, it < nit ? P.N(pp) : 0, row0, 0, cpr, lane);
         };
         load(0);
+        if constexpr (X_LDS) {
+            stage_x();
+            load_x(xp);
+        }
         for (int it = 0; it < nit; ++it) {
             int pp, row0;
             locate(it, pp, row0);
