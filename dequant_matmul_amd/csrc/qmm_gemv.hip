@@ -29,19 +29,19 @@
 //     round trips.
 //
 // Kernels
-//   gemv2_kernel  batch 1, k <= one segment (the projections that neither
-//                 gemv3 nor gemv1 takes): each lane holds its slice of x in
-//                 registers, waves are independent and persistent, and the
-//                 weight bytes of the next row group are in flight while the
-//                 current one is decoded.
-//   gemv3_kernel  batch 1, Q4_K with n <= 1024 or n >= 2048, and Q4_0 /
-//                 Q5_0 with few (<= 1024) or many (>= 4096) rows: x in LDS
-//                 (padded against bank conflicts), 8 or 16 waves per
-//                 compute unit, one row per item.
-//   gemv2m_kernel gemv2 over a table of up to 8 problems sharing k (the
-//                 grouped entry point): one launch instead of one per matrix.
+//   gemv3_kernel  batch 1, k <= one segment (every projection except the
+//                 wide-k down ones): x staged once per workgroup in LDS
+//                 (padded against bank conflicts) while the first weight
+//                 loads are in flight, each lane then holds its slice of x in
+//                 registers; waves are independent and persistent, one row
+//                 per item, and the weight bytes of the next items are in
+//                 flight while the current one is decoded; 8 or 16 waves
+//                 per compute unit.
+//   gemv2m_kernel the same loop (gemv2_body) over a table of up to 8
+//                 problems sharing k (the grouped entry point), x read by
+//                 each wave from L2: one launch instead of one per matrix.
 //   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
-//                 once per workgroup; otherwise as gemv2 (two rows per item,
+//                 once per workgroup; otherwise as gemv3 (two rows per item,
 //                 one when there are too few rows to give every CU a
 //                 workgroup).
 //   gemv_kernel   batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K (and unaligned
@@ -919,16 +919,6 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     }
 }
 
-template <int T, int R>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
-gemv2_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
-             float *__restrict__ y)
-{
-    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : 4 * SegStage<T, R>::LDS_DW];
-    const OneProb P{w, x, y, n};
-    gemv2_body<T, R>(P, k, rb, ws);
-}
-
 // Batch 1, one problem, x staged in LDS, NW wavefronts per workgroup (one
 // workgroup per CU: 16 waves, 4 per SIMD, hide the weight latency).
 template <int T, int R, int NW>
@@ -1171,24 +1161,6 @@ static hipError_t launch_b1_xlds(const uint8_t *w, int64_t n, int64_t k, size_t 
 }
 
 template <int T, int R>
-static hipError_t launch_b1_regs(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
-                                 hipStream_t s)
-{
-    static std::atomic<int> slot[64];
-    const int cap = per_device_cached(slot, [] { return gemv2_cap(gemv2_kernel<T, R>); });
-    if (cap == 0)
-        return hipErrorInvalidValue;
-    const int64_t nrg = (n + R - 1) / R;
-    // mid-size matrices run best with one workgroup per CU (each wave then
-    // walks two row groups), large ones with two (measured on MI355X)
-    const int64_t lim = nrg <= 4 * (int64_t)cap ? cap / 2 : cap;
-    const int64_t want = (nrg + 3) / 4;
-    const dim3 grid((unsigned)(want < lim ? want : lim)), block(256);
-    hipLaunchKernelGGL((gemv2_kernel<T, R>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
-    return hipGetLastError();
-}
-
-template <int T, int R>
 static hipError_t launch_b1_table(const GemvProbs &P, int64_t k, size_t rb, hipStream_t s)
 {
     static std::atomic<int> slot[64];
@@ -1235,24 +1207,21 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
 {
     if (batch == 1 && rb % 16 == 0) {
         if (k <= 64 * GemvUnit<T>::UE) {
-            // Q4_K (the cheapest decode per byte, so the most rows in flight
-            // per byte): x from LDS, 8 waves per CU, one row per item (also
-            // for 1024 x 4096: 4.38 -> 4.25 us; 2048 rows stay on gemv2)
-            if (T == T_Q4_K && (n >= 2048 || n <= 1024))
-                return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
-            // Q4_0 / Q5_0 with few or many rows: x from LDS as well, one
-            // row per item, which spares each wave its own read of all of x
-            // from L2 (measured on MI355X, Q4_0: 256 x 2048 2.74 -> 2.64 us
-            // with 8 waves per CU, 5632 x 2048 4.78 -> 4.48 us with 16;
-            // 2048 x 2048 is no faster either way)
-            if constexpr (T == T_Q4_0 || T == T_Q5_0) {
-                if (n <= 1024)
-                    return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
+            // x staged once per workgroup in LDS (while the first weight
+            // loads are in flight), one row per item: 8 waves per CU, 16 for
+            // the 32-element types with at least 4096 rows.  Measured on
+            // MI355X against the same loop with x read by every wave from L2:
+            // Q4_0 256 / 2048 / 5632 x 2048: 2.64 / 3.48 / 4.46 -> 2.21 /
+            // 2.78 / 4.01 us; Q8_0 2048 x 2048 3.57 -> 3.10 us; Q6_K 1024 x
+            // 4096 and 128256 x 4096: 3.81 -> 3.67 us and 81.0 -> 78.1 us;
+            // Q5_K 1024 / 4096 / 14336 x 4096: 4.44 / 6.69 / 13.5 -> 3.49 /
+            // 4.87 / 11.2 us.
+            if constexpr (T == T_Q4_0 || T == T_Q8_0 || T == T_Q5_0) {
                 if (n >= 4096)
                     return launch_b1_xlds<T, 1, 16>(w, n, k, rb, x, y, s);
+                return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
             }
-            return n <= 1024 ? launch_b1_regs<T, 1>(w, n, k, rb, x, y, s)
-                             : launch_b1_regs<T, 2>(w, n, k, rb, x, y, s);
+            return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
         }
         if (k <= 16384) {
             // two rows per item, unless that leaves compute units without a
