@@ -152,16 +152,18 @@ class Dequant:
 
 
 class Group:
-    """Several same-type, same-k batch-1 GEMVs issued as one qmm_gemv_multi call."""
+    """Several same-type, same-k batch-1 GEMVs issued as one qmm_gemv_multi
+    call; share_x: all of them read the first one's activation (as q / k / v
+    and gate / up read one normalized hidden state in a decoder layer)."""
 
-    def __init__(self, probs):
+    def __init__(self, probs, share_x=False):
         import ctypes
         self.probs = probs
         npb = len(probs)
         self.t, self.k, self.batch = probs[0].t, probs[0].k, probs[0].batch
         self.np = npb
         self.w = (ctypes.c_void_p * npb)(*[p.w.data_ptr() for p in probs])
-        self.x = (ctypes.c_void_p * npb)(*[p.x.data_ptr() for p in probs])
+        self.x = (ctypes.c_void_p * npb)(*[(probs[0] if share_x else p).x.data_ptr() for p in probs])
         self.y = (ctypes.c_void_p * npb)(*[p.y.data_ptr() for p in probs])
         self.n = (ctypes.c_int64 * npb)(*[p.n for p in probs])
         self.name = "+".join(p.name for p in probs)
@@ -172,7 +174,7 @@ class Group:
             raise RuntimeError("gemv_multi %s: %s" % (self.name, q.status_str(st)))
 
 
-def group_layers(probs, fuse):
+def group_layers(probs, fuse, share_x=False):
     """Split a 7-projections-per-layer list into launch groups: fuse = set of
     projection-name tuples issued together (e.g. ("gate", "up"))."""
     out = []
@@ -183,7 +185,7 @@ def group_layers(probs, fuse):
             if nm in done:
                 continue
             grp = next((g for g in fuse if nm in g), (nm,))
-            out.append(Group([layer[g] for g in grp]) if len(grp) > 1 else layer[nm])
+            out.append(Group([layer[g] for g in grp], share_x) if len(grp) > 1 else layer[nm])
             done.update(grp)
     return out
 
@@ -537,9 +539,12 @@ def main():
     # (the dispatch count shimmy's pipeline page gives: 6 per layer) and
     # q|k|v + gate|up (4 per layer)
     grouped = {}
-    for label, fuse in (("6_launches_per_layer", (("gate", "up"),)),
-                        ("4_launches_per_layer", (("q", "k", "v"), ("gate", "up")))):
-        gp = group_layers(probs, fuse)
+    # (and the 4-launch grouping once more with one activation per group, as
+    # in a decoder layer: q / k / v read one x, gate / up another)
+    for label, fuse, share in (("6_launches_per_layer", (("gate", "up"),), False),
+                               ("4_launches_per_layer", (("q", "k", "v"), ("gate", "up")), False),
+                               ("4_launches_per_layer_shared_x", (("q", "k", "v"), ("gate", "up")), True)):
+        gp = group_layers(probs, fuse, share)
         gg = capture(torch, q, gp)
         tg = time_graph(torch, gg, args.steps, args.warmup)
         grouped[label] = {"launches": len(gp), "ms_per_pass": round(tg * 1e3, 4),

@@ -40,6 +40,8 @@
 //   gemv2m_kernel the same loop (gemv2_body) over a table of up to 8
 //                 problems sharing k (the grouped entry point), x read by
 //                 each wave from L2: one launch instead of one per matrix.
+//   gemv3m_kernel the table with one x shared by every problem (q / k / v,
+//                 gate / up): x staged in LDS as in gemv3.
 //   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
 //                 once per workgroup; otherwise as gemv3 (two rows per item,
 //                 one when there are too few rows to give every CU a
@@ -941,6 +943,19 @@ gemv2m_kernel(const GemvProbs Pt, int k, int64_t rb)
     gemv2_body<T, R>(P, k, rb, ws);
 }
 
+// The table of problems with one x shared by all of them (the q / k / v or
+// gate / up projections of a layer read the same activation): x staged in
+// LDS as in gemv3, one row per item.
+template <int T, int R, int NW>
+__global__ void __launch_bounds__(64 * NW)
+gemv3m_kernel(const GemvProbs Pt, int k, int64_t rb)
+{
+    __shared__ __attribute__((aligned(16))) float xl[64 * (GemvUnit<T>::UE + 4)];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : NW * SegStage<T, R>::LDS_DW];
+    const TableProbs P{Pt};
+    gemv2_body<T, R, TableProbs, NW, true>(P, k, rb, ws, xl);
+}
+
 // --------------------------------------------------------------- gemv1 --
 // Batch 1, k spanning several segments: x staged in LDS once per workgroup;
 // each wave walks items (R rows x one segment) with the weight bytes of the
@@ -1175,6 +1190,21 @@ static hipError_t launch_b1_table(const GemvProbs &P, int64_t k, size_t rb, hipS
     return hipGetLastError();
 }
 
+// Shared-x table through gemv3m: at most one workgroup per CU.
+template <int T, int NW>
+static hipError_t launch_b1_table_xlds(const GemvProbs &P, int64_t k, size_t rb, hipStream_t s)
+{
+    const int cus = device_cu_count();
+    if (cus == 0)
+        return hipErrorInvalidValue;
+    const int64_t want = ((int64_t)P.rg0[P.np] + NW - 1) / NW;
+    if (want == 0)
+        return hipSuccess;
+    const dim3 grid((unsigned)(want < cus ? want : cus)), block(64 * NW);
+    hipLaunchKernelGGL((gemv3m_kernel<T, 1, NW>), grid, block, 0, s, P, (int)k, (int64_t)rb);
+    return hipGetLastError();
+}
+
 template <int T, int R, int NW, int XK, int D>
 static hipError_t launch_b1_lds(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                                 hipStream_t s)
@@ -1273,15 +1303,27 @@ static hipError_t launch_multi_t(int np, const void *const *w, const int64_t *n,
         for (int base = 0; base < np; base += GEMV_MAXP) {
             GemvProbs P{};
             P.np = np - base < GEMV_MAXP ? np - base : GEMV_MAXP;
+            // one x for every problem of this launch: x staged once in LDS
+            // per workgroup (gemv3m), one row per item; else gemv2m
+            bool shared = true;
+            int64_t rows = 0;
+            for (int i = 0; i < P.np; ++i) {
+                shared = shared && x[base + i] == x[base];
+                rows += n[base + i];
+            }
+            const int R = shared ? 1 : 2;
             P.rg0[0] = 0;
             for (int i = 0; i < P.np; ++i) {
                 P.w[i] = (const uint8_t *)w[base + i];
                 P.x[i] = x[base + i];
                 P.y[i] = y[base + i];
                 P.n[i] = (int)n[base + i];
-                P.rg0[i + 1] = P.rg0[i] + (int)((n[base + i] + 1) / 2);
+                P.rg0[i + 1] = P.rg0[i] + (int)((n[base + i] + R - 1) / R);
             }
-            const hipError_t e = launch_b1_table<T, 2>(P, k, rb, s);
+            constexpr bool small_blocks = GemvUnit<T>::UE == 32;
+            const hipError_t e = !shared ? launch_b1_table<T, 2>(P, k, rb, s)
+                                 : small_blocks && rows >= 4096 ? launch_b1_table_xlds<T, 16>(P, k, rb, s)
+                                                                : launch_b1_table_xlds<T, 8>(P, k, rb, s);
             if (e != hipSuccess)
                 return e;
         }

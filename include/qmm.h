@@ -195,7 +195,10 @@ QMM_API int qmm_gemv(int type, const void *w, int64_t n, int64_t k,
  * w, n, x, y are host arrays of nprob entries (device pointers / row counts),
  * read during the call only.  Per problem the same conventions and errors as
  * qmm_gemv apply; n[i] == 0 problems are skipped; nprob == 0 is a no-op.
- * Results are identical to nprob separate qmm_gemv calls.
+ * Results are identical to nprob separate qmm_gemv calls.  When every x[i]
+ * of a batch-1 call is the same pointer (q, k, v or gate, up reading one
+ * activation), that x is staged once per workgroup, which is faster than
+ * distinct x pointers holding equal values.
  */
 QMM_API int qmm_gemv_multi(int type, int nprob, const void *const *w, const int64_t *n, int64_t k,
                            const float *const *x, int64_t batch, float *const *y, void *stream);

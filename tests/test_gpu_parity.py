@@ -395,3 +395,26 @@ def test_gemv_multi_matches_single_calls(t, k, ns, batch):
         if n:
             ref, absum = oracle.gemv(t, w, n, k, x)
             check_tol(got, ref, absum, GEMV_TOL, "gemv_multi")
+
+
+@pytest.mark.parametrize("t,k,ns", [(G.Q4_0, 2048, [2048, 256, 256]), (G.Q4_0, 2048, [5632, 5632]),
+                                    (G.Q4_K, 4096, [4096, 1024, 1024]), (G.Q4_K, 4096, [14336, 14336]),
+                                    (G.Q6_K, 4096, [1024, 3, 0, 700]), (G.Q8_0, 1984, [37] * 9),
+                                    (G.Q5_0, 2048, [4100, 7]), (G.Q5_K, 3840, [0, 515, 1])])
+def test_gemv_multi_shared_x_matches_single_calls(t, k, ns):
+    """A grouped call whose problems all read one x (q / k / v, gate / up)
+    stages x once per workgroup; results stay bit-identical to one qmm_gemv
+    call per problem, and each matches the oracle."""
+    say("gemv_multi shared x", G.NAMES[t], k, ns)
+    ws = [G.gen_weights(t, n, k, seed=800 + i) for i, n in enumerate(ns)]
+    x = G.gen_x(k, 1, seed=900)
+    wd = [upload(w) for w in ws]
+    xd = upload(x)
+    ys = q.gemv_multi(wd, t, ns, k, [xd] * len(ns))
+    for w, n, y, a in zip(ws, ns, ys, wd):
+        single = q.gemv(a, t, n, k, xd).cpu().numpy()
+        got = y.cpu().numpy()
+        assert np.array_equal(got, single)
+        if n:
+            ref, absum = oracle.gemv(t, w, n, k, x)
+            check_tol(got, ref, absum, GEMV_TOL, "gemv_multi shared x")
