@@ -12,6 +12,8 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -35,9 +37,7 @@ def sources() -> list[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *sources(), "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,9 +45,24 @@ def build(verbose: bool = False) -> str:
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed (%d):\n%s" % (r.returncode, err))
+        raise RuntimeError("hipcc failed (%d): %s\n%s" % (r.returncode, " ".join(cmd), err))
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile each source to an object (in parallel: the translation units
+    share no device code), then link the shared library."""
+    srcs = sources()
+    jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
+    with tempfile.TemporaryDirectory(prefix="qmm_build_") as td:
+        objs = [os.path.join(td, os.path.basename(f) + ".o") for f in srcs]
+        compile_flags = [f for f in FLAGS if f != "-shared"]
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            list(ex.map(lambda so: _run([HIPCC, *compile_flags, "-c", so[0], "-o", so[1]], verbose),
+                        zip(srcs, objs)))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -81,6 +81,19 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations
+// (lgkmcnt(0)), not for its global loads in flight (a __syncthreads() waits
+// for those too).  The builtins alone carry no memory semantics for the
+// compiler: the empty asm statements with a memory clobber keep LDS accesses
+// on their side of the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Sum over the 64 lanes of a wavefront; every lane receives the total.
 // Within each 16-lane row: DPP swaps (quad_perm [1,0,3,2], [2,3,0,1],
 // row_half_mirror, row_mirror) -- register-to-register, no LDS round trip;

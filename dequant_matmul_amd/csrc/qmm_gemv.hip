@@ -16,11 +16,13 @@
 //     row segment into LDS with fully coalesced loads (64 lanes x 16 B
 //     contiguous) and each lane reads its unit back with aligned dword reads,
 //     realigned in registers with v_alignbyte_b32.
-//   - Codes are converted with one mask per dword plus v_cvt_f32_ubyteN (the
-//     sign-extending SDWA convert for Q8_0) and accumulated in fp32 per block
-//     or sub-block; the scale is applied once per (sub-)block.  Constant code
-//     offsets (-8, -32, -dmin m) go through the per-sub-block sum of x, which
-//     all rows share.
+//   - Codes are converted with a few bit operations per dword plus the byte
+//     converts (v_cvt_f32_ubyteN, or the sign-extending SDWA convert), and
+//     every product uses the element's own weight: integer code offsets
+//     (-8, -16, -32) become signed bytes before the convert, the K-quant
+//     weights d sc q - dmin m are formed per element with one fma.  Sums are
+//     fp32 per block or sub-block; integer-code scales are applied once per
+//     (sub-)block.
 //   - Per-lane partial sums are reduced across the wavefront with cross-lane
 //     shuffles; lane 0 writes y.
 //   - Loads are issued without branches (out-of-range lanes read a valid
@@ -239,65 +241,60 @@ template <> __device__ __forceinline__ f32x4 zero_acc<f32x4>() { return f32x4{0.
 // x of run j for batch b, from LDS (padded layout) ...
 template <int T, int XS>
 struct XFromLds {
-    static constexpr bool PRE = false;   // offset sums of x computed alongside the dot
     const float *xs;
     int u;
     __device__ __forceinline__ f32x4 operator()(int j, int b) const
     {
         return *(const f32x4 *)(xs + b * XS + xpad<GemvUnit<T>::UE>(run_elem<T>(u, j)));
     }
-    __device__ __forceinline__ float sum(int, int) const { return 0.f; }
 };
 
-// Sums of x over the groups of a unit that share a constant code offset:
-// Q4_0 the block (1), Q4_K the two sub-blocks (2), Q6_K the four 16-element
-// scale groups (4); Q8_0 has no offset.
-template <int T> struct XSumCount {
-    static constexpr int N = (T == T_Q4_0 || T == T_Q5_0) ? 1 : (T == T_Q4_K || T == T_Q5_K) ? 2 : T == T_Q6_K ? 4 : 1;
-};
-
-// ... or from registers (batch 1): the lane's unit is the same for every row,
-// so its offset sums are computed once (sums()) and reused.
+// ... or from registers (batch 1): the lane's unit is the same for every row.
 template <int T>
 struct XFromRegs {
-    static constexpr bool PRE = true;
     const f32x4 *xr;
-    const float *xsum;
     __device__ __forceinline__ f32x4 operator()(int j, int) const { return xr[j]; }
-    __device__ __forceinline__ float sum(int, int g) const { return xsum[g]; }
 };
 
-template <int T>
-__device__ __forceinline__ void unit_x_sums(const f32x4 *xr, float *xs)
+// Weights of four elements with unsigned codes q_c (bytes of q): each is
+// d sc q - dmin m rounded once, exactly as the dequantizer forms it.
+__device__ __forceinline__ f32x4 wts4(uint32_t q, float dsc, float ndm)
 {
-    if constexpr (T == T_Q4_0 || T == T_Q5_0) {
-        float a = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a += sum4(xr[i]) + sum4(xr[4 + i]);
-        xs[0] = a;
-    } else if constexpr (T == T_Q4_K || T == T_Q5_K) {
-        float a = 0.f, b = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            a += sum4(xr[i]);
-            b += sum4(xr[8 + i]);
-        }
-        xs[0] = a;
-        xs[1] = b;
-    } else if constexpr (T == T_Q6_K) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float a = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a += sum4(xr[4 * g + i]);
-            xs[g] = a;
-        }
-    } else {
-        xs[0] = 0.f;
-    }
+    return f32x4{__builtin_fmaf(ub0(q), dsc, ndm), __builtin_fmaf(ub1(q), dsc, ndm),
+                 __builtin_fmaf(ub2(q), dsc, ndm), __builtin_fmaf(ub3(q), dsc, ndm)};
+}
+
+__device__ __forceinline__ float dot4_f(const f32x4 &w, const f32x4 &x, float acc)
+{
+    acc = __builtin_fmaf(w.x, x.x, acc);
+    acc = __builtin_fmaf(w.y, x.y, acc);
+    acc = __builtin_fmaf(w.z, x.z, acc);
+    acc = __builtin_fmaf(w.w, x.w, acc);
+    return acc;
+}
+
+__device__ __forceinline__ f32x4 dot4_f(const f32x4 &w, const f32x4 &x, f32x4 acc)
+{
+    acc.x = __builtin_fmaf(w.x, x.x, acc.x);
+    acc.y = __builtin_fmaf(w.y, x.y, acc.y);
+    acc.z = __builtin_fmaf(w.z, x.z, acc.z);
+    acc.w = __builtin_fmaf(w.w, x.w, acc.w);
+    return acc;
 }
 
 // Contribution of lane-unit u of R rows to acc[r][b].
+//
+// Every product is taken with the element's own weight, offset included, so
+// that the rounding error of the sums is relative to sum |w x| for any input
+// (a row of zero weights gives exactly 0):
+//   - the constant code offsets become signed integer bytes before the
+//     convert: a b-bit code q with offset 2^(b-1) is XOR-ed with 2^(b-1),
+//     which is q - 2^(b-1) in b-bit two's complement, and shifted to the top
+//     of its byte, so the sign-extending byte convert gives 2^(8-b) (q - off)
+//     exactly (Q4_0 16 (q - 8), Q5_0 8 (q - 16), Q6_K 4 (q - 32)); the power
+//     of two is folded into the block scale;
+//   - Q4_K / Q5_K weights d sc q - dmin m are formed per element with one
+//     fused multiply-add (d sc and dmin m are exact products).
 template <int T, int B, int R, class XG>
 __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const XG &xg, float (&acc)[R][B])
 {
@@ -324,15 +321,13 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d, fin(s[r][b]), acc[r][b]);
         }
-    } else if constexpr (T == T_Q4_0) {
+    } else if constexpr (T == T_Q4_0 || T == T_Q5_0) {
+        // Q4_0: bytes 16 (q - 8); Q5_0: bytes 8 (q - 16)
         AccT slo[R][B], shi[R][B];
-        float xsum[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            xsum[b] = 0.f;
+        for (int b = 0; b < B; ++b)
 #pragma unroll
             for (int r = 0; r < R; ++r) slo[r][b] = shi[r][b] = zero_acc<AccT>();
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f32x4 xl[B], xh[B];
@@ -340,83 +335,41 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             for (int b = 0; b < B; ++b) {
                 xl[b] = xg(i, b);
                 xh[b] = xg(4 + i, b);
-                if constexpr (!XG::PRE)
-                    xsum[b] += sum4(xl[b]) + sum4(xh[b]);
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t lo = opaque(raw[r].c[i] & 0x0f0f0f0fu);
-                const uint32_t hi = opaque(raw[r].c[i] & 0xf0f0f0f0u);   // 16 * code
+                uint32_t lo, hi;
+                if constexpr (T == T_Q4_0) {
+                    // 16 q with bit 7 flipped: 16 (q - 8) as int8
+                    lo = opaque(((raw[r].c[i] << 4) & 0xf0f0f0f0u) ^ 0x80808080u);
+                    hi = opaque((raw[r].c[i] & 0xf0f0f0f0u) ^ 0x80808080u);
+                } else {
+                    // 5-bit q = nibble | bit 4 from the block's word; flipping
+                    // the word's bits gives q - 16 (5-bit), moved up by 3
+                    const uint32_t c = raw[r].c[i], hn = ~raw[r].qh;
+                    lo = opaque(((c & 0x0f0f0f0fu) | bits_to_byte_bit4(hn >> (4 * i))) << 3);
+                    hi = opaque((((c >> 4) & 0x0f0f0f0fu) | bits_to_byte_bit4(hn >> (16 + 4 * i))) << 3);
+                }
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    slo[r][b] = dot4_u(lo, xl[b], slo[r][b]);
-                    shi[r][b] = dot4_u(hi, xh[b], shi[r][b]);
+                    slo[r][b] = dot4_s(lo, xl[b], slo[r][b]);
+                    shi[r][b] = dot4_s(hi, xh[b], shi[r][b]);
                 }
             }
         }
-        if constexpr (XG::PRE)
-#pragma unroll
-            for (int b = 0; b < B; ++b) xsum[b] = xg.sum(b, 0);
-        // d * sum (q - 8) x = d * (slo + shi/16 - 8 sum x)
+        constexpr float INV = T == T_Q4_0 ? 0.0625f : 0.125f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float d = h2f(raw[r].d);
+            const float d = h2f(raw[r].d) * INV;
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const float t = __builtin_fmaf(fin(shi[r][b]), 0.0625f, fin(slo[r][b]));
-                acc[r][b] = __builtin_fmaf(d, __builtin_fmaf(-8.f, xsum[b], t), acc[r][b]);
-            }
+            for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d, fin(slo[r][b]) + fin(shi[r][b]), acc[r][b]);
         }
-    } else if constexpr (T == T_Q5_0) {
-        // as Q4_0, with bit 4 of each code from the block's 32-bit word
-        AccT slo[R][B], shi[R][B];
-        float xsum[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            xsum[b] = 0.f;
-#pragma unroll
-            for (int r = 0; r < R; ++r) slo[r][b] = shi[r][b] = zero_acc<AccT>();
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f32x4 xl[B], xh[B];
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                xl[b] = xg(i, b);
-                xh[b] = xg(4 + i, b);
-                if constexpr (!XG::PRE)
-                    xsum[b] += sum4(xl[b]) + sum4(xh[b]);
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t c = raw[r].c[i], hb = raw[r].qh;
-                const uint32_t lo = opaque((c & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (4 * i)));
-                const uint32_t hi = opaque(((c >> 4) & 0x0f0f0f0fu) | bits_to_byte_bit4(hb >> (16 + 4 * i)));
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    slo[r][b] = dot4_u(lo, xl[b], slo[r][b]);
-                    shi[r][b] = dot4_u(hi, xh[b], shi[r][b]);
-                }
-            }
-        }
-        if constexpr (XG::PRE)
-#pragma unroll
-            for (int b = 0; b < B; ++b) xsum[b] = xg.sum(b, 0);
-        // d * sum (q - 16) x = d * (slo + shi - 16 sum x)
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float d = h2f(raw[r].d);
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const float t = fin(slo[r][b]) + fin(shi[r][b]);
-                acc[r][b] = __builtin_fmaf(d, __builtin_fmaf(-16.f, xsum[b], t), acc[r][b]);
-            }
-        }
-    } else if constexpr (T == T_Q5_K) {
-        // as Q4_K, with bit 4 of each code at bit 2p (low nibbles, sub-block
-        // 2p) or 2p + 1 (high nibbles) of the qh byte of its element
+    } else if constexpr (T == T_Q4_K || T == T_Q5_K) {
+        // unit = (super-block, code group p = u % 4): sub-block 2p in the low
+        // nibbles, 2p+1 in the high nibbles (Q5_K: bit 4 at bit 2p / 2p+1 of
+        // the qh byte of its element)
         const int p = u & 3;
-        float dsc0[R], dsc1[R], dm0[R], dm1[R];
+        float dsc0[R], dsc1[R], ndm0[R], ndm1[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             uint32_t sc0, m0, sc1, m1;
@@ -424,18 +377,16 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             q4k_scale_min(raw[r].hd.y, raw[r].hd.z, raw[r].hd.w, 2 * p + 1, sc1, m1);
             const float d = h2f(raw[r].hd.x & 0xffffu), dmin = h2f(raw[r].hd.x >> 16);
             dsc0[r] = d * (float)sc0;
-            dsc1[r] = d * (float)sc1;
-            dm0[r] = dmin * (float)m0;
-            dm1[r] = dmin * (float)m1;
+            // Q4_K high nibbles convert as 16 q
+            dsc1[r] = T == T_Q4_K ? d * (float)sc1 * 0.0625f : d * (float)sc1;
+            ndm0[r] = -(dmin * (float)m0);
+            ndm1[r] = -(dmin * (float)m1);
         }
         AccT s0[R][B], s1[R][B];
-        float x0[B], x1[B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            x0[b] = x1[b] = 0.f;
+        for (int b = 0; b < B; ++b)
 #pragma unroll
             for (int r = 0; r < R; ++r) s0[r][b] = s1[r][b] = zero_acc<AccT>();
-        }
         const uint32_t sh0 = 2u * (uint32_t)p;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -444,112 +395,42 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             for (int b = 0; b < B; ++b) {
                 xl[b] = xg(i, b);
                 xh[b] = xg(8 + i, b);
-                if constexpr (!XG::PRE) {
-                    x0[b] += sum4(xl[b]);
-                    x1[b] += sum4(xh[b]);
-                }
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t c = raw[r].c[i], hb = raw[r].h[i];
-                const uint32_t lo = opaque((c & 0x0f0f0f0fu) | (((hb >> sh0) & 0x01010101u) << 4));
-                const uint32_t hi = opaque(((c >> 4) & 0x0f0f0f0fu) | (((hb >> (sh0 + 1u)) & 0x01010101u) << 4));
+                uint32_t lo, hi;
+                if constexpr (T == T_Q4_K) {
+                    lo = opaque(raw[r].c[i] & 0x0f0f0f0fu);
+                    hi = opaque(raw[r].c[i] & 0xf0f0f0f0u);
+                } else {
+                    const uint32_t c = raw[r].c[i], hb = raw[r].h[i];
+                    lo = opaque((c & 0x0f0f0f0fu) | (((hb >> sh0) & 0x01010101u) << 4));
+                    hi = opaque(((c >> 4) & 0x0f0f0f0fu) | (((hb >> (sh0 + 1u)) & 0x01010101u) << 4));
+                }
+                const f32x4 wl = wts4(lo, dsc0[r], ndm0[r]), wh = wts4(hi, dsc1[r], ndm1[r]);
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
-                    s0[r][b] = dot4_u(lo, xl[b], s0[r][b]);
-                    s1[r][b] = dot4_u(hi, xh[b], s1[r][b]);
+                    s0[r][b] = dot4_f(wl, xl[b], s0[r][b]);
+                    s1[r][b] = dot4_f(wh, xh[b], s1[r][b]);
                 }
             }
         }
-        if constexpr (XG::PRE)
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                x0[b] = xg.sum(b, 0);
-                x1[b] = xg.sum(b, 1);
-            }
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float t = dsc0[r] * fin(s0[r][b]);
-                t = __builtin_fmaf(dsc1[r], fin(s1[r][b]), t);
-                t = __builtin_fmaf(-dm0[r], x0[b], t);
-                t = __builtin_fmaf(-dm1[r], x1[b], t);
-                acc[r][b] += t;
-            }
-    } else if constexpr (T == T_Q4_K) {
-        // unit = (super-block, code group p = u % 4): sub-block 2p in the low
-        // nibbles, 2p+1 in the high nibbles
-        const int p = u & 3;
-        float dsc0[R], dsc1[R], dm0[R], dm1[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            uint32_t sc0, m0, sc1, m1;
-            q4k_scale_min(raw[r].hd.y, raw[r].hd.z, raw[r].hd.w, 2 * p, sc0, m0);
-            q4k_scale_min(raw[r].hd.y, raw[r].hd.z, raw[r].hd.w, 2 * p + 1, sc1, m1);
-            const float d = h2f(raw[r].hd.x & 0xffffu), dmin = h2f(raw[r].hd.x >> 16);
-            dsc0[r] = d * (float)sc0;
-            dsc1[r] = d * (float)sc1 * 0.0625f;   // high nibbles convert as 16 q
-            dm0[r] = dmin * (float)m0;
-            dm1[r] = dmin * (float)m1;
-        }
-        AccT s0[R][B], s1[R][B];
-        float x0[B], x1[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            x0[b] = x1[b] = 0.f;
-#pragma unroll
-            for (int r = 0; r < R; ++r) s0[r][b] = s1[r][b] = zero_acc<AccT>();
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            f32x4 xl[B], xh[B];
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                xl[b] = xg(i, b);
-                xh[b] = xg(8 + i, b);
-                if constexpr (!XG::PRE) {
-                    x0[b] += sum4(xl[b]);
-                    x1[b] += sum4(xh[b]);
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const uint32_t lo = opaque(raw[r].c[i] & 0x0f0f0f0fu);
-                const uint32_t hi = opaque(raw[r].c[i] & 0xf0f0f0f0u);
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    s0[r][b] = dot4_u(lo, xl[b], s0[r][b]);
-                    s1[r][b] = dot4_u(hi, xh[b], s1[r][b]);
-                }
-            }
-        }
-        if constexpr (XG::PRE)
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                x0[b] = xg.sum(b, 0);
-                x1[b] = xg.sum(b, 1);
-            }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float t = dsc0[r] * fin(s0[r][b]);
-                t = __builtin_fmaf(dsc1[r], fin(s1[r][b]), t);
-                t = __builtin_fmaf(-dm0[r], x0[b], t);
-                t = __builtin_fmaf(-dm1[r], x1[b], t);
-                acc[r][b] += t;
-            }
+            for (int b = 0; b < B; ++b) acc[r][b] += fin(s0[r][b]) + fin(s1[r][b]);
     } else {  // Q6_K
         // unit = (super-block, half h, l-range 16 hf .. 16 hf + 15): for each
         // g the 16 elements 128h + 32g + 16hf + i belong to sub-block
         // 8h + 2g + hf; low nibble in ql (g = 0/2 in qa, 1/3 in qb), high bits
-        // at bit 2g of qh
+        // at bit 2g of qh.  Bytes 4 (q - 32): the low 4 bits of q at bits 2..5,
+        // the high 2 bits at 6..7 with bit 5 of q flipped (qh XOR 0b10 per
+        // 2-bit field)
         const int hf = u & 1;
         float dsc[R][4];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float d = h2f(raw[r].d);
+            const float d = h2f(raw[r].d) * 0.25f;
             const uint32_t sh = 8u * hf;
             dsc[r][0] = d * (float)(int8_t)(raw[r].sc[0] >> sh);          // scale 8h + hf
             dsc[r][1] = d * (float)(int8_t)(raw[r].sc[0] >> (16 + sh));   // scale 8h + 2 + hf
@@ -557,45 +438,33 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             dsc[r][3] = d * (float)(int8_t)(raw[r].sc[1] >> (16 + sh));   // scale 8h + 6 + hf
         }
         AccT s[R][B][4];
-        float xgs[B][4];
 #pragma unroll
         for (int b = 0; b < B; ++b)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                xgs[b][g] = 0.f;
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int r = 0; r < R; ++r) s[r][b][g] = zero_acc<AccT>();
-            }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 f32x4 xv[B];
 #pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    xv[b] = xg(4 * g + i, b);
-                    if constexpr (!XG::PRE)
-                        xgs[b][g] += sum4(xv[b]);
-                }
+                for (int b = 0; b < B; ++b) xv[b] = xg(4 * g + i, b);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const uint32_t a = raw[r].qa[i], bq = raw[r].qb[i], hb = raw[r].qh[i];
+                    const uint32_t a = raw[r].qa[i], bq = raw[r].qb[i], hx = raw[r].qh[i] ^ 0xaaaaaaaau;
                     uint32_t q;
-                    if (g == 0) q = (a & 0x0f0f0f0fu) | ((hb & 0x03030303u) << 4);
-                    else if (g == 1) q = (bq & 0x0f0f0f0fu) | ((hb & 0x0c0c0c0cu) << 2);
-                    else if (g == 2) q = ((a >> 4) & 0x0f0f0f0fu) | (hb & 0x30303030u);
-                    else q = ((bq >> 4) & 0x0f0f0f0fu) | ((hb >> 2) & 0x30303030u);
+                    if (g == 0) q = ((a << 2) & 0x3c3c3c3cu) | ((hx << 6) & 0xc0c0c0c0u);
+                    else if (g == 1) q = ((bq << 2) & 0x3c3c3c3cu) | ((hx << 4) & 0xc0c0c0c0u);
+                    else if (g == 2) q = ((a >> 2) & 0x3c3c3c3cu) | ((hx << 2) & 0xc0c0c0c0u);
+                    else q = ((bq >> 2) & 0x3c3c3c3cu) | (hx & 0xc0c0c0c0u);
                     q = opaque(q);
 #pragma unroll
-                    for (int b = 0; b < B; ++b) s[r][b][g] = dot4_u(q, xv[b], s[r][b][g]);
+                    for (int b = 0; b < B; ++b) s[r][b][g] = dot4_s(q, xv[b], s[r][b][g]);
                 }
             }
         }
-        if constexpr (XG::PRE)
-#pragma unroll
-            for (int b = 0; b < B; ++b)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) xgs[b][g] = xg.sum(b, g);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -603,7 +472,7 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
                 float t = 0.f;
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    t = __builtin_fmaf(dsc[r][g], __builtin_fmaf(-32.f, xgs[b][g], fin(s[r][b][g])), t);
+                    t = __builtin_fmaf(dsc[r][g], fin(s[r][b][g]), t);
                 acc[r][b] += t;
             }
     }
@@ -752,8 +621,7 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
                 if (e < k)
                     *(f32x4 *)(xl + xpad<UE>(e)) = xst[j];
             }
-            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only
-            __builtin_amdgcn_s_barrier();
+            lds_barrier();
         }
     };
     // each wave takes a contiguous run of row groups (run lengths differ by
@@ -769,23 +637,21 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     // problem and first row of item it (past the end: the last item)
     auto locate = [&](int it, int &pp, int &row0) __attribute__((always_inline)) {
         it = min(it, max(nit - 1, 0));
-        const int rg = rgs + it;
+        const int rg = min(rgs + it, nrg - 1);   // a wave with no item: the last row group
         pp = P.find(rg);
         row0 = (rg - P.rg_begin(pp)) * R;
     };
 
-    // this lane's slice of x for the current problem, and its offset sums
+    // this lane's slice of x for the current problem
     f32x4 xr[NRUN];
-    float xsum[XSumCount<T>::N];
     auto load_x = [&](int pp) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < NRUN; ++j) {
             const int e = active ? run_elem<T>(lane, j) : 0;
             xr[j] = X_LDS ? *(const f32x4 *)(xl + xpad<UE>(e)) : *(const f32x4 *)(P.X(pp) + e);
         }
-        unit_x_sums<T>(xr, xsum);
     };
-    const XFromRegs<T> xg{xr, xsum};
+    const XFromRegs<T> xg{xr};
 
     float acc[R][1];
 #pragma unroll
@@ -1300,25 +1166,38 @@ static hipError_t launch_multi_t(int np, const void *const *w, const int64_t *n,
                                  const float *const *x, int batch, float *const *y, hipStream_t s)
 {
     if (batch == 1 && rb % 16 == 0 && k <= 64 * GemvUnit<T>::UE) {
-        for (int base = 0; base < np; base += GEMV_MAXP) {
+        // empty problems are left out of the tables: every table entry then
+        // has rows (and a weight pointer), so a wave with no item of its own,
+        // whose dummy loads read the first bytes of the last problem, never
+        // meets an empty one (whose w may be NULL)
+        int live[GEMV_MAXP];
+        int i0 = 0;
+        while (i0 < np) {
+            int cnt = 0;
+            for (; i0 < np && cnt < GEMV_MAXP; ++i0)
+                if (n[i0] > 0)
+                    live[cnt++] = i0;
+            if (cnt == 0)
+                break;
             GemvProbs P{};
-            P.np = np - base < GEMV_MAXP ? np - base : GEMV_MAXP;
+            P.np = cnt;
             // one x for every problem of this launch: x staged once in LDS
             // per workgroup (gemv3m), one row per item; else gemv2m
             bool shared = true;
             int64_t rows = 0;
             for (int i = 0; i < P.np; ++i) {
-                shared = shared && x[base + i] == x[base];
-                rows += n[base + i];
+                shared = shared && x[live[i]] == x[live[0]];
+                rows += n[live[i]];
             }
             const int R = shared ? 1 : 2;
             P.rg0[0] = 0;
             for (int i = 0; i < P.np; ++i) {
-                P.w[i] = (const uint8_t *)w[base + i];
-                P.x[i] = x[base + i];
-                P.y[i] = y[base + i];
-                P.n[i] = (int)n[base + i];
-                P.rg0[i + 1] = P.rg0[i] + (int)((n[base + i] + R - 1) / R);
+                const int j = live[i];
+                P.w[i] = (const uint8_t *)w[j];
+                P.x[i] = x[j];
+                P.y[i] = y[j];
+                P.n[i] = (int)n[j];
+                P.rg0[i + 1] = P.rg0[i] + (int)((n[j] + R - 1) / R);
             }
             constexpr bool small_blocks = GemvUnit<T>::UE == 32;
             const hipError_t e = !shared ? launch_b1_table<T, 2>(P, k, rb, s)

@@ -8,20 +8,24 @@
 // 256 weights is one 16 x 16 x 256 product:
 //
 //   A (16 x 256, fp16): activation rows.  Row 2b holds the high part of
-//     x[b] * 2^sh, row 2b+1 the remainder (both fp16, round to nearest even),
-//     so hi + lo carries about 22 significant bits of the fp32 input.  sh is
-//     a power of two per (row b, super-block) that puts the block's largest
-//     |x| in [2^14, 2^15): no fp16 overflow, and the remainder stays normal
-//     for every element within 2^-17 of the largest.
-//   B (256 x 16, fp16): 16 weight rows, decoded to code x sub-block scale --
-//     q * sc for Q4_K (at most 945), (q - 32) * scale for Q6_K (at most 2048
-//     in magnitude).  Both are integers that fp16 holds exactly, formed by one
-//     fused fp16 multiply-add from a biased code.
+//     x[b] * 2^sh, row 2b+1 the remainder times 2^11 (both fp16, round to
+//     nearest even), so hi + 2^-11 lo carries about 22 significant bits of
+//     the fp32 input.  sh is a power of two per (row b, super-block) that puts
+//     the block's largest |x| in [2^14, 2^15): no fp16 overflow, and both
+//     parts stay normal for every element down to 2^-29 of the largest.
+//   B (256 x 16, fp16): 16 weight rows.  Q6_K: (q - 32) * scale, an integer
+//     of magnitude at most 2048 that fp16 holds exactly, formed by one fused
+//     fp16 multiply-add from a biased code; the super-block scale d is applied
+//     to the fp32 sums.  Q4_K: the weight d sc q - dmin m itself, formed per
+//     element in fp32 exactly as the dequantizer forms it (after a power of
+//     two 2^s per super-block that keeps it below 2^15), and split into
+//     hi = fp16(w) and lo = fp16((w - hi) 2^11): two B operands, whose sum
+//     holds every weight of the block to 22 bits (exactly when d and dmin lie
+//     within 2^8 of each other).  No cancellation happens after a rounding:
+//     a row of zero weights gives exactly 0.
 //   C (16 x 16, fp32): the sum over the super-block; then, per row j and
-//     batch b, y[b][j] += 2^-sh * (d * (C[2b][j] + C[2b+1][j])) in fp32 --
-//     the super-block scale d (and for Q4_K the dmin * sum_j m_j X_j term,
-//     one more 16x16x16 product of the eight 6-bit mins against the
-//     activation sums of the eight sub-blocks) never passes through fp16.
+//     batch b, y[b][j] += 2^-sh (C_hi + 2^-11 C_lo) (Q6_K: times d; Q4_K:
+//     both weight parts, times 2^-s) in fp32.
 //
 // Block layouts: Q4_K fp16 d, fp16 dmin, 12 bytes of packed 6-bit scales and
 // mins, 128 code bytes (sub-block j of 32: nibble j%2 of bytes 32(j/2)..+31);
@@ -88,7 +92,6 @@ __device__ __forceinline__ uint32_t byte_pair(uint32_t hb4, uint32_t v, uint32_t
 //         128(G/2) + 32g' + 16(G%2) + 0..15 (lane-local index 16g' + l).
 struct XFrag {
     h8 a[8];      // A operands of the 8 MFMAs of the super-block
-    h4 a2;        // Q4_K: sub-block sums (min term), 16x16x16 A operand
     float xs0;    // 2^-sh of batch rows 2G and 2G+1 (C layout of this lane)
     float xs1;
 };
@@ -131,8 +134,9 @@ __device__ __forceinline__ void convert_x(fl4 v[16], XFrag &f)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             v[q][c] = __builtin_amdgcn_ldexpf(v[q][c], sh);
-    // row 2b keeps the fp16 value, row 2b+1 the fp16 of the remainder
-    const float pm = (r & 1) ? 1.f : 0.f;
+    // row 2b keeps the fp16 value, row 2b+1 the fp16 of the remainder times
+    // 2^11 (the remainder is exact in fp32, at most 16 in magnitude)
+    const float pm = (r & 1) ? 1.f : 0.f, ps = (r & 1) ? 2048.f : 1.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         uint32_t o[4];
@@ -141,31 +145,9 @@ __device__ __forceinline__ void convert_x(fl4 v[16], XFrag &f)
             const int j0 = 8 * i + (pr & 1) + 4 * (pr >> 1), j1 = j0 + 2;
             const float a = vget(v, j0), b = vget(v, j1);
             const h2 h = as_h2(pk_rne(a, b));
-            o[pr] = pk_rne(fmaf(-pm, (float)h[0], a), fmaf(-pm, (float)h[1], b));
+            o[pr] = pk_rne(fmaf(-pm, (float)h[0], a) * ps, fmaf(-pm, (float)h[1], b) * ps);
         }
         f.a[i] = __builtin_bit_cast(h8, (u32x4){o[0], o[1], o[2], o[3]});
-    }
-    if (T == T_Q4_K) {
-        // sums of sub-blocks 2G and 2G+1 (of the scaled values)
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            s0 += (v[q][0] + v[q][1]) + (v[q][2] + v[q][3]);
-            s1 += (v[q + 8][0] + v[q + 8][1]) + (v[q + 8][2] + v[q + 8][3]);
-        }
-        // 16x16x16 A operand, lane (r, G): k slots 4G..4G+3 of row r.  Row 2b:
-        // slots 0..7 = high parts of the eight sums, 8..15 = remainders; row
-        // 2b+1 = 0.  Sums are below 2^20; the factor 2^-6 keeps them in fp16.
-        const int src = 32 * (G & 1) + r;     // lanes holding sub-blocks 4(G&1) .. +3
-        const float x0 = __shfl(s0, src) * 0x1p-6f, x1 = __shfl(s1, src) * 0x1p-6f;
-        const float x2 = __shfl(s0, src + 16) * 0x1p-6f, x3 = __shfl(s1, src + 16) * 0x1p-6f;
-        const uint32_t h01 = pk_rne(x0, x1), h23 = pk_rne(x2, x3);
-        const h2 a01 = as_h2(h01), a23 = as_h2(h23);
-        const uint32_t l01 = pk_rne(x0 - (float)a01[0], x1 - (float)a01[1]);
-        const uint32_t l23 = pk_rne(x2 - (float)a23[0], x3 - (float)a23[1]);
-        const bool odd = (r & 1) != 0, lo = G >= 2;
-        const uint32_t w0 = odd ? 0u : (lo ? l01 : h01), w1 = odd ? 0u : (lo ? l23 : h23);
-        f.a2 = __builtin_bit_cast(h4, (uint32_t __attribute__((ext_vector_type(2)))){w0, w1});
     }
     const float xs = __builtin_amdgcn_ldexpf(1.f, -sh);
     f.xs0 = __shfl(xs, 4 * G);        // row 4G   = batch 2G
@@ -258,35 +240,37 @@ __device__ __forceinline__ void sb_dot<T_Q4_K>(const WRawB<T_Q4_K> &r, const XFr
     const uint32_t mlo = hz & 0x3f3f3f3fu;
     const uint32_t mhi = ((hw >> 4) & 0x0f0f0f0fu) | ((hz >> 2) & 0x30303030u);
     const uint32_t sc = (g >= 2 ? schi : sclo) >> (16 * (g & 1));   // bytes: sc_2g, sc_2g+1
-    const uint32_t m4 = (g & 1) ? mhi : mlo;                        // mins 4(g&1) .. +3
-    const h2 k1024 = h2c(1024.f), kn1024 = h2c(-1024.f);
-    const h2 sa = as_h2(byte_pair(0x64646464u, sc, 0x04000400u)) - k1024;   // (sc_2g, sc_2g)
-    const h2 sb = as_h2(byte_pair(0x64646464u, sc, 0x04010401u)) - k1024;   // (sc_2g+1, sc_2g+1)
-    const h2 na = sa * kn1024, nb = sb * kn1024;
+    const uint32_t mm = (g >= 2 ? mhi : mlo) >> (16 * (g & 1));     // bytes: m_2g, m_2g+1
+    // 2^s with |w| 2^s < 1024 max(|d|, |dmin|) 2^s <= 2^15
+    const float d = h2f(r.hd.x & 0xffffu), dmin = h2f(r.hd.x >> 16);
+    const int s = 5 - __builtin_amdgcn_frexp_expf(fmaxf(fabsf(d), fabsf(dmin)));
+    const float ds = __builtin_amdgcn_ldexpf(d, s), dms = __builtin_amdgcn_ldexpf(dmin, s);
+    // d sc and dmin m (times 2^s) are exact products
+    const float dsc0 = ds * ub0(sc), dsc1 = ds * ub1(sc);
+    const float ndm0 = -(dms * ub0(mm)), ndm1 = -(dms * ub1(mm));
     const uint32_t D[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
-    fl4 c = {0.f, 0.f, 0.f, 0.f};
+    fl4 ch = {0.f, 0.f, 0.f, 0.f}, cl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int t0 = 2 * (i & 3), ns = i < 4 ? 0 : 4;
-        const h2 s2 = i < 4 ? sa : sb, n2 = i < 4 ? na : nb;
-        uint32_t o[4];
+        const float dsc = i < 4 ? dsc0 : dsc1, ndm = i < 4 ? ndm0 : ndm1;
+        uint32_t oh[4], ol[4];
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-            const uint32_t dw = D[t0 + (pr >> 1)] >> (ns + 8 * (pr & 1));
-            const h2 code = as_h2((dw & 0x000f000fu) | 0x64006400u);      // 1024 + q
-            o[pr] = as_u(__builtin_elementwise_fma(code, s2, n2));        // q * sc, exact
+            const uint32_t q = (D[t0 + (pr >> 1)] >> (ns + 8 * (pr & 1))) & 0x000f000fu;   // codes in bytes 0, 2
+            const float w0 = fmaf(ub0(q), dsc, ndm), w1 = fmaf(ub2(q), dsc, ndm);           // 2^s w, one rounding
+            oh[pr] = pk_rne(w0, w1);
+            const h2 h = as_h2(oh[pr]);
+            ol[pr] = pk_rne((w0 - (float)h[0]) * 2048.f, (w1 - (float)h[1]) * 2048.f);     // exact remainders
         }
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){o[0], o[1], o[2], o[3]}),
-                                                   c, 0, 0, 0);
+        ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){oh[0], oh[1], oh[2], oh[3]}),
+                                                    ch, 0, 0, 0);
+        cl = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){ol[0], ol[1], ol[2], ol[3]}),
+                                                    cl, 0, 0, 0);
     }
-    const uint32_t m01 = as_u(as_h2(byte_pair(0x64646464u, m4, 0x04010400u)) - k1024);
-    const uint32_t m23 = as_u(as_h2(byte_pair(0x64646464u, m4, 0x04030402u)) - k1024);
-    const fl4 c2 = __builtin_amdgcn_mfma_f32_16x16x16f16(
-        f.a2, __builtin_bit_cast(h4, (uint32_t __attribute__((ext_vector_type(2)))){m01, m23}),
-        (fl4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    const float d = h2f(r.hd.x & 0xffffu), dm = h2f(r.hd.x >> 16) * 64.f;
-    acc0 = fmaf(f.xs0, fmaf(d, c[0] + c[1], -dm * c2[0]), acc0);
-    acc1 = fmaf(f.xs1, fmaf(d, c[2] + c[3], -dm * c2[2]), acc1);
+    const float u = __builtin_amdgcn_ldexpf(1.f, -s);
+    acc0 = fmaf(f.xs0 * u, fmaf(0x1p-11f, fmaf(0x1p-11f, cl[1], cl[0]), fmaf(0x1p-11f, ch[1], ch[0])), acc0);
+    acc1 = fmaf(f.xs1 * u, fmaf(0x1p-11f, fmaf(0x1p-11f, cl[3], cl[2]), fmaf(0x1p-11f, ch[3], ch[2])), acc1);
 }
 
 template <>
@@ -336,8 +320,8 @@ __device__ __forceinline__ void sb_dot<T_Q6_K>(const WRawB<T_Q6_K> &r, const XFr
                                                    c, 0, 0, 0);
     }
     const float d = h2f(r.d);
-    acc0 = fmaf(f.xs0 * d, c[0] + c[1], acc0);
-    acc1 = fmaf(f.xs1 * d, c[2] + c[3], acc1);
+    acc0 = fmaf(f.xs0 * d, fmaf(0x1p-11f, c[1], c[0]), acc0);
+    acc1 = fmaf(f.xs1 * d, fmaf(0x1p-11f, c[3], c[2]), acc1);
 }
 
 // ------------------------------------------------------------------ kernel --
@@ -479,8 +463,6 @@ template <> struct RawLoads<T_Q6_K> { static constexpr int N = 9; };
 // s_waitcnt with only the vector memory counter limited to n (gfx9 encoding:
 // vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 #define QMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
-// LDS operations of this wave complete (vmcnt and expcnt untouched).
-#define QMM_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xc07f)
 
 template <int T, bool TWO, int D>
 __device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n, int k, int64_t rb,
@@ -544,8 +526,7 @@ __device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n,
         }
         // cross-wave sum of these D tiles (raw barriers: no wait for the
         // weight loads in flight)
-        QMM_WAIT_LGKM0();
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();
         const int nt = min(D, t_count - t);
         if ((int)threadIdx.x < nt * 64) {
             const int j = threadIdx.x >> 6, ln = threadIdx.x & 63;
@@ -561,8 +542,7 @@ __device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n,
                     y[(int64_t)(b0 + 1) * n + row] = s[1];
             }
         }
-        QMM_WAIT_LGKM0();
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();
     }
 }
 
@@ -611,8 +591,7 @@ gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const flo
         for (int t = 0; t < t_count; t += D) {
             for (int j = 0; j < D; ++j)
                 red[j][wave][lane] = (fl2){0.f, 0.f};
-            QMM_WAIT_LGKM0();
-            __builtin_amdgcn_s_barrier();
+            lds_barrier();
             const int nt = min(D, t_count - t);
             if ((int)threadIdx.x < nt * 64) {
                 const int j = threadIdx.x >> 6, ln = threadIdx.x & 63;
@@ -627,8 +606,7 @@ gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const flo
                         y[(int64_t)(b0 + 1) * n + row] = s[1];
                 }
             }
-            QMM_WAIT_LGKM0();
-            __builtin_amdgcn_s_barrier();
+            lds_barrier();
         }
     }
 }

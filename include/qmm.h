@@ -62,6 +62,11 @@
  *     unrelated work on the stream are not reported here.
  *   - Empty problems (n == 0, or batch / m == 0) return QMM_OK and enqueue
  *     nothing; k == 0 with n > 0 writes zeros to the output (empty sums).
+ *     This is deliberate, not an argument error: an empty matrix product is
+ *     well defined, and callers whose row or token counts vary need no
+ *     special case.  Negative sizes are errors.
+ *   - Block types are passed as int (the qmm_type values) and streams as
+ *     void *, so that this header needs no HIP header.
  */
 #ifndef QMM_H
 #define QMM_H
@@ -172,12 +177,21 @@ QMM_API int qmm_quantize_f16(int type, const uint16_t *x, int64_t n, int64_t k, 
  * Decode GEMV: y[b][j] = sum_i w[j][i] * x[b][i] for b < batch, j < n.
  * x: fp32 [batch][k], y: fp32 [batch][n], 1 <= batch <= 8 (batch 0 = empty).
  * Weights are read once from the quantized bytes and decoded in registers.
- * Batch 1 (all types) and batch 2..8 of Q8_0 / Q4_0: fp32 products and sums.
- * Batch 2..8 of Q4_K / Q6_K run on the fp16 matrix cores: per 256-element
- * block and activation row, x is scaled by a power of two and split into
- * two fp16 parts (about 22 significant bits), the weights enter as exact
- * fp16 integers (code x sub-block scale), sums are fp32 and the block
- * scales are applied in fp32; x must be finite.  All paths are
+ * Every product uses the element's own weight (integer code offsets are
+ * applied to the code before the multiply, K-quant weights d sc q - dmin m
+ * are formed per element), so there is no cancellation after a rounding:
+ * |y - exact| <= 2e-5 * sum_i |w[j][i] x[b][i]| for every output, and a row
+ * of zero weights gives exactly 0.
+ * Batch 1 (all types) and batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K: fp32
+ * products and sums.  Batch 2..8 of Q4_K / Q6_K run on the fp16 matrix
+ * cores: per 256-element block and activation row, x is scaled by a power
+ * of two and split into two fp16 parts (about 22 significant bits); Q6_K
+ * weights enter as exact fp16 integers (code x sub-block scale), Q4_K
+ * weights as two fp16 parts of the fp32 weight; sums are fp32.  On that
+ * path an element of x smaller than about 2^-34 of the largest |x| of its
+ * 256-element block keeps an absolute error of about 2^-50 of that largest
+ * value (not a relative one): the bound above can fail only for rows whose
+ * sum is carried by such elements.  x must be finite.  All paths are
  * deterministic.  (dotLLM "GPU Inference", Custom Kernels table:
  * quantized_gemv_* operating directly on quantized weights; the decode path
  * is memory-bandwidth bound.)

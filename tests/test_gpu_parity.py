@@ -334,18 +334,24 @@ def test_gemm_one_hot_subnormal_scales(t):
         assert np.array_equal(got[r], W16[:, c]), (r, c)
 
 
+# every 8th row of M plus the edges: at least one row of every 16-row wave
+# slice of every M tile, whatever the tile shape
+GEMM_ROWS = sorted(set(range(0, 512, 8)) | set(range(7, 512, 16)) | {1, 511})
+
+
 @pytest.mark.parametrize("t,n", [(G.Q8_0, 14336), (G.Q8_0, 4096), (G.Q4_K, 14336), (G.Q4_K, 4096),
                                  (G.Q4_0, 4096), (G.Q6_K, 4096), (G.Q5_0, 4096), (G.Q5_K, 14336),
-                                 (G.Q6_K, 14336), (G.Q4_K, 14296), (G.Q8_0, 14200)])   # 112-column tiles, ragged n
+                                 (G.Q6_K, 14336), (G.Q4_K, 14296), (G.Q8_0, 14200),   # ragged n
+                                 (G.Q4_0, 14336), (G.Q5_0, 14336), (G.Q5_K, 4096)]
+                         + [(t, 16384) for t in TYPES])
 def test_gemm_prefill_workload_shapes(t, n):
     m, k = G.PREFILL_M, 4096
     say("gemm full", G.NAMES[t], m, n, k)
     w = G.gen_weights(t, n, k, seed=13)
     X = G.gen_x_f16(m, k, seed=14)
     got = q.gemm_prefill(upload(w), t, n, k, upload(X)).cpu().numpy()
-    rows = [0, 1, 127, 128, 255, 300, 510, 511]
-    ref, absum = oracle.gemm(t, w, n, k, X, rows=rows)
-    say("  worst relative error", check_tol(got[rows], ref, absum, GEMM_TOL, "gemm full"))
+    ref, absum = oracle.gemm(t, w, n, k, X, rows=GEMM_ROWS)
+    say("  worst relative error", check_tol(got[GEMM_ROWS], ref, absum, GEMM_TOL, "gemm full"))
 
 
 @pytest.mark.parametrize("t", [G.Q4_K, G.Q6_K])
@@ -375,9 +381,12 @@ def test_native_library_loaded():
 
 # ------------------------------------------------------------ gemv_multi ---
 
+# [700, 0] and [37] * 7 + [0]: a trailing empty problem (its weight tensor
+# is empty, a null pointer) while waves outnumber the row groups
 @pytest.mark.parametrize("t,k,ns", [(G.Q4_K, 4096, [4096, 1024, 1024]), (G.Q4_0, 2048, [5632, 5632]),
                                     (G.Q6_K, 4096, [1024, 3, 0, 700]), (G.Q8_0, 2048, [37] * 9),
-                                    (G.Q4_K, 14336, [300, 200])])
+                                    (G.Q4_K, 14336, [300, 200]), (G.Q4_0, 2048, [700, 0]),
+                                    (G.Q8_0, 2048, [37] * 7 + [0])])
 @pytest.mark.parametrize("batch", [1, 4])
 def test_gemv_multi_matches_single_calls(t, k, ns, batch):
     """One grouped call gives bit-identical results to one qmm_gemv call per
@@ -400,7 +409,8 @@ def test_gemv_multi_matches_single_calls(t, k, ns, batch):
 @pytest.mark.parametrize("t,k,ns", [(G.Q4_0, 2048, [2048, 256, 256]), (G.Q4_0, 2048, [5632, 5632]),
                                     (G.Q4_K, 4096, [4096, 1024, 1024]), (G.Q4_K, 4096, [14336, 14336]),
                                     (G.Q6_K, 4096, [1024, 3, 0, 700]), (G.Q8_0, 1984, [37] * 9),
-                                    (G.Q5_0, 2048, [4100, 7]), (G.Q5_K, 3840, [0, 515, 1])])
+                                    (G.Q5_0, 2048, [4100, 7]), (G.Q5_K, 3840, [0, 515, 1]),
+                                    (G.Q4_K, 4096, [700, 0]), (G.Q4_0, 2048, [37] * 7 + [0])])
 def test_gemv_multi_shared_x_matches_single_calls(t, k, ns):
     """A grouped call whose problems all read one x (q / k / v, gate / up)
     stages x once per workgroup; results stay bit-identical to one qmm_gemv
@@ -418,3 +428,85 @@ def test_gemv_multi_shared_x_matches_single_calls(t, k, ns):
         if n:
             ref, absum = oracle.gemv(t, w, n, k, x)
             check_tol(got, ref, absum, GEMV_TOL, "gemv_multi shared x")
+
+
+# ------------------------------------------------------ zero-weight rows ---
+
+import zero_rows as Z  # noqa: E402
+
+ZERO_KINDS = ["zero", "sparse", "single", "dense", "random"]
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("batch", [1, 2, 5, 8])
+def test_gemv_zero_weight_rows(t, batch):
+    """Rows of exactly zero weights, mostly zero weights, one nonzero weight,
+    or one zero weight per block (tests/zero_rows.py): Q8_0 code 0, Q4_0 code
+    8, Q5_0 code 16, Q6_K code 32, Q4_K / Q5_K with d sc q = dmin m.  Every
+    product uses the element's own weight, so zero rows give exactly 0 and
+    every output meets 2e-5 relative to sum |w x| of its own row (no
+    cancellation after a rounding).  Shapes cover the one-segment, the
+    multi-segment and the batch kernels."""
+    be = G.BLOCK_ELEMS[t]
+    shapes = [(70, 8 * be)] + ([(45, 4096), (37, 14336)] if be == 256 else [(45, 2048), (37, 5632)])
+    for n, k in shapes:
+        say("gemv zero rows", G.NAMES[t], n, k, batch)
+        w = Z.make_matrix(t, n, k, ZERO_KINDS, np.random.default_rng(1000 * t + k + batch))
+        x = G.gen_x(k, batch, seed=40 + k)
+        ref, absum = oracle.gemv(t, w, n, k, x)
+        assert (absum[:, 0::5] == 0).all()       # the all-zero rows
+        got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+        check_tol(got, ref, absum, GEMV_TOL, "zero rows %s n=%d k=%d B=%d" % (G.NAMES[t], n, k, batch))
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("batch", [1, 4, 8])
+@pytest.mark.parametrize("ratio", [1e-8, 1e-10])
+def test_gemv_large_x_on_zero_weight(t, batch, ratio):
+    """In every block the largest |x| sits on a weight that is zero in every
+    row, and the other elements (~ N(0, 1)) are about `ratio` times smaller:
+    sum |w x| comes from the small elements alone.  The batch path splits x
+    into two fp16 parts after scaling each 256-element block to its largest
+    |x|; elements down to about 2^-34 of that largest keep the 2e-5 bound."""
+    be = G.BLOCK_ELEMS[t]
+    n, k = 40, 4 * 256
+    w = Z.make_matrix(t, n, k, ["dense"], np.random.default_rng(77 + t), zero_pos=5)
+    x = G.gen_x(k, batch, seed=78).astype(np.float64)
+    x[:, 5::be] = np.where(x[:, 5::be] < 0, -1.0, 1.0) / ratio
+    x = x.astype(np.float32)
+    say("gemv large x on zero weight", G.NAMES[t], batch, ratio)
+    ref, absum = oracle.gemv(t, w, n, k, x)
+    got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+    say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "large x on zero weight"))
+
+
+@pytest.mark.parametrize("t", [G.Q4_K, G.Q5_K])
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_gemv_k_quant_scale_ratio(t, batch):
+    """d and dmin far apart (one of them 2^-12 times the other, which puts it
+    among the fp16 subnormals for these ranges), and dmin = 0: the
+    per-element weights d sc q - dmin m then need all 24 bits of fp32, which
+    the batch path carries as two fp16 parts per weight."""
+    n, k = 48, 6 * 256
+    bb = G.BLOCK_BYTES[t]
+    x = G.gen_x(k, batch, seed=92)
+
+    def put(w, b, off, v):
+        w[:, b * bb + off:b * bb + off + 2] = np.frombuffer(v.astype(np.float16).tobytes(), np.uint8).reshape(-1, 2)
+
+    for mode in ("dmin_small", "d_small", "dmin_zero"):
+        w = G.gen_weights(t, n, k, seed=93).reshape(n, -1).copy()
+        for b in range(k // 256):
+            d = np.frombuffer(w[:, b * bb:b * bb + 2].tobytes(), np.float16).astype(np.float64)
+            if mode == "dmin_small":
+                put(w, b, 2, d * 2.0 ** -12)
+            elif mode == "d_small":
+                put(w, b, 2, d)
+                put(w, b, 0, d * 2.0 ** -12)
+            else:
+                put(w, b, 2, np.zeros_like(d))
+        w = w.reshape(-1)
+        say("gemv K-quant scale ratio", G.NAMES[t], batch, mode)
+        ref, absum = oracle.gemv(t, w, n, k, x)
+        got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+        check_tol(got, ref, absum, GEMV_TOL, "scale ratio %s %s" % (G.NAMES[t], mode))
