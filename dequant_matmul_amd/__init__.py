@@ -43,6 +43,7 @@ SIGNATURES = {
     "qmm_gemv": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
     "qmm_gemv_multi": (_I, [_I, _I, _P, _P, _I64, _P, _I64, _P, _P]),
     "qmm_gemm_prefill": (_I, [_I, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "qmm_gemv_pass": (_I, [_I, _P, _P]),
     "qmm_status_str": (ctypes.c_char_p, [_I]),
     "qmm_version": (ctypes.c_char_p, []),
 }
@@ -235,6 +236,37 @@ def gemv_multi(ws, qtype: int, ns, k: int, xs, outs=None):
     _call(lib.qmm_gemv_multi(qtype, np_, wp, nn, k, xp, B, yp, _stream_ptr(dev) if np_ else None),
           "qmm_gemv_multi")
     return outs
+
+
+class PassGemv(ctypes.Structure):
+    """One GEMV of a decode pass (struct qmm_pass_gemv of include/qmm.h)."""
+    _fields_ = [("w", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("type", ctypes.c_int32), ("stage", ctypes.c_int32)]
+
+
+def pass_table(problems):
+    """ctypes table of a decode pass from (w, qtype, n, k, x, y, stage) tuples
+    of device tensors (w uint8, x fp32 of k elements, y fp32 of n)."""
+    torch = _torch()
+    tab = (PassGemv * max(1, len(problems)))()
+    for i, (w, qtype, n, k, x, y, stage) in enumerate(problems):
+        _check_w(w, qtype, n, k)
+        for t, cnt in ((x, k), (y, n)):
+            if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != cnt:
+                raise ValueError("pass problem %d: x / y must be contiguous fp32 device tensors of k / n elements" % i)
+        tab[i] = PassGemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), n, k, qtype, stage)
+    return tab
+
+
+def gemv_pass(problems, table=None, stream=None):
+    """Run a decode pass: problems = [(w, qtype, n, k, x, y, stage), ...] in
+    nondecreasing stage order; each writes y = W x, and every problem of a
+    stage completes before a later stage reads its x."""
+    if table is None:
+        table = pass_table(problems)
+    n = len(problems)
+    st = stream if stream is not None else (_stream_ptr(problems[0][0].device) if n else None)
+    _call(lib.qmm_gemv_pass(n, ctypes.cast(table, ctypes.c_void_p), st), "qmm_gemv_pass")
 
 
 def gemm_prefill(w, qtype: int, n: int, k: int, x, out=None):

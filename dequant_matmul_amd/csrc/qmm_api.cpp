@@ -6,6 +6,8 @@
 #include "../../include/qmm.h"
 #include "qmm_launch.h"
 
+#include <vector>
+
 namespace {
 
 int block_elems(int t)
@@ -29,6 +31,10 @@ int block_bytes(int t)
     default: return 0;
     }
 }
+
+// Elements per lane-unit of the GEMV decode: 64 for the 256-element
+// super-blocks, 32 for the 32-element blocks.
+int unit_elems(int t) { return block_elems(t) == 256 ? 64 : 32; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -256,6 +262,118 @@ int qmm_gemm_prefill(int type, const void *w, int64_t n, int64_t k, const uint16
     if (k == 0)
         return hip_status(qmm::launch_fill_zero(y, m * n, (hipStream_t)stream));
     return hip_status(qmm::launch_gemm(type, w, n, k, rb, x, m, y, (hipStream_t)stream));
+}
+
+int qmm_gemv_pass(int nprob, const qmm_pass_gemv *probs, void *stream)
+{
+    if (nprob < 0)
+        return QMM_ERR_SHAPE;
+    if (nprob == 0)
+        return QMM_OK;
+    if (probs == nullptr)
+        return QMM_ERR_NULL;
+    for (int i = 0; i < nprob; ++i) {
+        const qmm_pass_gemv &P = probs[i];
+        size_t rb = 0;
+        const int st = check_common(P.type, P.w, P.n, P.k, &rb);
+        if (st != QMM_OK)
+            return st;
+        if (P.stage < 0 || (i > 0 && P.stage < probs[i - 1].stage))
+            return QMM_ERR_SHAPE;
+        if (P.n == 0 || P.k == 0)
+            continue;
+        if (P.x == nullptr || P.y == nullptr)
+            return QMM_ERR_NULL;
+        if (!aligned16(P.x) || !aligned16(P.y))
+            return QMM_ERR_ALIGN;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    std::vector<bool> done(nprob, false);
+    for (int a = 0; a < nprob;) {
+        int b = a;
+        while (b < nprob && probs[b].stage == probs[a].stage)
+            ++b;
+        // stage [a, b): problems with rows, grouped by the x they read
+        for (int i = a; i < b; ++i) {
+            const qmm_pass_gemv &Pi = probs[i];
+            if (done[i])
+                continue;
+            if (Pi.n == 0) {
+                done[i] = true;
+                continue;
+            }
+            if (Pi.k == 0) {
+                done[i] = true;
+                const int st = hip_status(qmm::launch_fill_zero(Pi.y, Pi.n, s));
+                if (st != QMM_OK)
+                    return st;
+                continue;
+            }
+            // the problems of this stage reading the same x, with single-segment
+            // 16-byte rows of the same lane-unit size: one launch (up to three
+            // block types of up to eight problems each); any other problem:
+            // its own launch
+            const int ue = unit_elems(Pi.type);
+            const size_t rbi = qmm_row_bytes(Pi.type, Pi.k);
+            const bool one_seg = Pi.k <= 64 * ue && rbi % 16 == 0;
+            if (!one_seg) {
+                done[i] = true;
+                const int st = hip_status(qmm::launch_gemv(Pi.type, Pi.w, Pi.n, Pi.k, rbi, Pi.x, 1, Pi.y, s));
+                if (st != QMM_OK)
+                    return st;
+                continue;
+            }
+            int types[qmm::STAGE_GROUPS], np[qmm::STAGE_GROUPS], ng = 0;
+            const void *w[qmm::STAGE_GROUPS * qmm::STAGE_PROBS];
+            int64_t n[qmm::STAGE_GROUPS * qmm::STAGE_PROBS];
+            float *y[qmm::STAGE_GROUPS * qmm::STAGE_PROBS];
+            int members[qmm::STAGE_GROUPS][qmm::STAGE_PROBS];
+            for (int j = i; j < b; ++j) {
+                const qmm_pass_gemv &Pj = probs[j];
+                if (done[j] || Pj.n == 0 || Pj.x != Pi.x || Pj.k != Pi.k || unit_elems(Pj.type) != ue ||
+                    qmm_row_bytes(Pj.type, Pj.k) % 16 != 0)
+                    continue;
+                int g = 0;
+                while (g < ng && types[g] != Pj.type)
+                    ++g;
+                if (g == ng) {
+                    if (ng == qmm::STAGE_GROUPS)
+                        continue;   // a later launch takes it
+                    types[ng] = Pj.type;
+                    np[ng++] = 0;
+                }
+                if (np[g] == qmm::STAGE_PROBS)
+                    continue;
+                members[g][np[g]++] = j;
+                done[j] = true;
+            }
+            int total = 0;
+            for (int g = 0; g < ng; ++g)
+                total += np[g];
+            if (total == 1) {
+                const int j = members[0][0];
+                const int st = hip_status(qmm::launch_gemv(probs[j].type, probs[j].w, probs[j].n, probs[j].k,
+                                                           qmm_row_bytes(probs[j].type, probs[j].k), probs[j].x,
+                                                           1, probs[j].y, s));
+                if (st != QMM_OK)
+                    return st;
+                continue;
+            }
+            int c = 0;
+            for (int g = 0; g < ng; ++g)
+                for (int m = 0; m < np[g]; ++m, ++c) {
+                    const qmm_pass_gemv &Pj = probs[members[g][m]];
+                    w[c] = Pj.w;
+                    n[c] = Pj.n;
+                    y[c] = Pj.y;
+                }
+            const int st = hip_status(qmm::launch_gemv_stage(ng, types, np, w, n, Pi.k, Pi.x, y, s));
+            if (st != QMM_OK)
+                return st;
+        }
+        a = b;
+    }
+    return QMM_OK;
 }
 
 const char *qmm_status_str(int status)

@@ -79,4 +79,14 @@ hipError_t launch_gemm(int type, const void *w, int64_t n, int64_t k, size_t rb,
 
 hipError_t launch_fill_zero(float *p, int64_t count, hipStream_t s);
 
+// One stage of a decode pass in one launch (batch 1): ng <= 3 groups of
+// problems, group g of block type type[g] with np[g] <= 8 problems (w, n, y
+// listed group after group), every problem reading x (k elements, at most
+// one lane-unit segment for its type); all types of a launch have the same
+// lane-unit size (the 256-element types, or the 32-element ones).
+constexpr int STAGE_GROUPS = 3;
+constexpr int STAGE_PROBS = 8;
+hipError_t launch_gemv_stage(int ng, const int *type, const int *np, const void *const *w, const int64_t *n,
+                             int64_t k, const float *x, float *const *y, hipStream_t s);
+
 }  // namespace qmm

@@ -237,6 +237,47 @@ QMM_API int qmm_gemv_multi(int type, int nprob, const void *const *w, const int6
 QMM_API int qmm_gemm_prefill(int type, const void *w, int64_t n, int64_t k,
                      const uint16_t *x, int64_t m, float *y, void *stream);
 
+/*
+ * Decode pass: the batch-1 GEMVs of one token, stage by stage.  (shimmy
+ * "Airframe GPU pipeline", dispatch counts: a token's dispatches are encoded
+ * in one command buffer, the FFN gate and up projections as one dispatch;
+ * dotLLM "GPU Inference", Synchronization Model: one stream, no host sync
+ * inside the forward pass; both pages: decode is bound by reading the
+ * weights.)
+ *
+ * Problem i computes probs[i].y = W_i x_i as qmm_gemv at batch 1 (same
+ * decode, same 2e-5 bound).  probs[i].stage must not decrease along the
+ * array; problems with equal stage values form one stage, and every problem
+ * of a stage is complete before any problem of a later stage reads its x,
+ * so a later stage may read an earlier stage's y (o reading attention
+ * output, down reading the gated FFN activation, ...).  Problems of one
+ * stage must not write what another problem of the same stage reads.
+ *
+ * Launches: one per stage and x -- the problems of a stage that read the
+ * same x (q / k / v, or gate / up) run as one launch even when their block
+ * types differ (up to three types of up to eight problems each, of the same
+ * lane-unit size: the 256-element K-quants, or the 32-element types), with
+ * x staged once per workgroup; a problem whose k spans several lane-unit
+ * segments (k > 4096 for the K-quants, > 2048 for the others) or whose rows
+ * are not 16-byte multiples gets a launch of its own.  Each launch is
+ * stream-ordered after the ones before it.
+ *
+ * Per problem the conventions and errors of qmm_gemv apply (w, x, y may be
+ * NULL when n == 0; k == 0 writes zeros).  Any argument error returns before
+ * anything is enqueued.
+ */
+typedef struct qmm_pass_gemv {
+    const void *w;  /* device: n rows of qmm_row_bytes(type, k) bytes */
+    const float *x; /* device: fp32 [k] */
+    float *y;       /* device: fp32 [n] */
+    int64_t n;
+    int64_t k;
+    int32_t type;   /* qmm_type */
+    int32_t stage;  /* nondecreasing along the array */
+} qmm_pass_gemv;
+
+QMM_API int qmm_gemv_pass(int nprob, const qmm_pass_gemv *probs, void *stream);
+
 /* Static text for a status code (never NULL). */
 QMM_API const char *qmm_status_str(int status);
 

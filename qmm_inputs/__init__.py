@@ -208,6 +208,19 @@ def workload(cfg: int):
     return [(nm, t, n, k, 1000 * cfg + i) for i, (nm, t, n, k) in enumerate(mats)]
 
 
+def decode_stage(name: str) -> int:
+    """Stage of a decode-stream matrix in a decoder's dataflow: per layer L,
+    q / k / v read the normalized hidden state (stage 4L), o reads the
+    attention output (4L + 1), gate / up the normalized hidden state after
+    attention (4L + 2), down the gated FFN activation (4L + 3); the LM head
+    comes after the last layer."""
+    if name == "lm_head":
+        return 1 << 20
+    layer, proj = name.split(".")
+    L = int(layer[1:])
+    return 4 * L + {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}[proj]
+
+
 def x_seed(cfg: int, i: int) -> int:
     return 1000 * cfg + 500 + i
 

@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     syms = declared_symbols()
     assert {"qmm_dequant", "qmm_dequant_f16", "qmm_embed", "qmm_embed_f16", "qmm_quantize", "qmm_quantize_f16",
             "qmm_gemv", "qmm_gemv_multi", "qmm_gemm_prefill", "qmm_row_bytes", "qmm_block_elems",
-            "qmm_block_bytes", "qmm_status_str", "qmm_version"} == set(syms)
+            "qmm_block_bytes", "qmm_status_str", "qmm_version", "qmm_gemv_pass"} == set(syms)
 
 
 def test_library_exports_every_declared_symbol():
@@ -175,6 +175,38 @@ def test_validation_errors_gemv_multi():
     assert L.qmm_gemv_multi(q.Q4_K, 2, w, N2(4, 8), 256, P2(A, None), 1, y, None) == q.ERR_NULL
     assert L.qmm_gemv_multi(q.Q4_K, 2, w, n, 256, x, 0, y, None) == q.OK
     assert L.qmm_gemv_multi(q.Q4_K, 2, P2(None, None), N2(0, 0), 256, x, 1, y, None) == q.OK
+
+
+def test_validation_errors_gemv_pass():
+    q = _lib()
+    L = q.lib
+
+    def call(*rows):
+        t = (q.PassGemv * len(rows))()
+        for i, r in enumerate(rows):
+            t[i] = q.PassGemv(*r)
+        return L.qmm_gemv_pass(len(rows), ctypes.cast(t, ctypes.c_void_p), None)
+
+    ok = (A, A, A, 64, 4096, q.Q4_K, 0)
+    assert L.qmm_gemv_pass(0, None, None) == q.OK
+    assert L.qmm_gemv_pass(-1, None, None) == q.ERR_SHAPE
+    assert L.qmm_gemv_pass(1, None, None) == q.ERR_NULL
+    assert call((A, A, A, 64, 4096, 9, 0)) == q.ERR_TYPE
+    assert call((A, A, A, 64, 4000, q.Q4_K, 0)) == q.ERR_SHAPE            # k not a block multiple
+    assert call((A, A, A, -1, 4096, q.Q4_K, 0)) == q.ERR_SHAPE
+    assert call((A, A, A, 64, -256, q.Q4_K, 0)) == q.ERR_SHAPE
+    assert call((A, A, A, 64, 4096, q.Q4_K, -1)) == q.ERR_SHAPE           # negative stage
+    assert call((A, A, A, 64, 4096, q.Q4_K, 1), ok) == q.ERR_SHAPE        # stages decrease
+    assert call((None, A, A, 64, 4096, q.Q4_K, 0)) == q.ERR_NULL
+    assert call((A, None, A, 64, 4096, q.Q4_K, 0)) == q.ERR_NULL
+    assert call((A, A, None, 64, 4096, q.Q4_K, 0)) == q.ERR_NULL
+    assert call((MIS, A, A, 64, 4096, q.Q4_K, 0)) == q.ERR_ALIGN
+    assert call((A, MIS, A, 64, 4096, q.Q4_K, 0)) == q.ERR_ALIGN
+    assert call((A, A, MIS, 64, 4096, q.Q4_K, 0)) == q.ERR_ALIGN
+    # a bad later problem: nothing of the earlier ones is enqueued either
+    assert call(ok, (A, None, A, 64, 4096, q.Q4_K, 1)) == q.ERR_NULL
+    # empty problems are skipped (null pointers allowed); nothing to run -> OK
+    assert call((None, None, None, 0, 4096, q.Q4_K, 0)) == q.OK
 
 
 def test_binding_has_no_cpu_fallback():
