@@ -1,31 +1,36 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized-weight matmul on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|q8_0|q4_k|prefill|mix|q5|embed|kv|dequant]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--secondary all|none|<name>[,<name>...]]
 
-A step is one decode pass over the TinyLlama-shaped Q4_0 weight stream:
-22 layers x (q, k, v, o, gate, up, down) = 154 GEMVs at batch 1 on one
-stream, each with a fresh fp32 activation, as one captured HIP graph (one
-submission per token, no host synchronization inside the pass).  Inputs are
-resident in HBM before timing starts.  The 545 MB stream is larger than the
-256 MB last-level cache, so every pass reads the weights from HBM.
+A step is one decode pass over the largest workload that fits one GPU: the
+Llama-3-8B-shaped Q4_K_M-style mix at batch 1 -- 32 layers of (q, k, v, o,
+gate, up, down) with v and down in Q6_K, plus the 128256 x 4096 Q6_K LM
+head: 225 GEMVs, 4.88 GB of weights.  The pass runs through qmm_gemv_pass
+in the decoder's stage order (q|k|v, o, gate|up, down per layer, then the
+head; one launch per stage, every stage after the one before it), captured
+as one HIP graph and replayed once per step.  Inputs are resident in HBM
+before timing starts; 4.88 GB is far larger than the 256 MB last-level
+cache, so every pass reads the weights from HBM.
 
-Printed: one JSON line with the whole-pass HBM throughput (GB/s), its fraction
-of the 8 TB/s peak, the decode-equivalent tokens/s, the roofline of the
-dominant kernel (the Q4_0 GEMV) from per-launch HIP-event timings, the CPU
-oracle timed on a bounded sample of the same workload, and secondary figures
-for the other workloads (Q8_0 single matrix, Llama-3-8B Q4_K set, 512-token
-prefill GEMMs, Q4_K_M-style mix with a Q6_K LM head at batch 1/4/8, the
-same shapes in the 5-bit types Q5_K / Q5_0, the quantized embedding
-gather for one decode token and a 512-token chunk, and the Q8_0 / Q4_0
-KV-cache codec: encoding and decoding K rows of one Llama-3-8B layer, and
-the dequant-only kernel to fp32 / fp16).
+Printed: one JSON line with the whole-pass throughput (GB/s of algorithmic
+bytes), its fraction of the 8 TB/s HBM peak, decode-equivalent tokens/s, the
+roofline of the dominant kernel (the mixed-type stage GEMV that runs q|k|v
+and gate|up) from HIP-event timings of its launches, the CPU oracle on the
+host (one thread and all cores, per workload), and secondary figures with
+their own roofline blocks: the Q8_0 2048 x 2048 GEMV, the TinyLlama Q4_0 and
+Llama-3-8B Q4_K passes, the 512-token prefill GEMMs (TFLOP/s against the
+fp16 dense peak), the same mix at batch 4 and 8 with the skinny GEMM beside
+it, the 5-bit types, the embedding gather, the KV-cache codec and the
+dequant-only kernel.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -39,16 +44,30 @@ import qmm_inputs as G  # noqa: E402
 METRIC = "quantized GEMV HBM GB/s (% of peak) + decode tok/s equiv; prefill GEMM TFLOP/s"
 HBM_PEAK_GBS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
-# HBM bytes per launch of the dominant kernel (the batch-1 Q4_0 GEMV over the
-# decode stream) from rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by what the
-# same counters read for a plain 256 MiB device copy (reads x2.0, writes
-# x1.0).  It describes the kernels it was measured on: set it to None when
-# they change, until the counters are taken again.
-TRAFFIC = 3759748   # bytes per launch, averaged over one pass (gemv3_kernel<0,1,8/16>, gemv1_kernel<0,1,...>)
+
+# HBM bytes per launch of the dominant kernel from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE, summed over the launches of the headline
+# command and divided by them), each scaled by what the same counter reads
+# for a plain 256 MiB device copy (reads x2.0, writes x1.0).  They describe
+# the kernel sources they were taken on (SHA-256 prefix of the files in
+# TRAFFIC_SOURCES): when the sources change, the line reports null until the
+# counters are taken again.
+TRAFFIC = {"sources_sha16": None, "bytes_per_launch": None}
+TRAFFIC_SOURCES = ("dequant_matmul_amd/csrc/qmm_gemv.hip", "dequant_matmul_amd/csrc/qmm_gemv_unit.h",
+                   "dequant_matmul_amd/csrc/qmm_device.h")
+SECONDARIES = ("q8_0", "tinyllama", "q4_k", "prefill", "mix_batch", "q5", "embed", "kv", "dequant")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def sources_sha16():
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -56,16 +75,25 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--secondary", choices=["all", "none", "q8_0", "q4_k", "prefill", "mix", "q5", "embed", "kv", "dequant"], default="all",
-                   help="which secondary workloads to run after the primary line's (all by default)")
+    p.add_argument("--secondary", default="all",
+                   help="comma list of secondary workloads to run after the primary line's (all, none, or any of "
+                        + ", ".join(SECONDARIES) + ")")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=2.0,
+                   help="target CPU time of each oracle sample (per workload and thread count)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB 10 times (reference for HBM byte counters)")
     p.add_argument("--reference-bw", action="store_true",
-                   help="only time plain device fills and copies (torch kernels) of 16 MB and 235 MB, rotating over "
-                        "more than 400 MB: reference bandwidths for the streaming kernels")
-    return p.parse_args()
+                   help="only time plain device fills, reads and copies (torch kernels) of 16 MB and 235 MB")
+    p.add_argument("--dominant-only", action="store_true",
+                   help="only replay the dominant kernel's launches of the headline pass (for counter runs)")
+    a = p.parse_args()
+    a.secondary = [s for s in a.secondary.split(",") if s] if a.secondary not in ("all", "none") else (
+        list(SECONDARIES) if a.secondary == "all" else [])
+    for s in a.secondary:
+        if s not in SECONDARIES:
+            p.error("unknown secondary %r" % s)
+    return a
 
 
 # ----------------------------------------------------------------- helpers --
@@ -81,10 +109,9 @@ class Problem:
         if kind == "gemv":
             # algorithmic bytes: weights + x + y (x re-reads from cache not counted)
             self.bytes = wbytes + 4 * self.batch * k + 4 * self.batch * n
-            self.flops = 2 * self.batch * n * k
         else:
             self.bytes = wbytes + 2 * self.batch * k + 4 * self.batch * n
-            self.flops = 2 * self.batch * n * k
+        self.flops = 2 * self.batch * n * k
         self.wbytes = wbytes
 
     def launch(self, q, stream):
@@ -151,48 +178,93 @@ class Dequant:
             raise RuntimeError("dequant %s: %s" % (self.name, q.status_str(st)))
 
 
-class Group:
-    """Several same-type, same-k batch-1 GEMVs issued as one qmm_gemv_multi
-    call; share_x: all of them read the first one's activation (as q / k / v
-    and gate / up read one normalized hidden state in a decoder layer)."""
+class Pass:
+    """A decode pass (qmm_gemv_pass) over a workload's matrices at batch 1, in
+    the decoder's stage order.  share_x: the problems of a stage read one x
+    (q / k / v the normalized hidden state, gate / up the normalized state
+    after attention), as in a decoder; else each GEMV has its own x."""
 
-    def __init__(self, probs, share_x=False):
-        import ctypes
-        self.probs = probs
-        npb = len(probs)
-        self.t, self.k, self.batch = probs[0].t, probs[0].k, probs[0].batch
-        self.np = npb
-        self.w = (ctypes.c_void_p * npb)(*[p.w.data_ptr() for p in probs])
-        self.x = (ctypes.c_void_p * npb)(*[(probs[0] if share_x else p).x.data_ptr() for p in probs])
-        self.y = (ctypes.c_void_p * npb)(*[p.y.data_ptr() for p in probs])
-        self.n = (ctypes.c_int64 * npb)(*[p.n for p in probs])
-        self.name = "+".join(p.name for p in probs)
+    def __init__(self, torch, q, cfg, weights, dev, share_x=True, only=None):
+        self.q = q
+        self.probs, self.plist = [], []
+        xs = {}
+        for i, (name, t, n, k, w) in enumerate(weights):
+            st = G.decode_stage(name)
+            if only is not None and not only(name):
+                continue
+            key = st if share_x else i
+            if key not in xs:
+                xs[key] = torch.from_numpy(G.gen_x(k, 1, G.x_seed(cfg, i))).to(dev)
+            x = xs[key]
+            y = torch.empty((1, n), dtype=torch.float32, device=dev)
+            self.probs.append(Problem(torch, name, t, n, k, w, x, y))
+            self.plist.append((w, t, n, k, x.view(-1), y.view(-1), st))
+        self.table = q.pass_table(self.plist)
+        # algorithmic bytes: weights, each distinct x once, every y
+        self.wbytes = sum(p.wbytes for p in self.probs)
+        self.bytes = self.wbytes + sum(4 * x.numel() for x in xs.values()) + sum(4 * p.n for p in self.probs)
+        self.stages = len({e[6] for e in self.plist})
 
     def launch(self, q, stream):
-        st = q.lib.qmm_gemv_multi(self.t, self.np, self.w, self.n, self.k, self.x, self.batch, self.y, stream)
-        if st != 0:
-            raise RuntimeError("gemv_multi %s: %s" % (self.name, q.status_str(st)))
+        q.gemv_pass(self.plist, table=self.table, stream=stream)
 
 
-def group_layers(probs, fuse, share_x=False):
-    """Split a 7-projections-per-layer list into launch groups: fuse = set of
-    projection-name tuples issued together (e.g. ("gate", "up"))."""
-    out = []
-    for L in range(0, len(probs), 7):
-        layer = {p.name.split(".")[-1]: p for p in probs[L:L + 7]}
-        done = set()
-        for nm in ("q", "k", "v", "o", "gate", "up", "down"):
-            if nm in done:
-                continue
-            grp = next((g for g in fuse if nm in g), (nm,))
-            out.append(Group([layer[g] for g in grp], share_x) if len(grp) > 1 else layer[nm])
-            done.update(grp)
-    return out
+def capture(torch, q, work):
+    """One HIP graph of `work` (a list of objects with .launch(q, stream), or
+    one such object)."""
+    work = work if isinstance(work, list) else [work]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for p in work:                                   # warm (outside capture)
+            p.launch(q, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for p in work:
+            p.launch(q, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return g
 
 
-def build_weights(torch, cfg, dev="cuda:0"):
-    return [(name, t, n, k, torch.from_numpy(G.gen_weights(t, n, k, seed)).to(dev))
-            for (name, t, n, k, seed) in G.workload(cfg)]
+def time_graph(torch, g, steps, warmup, min_warm_s=0.03):
+    """Event time per replay: the requested warm-up replays, continued until
+    at least min_warm_s of replays have run (sustained load takes tens of
+    milliseconds to reach steady clocks), then `steps` timed ones between
+    two events on the stream the graph runs on."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < min_warm_s:
+        g.replay()
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def roofline(achieved, peak, unit, bound, **extra):
+    d = {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4)}
+    d.update(extra)
+    return d
+
+
+def build_weights(torch, cfg, dev="cuda:0", keep_host=False):
+    out, host = [], []
+    for (name, t, n, k, seed) in G.workload(cfg):
+        w = G.gen_weights(t, n, k, seed)
+        out.append((name, t, n, k, torch.from_numpy(w).to(dev)))
+        if keep_host:
+            host.append(w)
+    return (out, host) if keep_host else out
 
 
 def make_gemvs(torch, cfg, weights, batch, dev="cuda:0"):
@@ -204,83 +276,101 @@ def make_gemvs(torch, cfg, weights, batch, dev="cuda:0"):
     return probs
 
 
-def run_pass(q, probs, stream):
-    for p in probs:
-        p.launch(q, stream)
+# ------------------------------------------------------------ CPU baseline --
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
-def capture(torch, q, probs):
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        run_pass(q, probs, torch.cuda.current_stream().cuda_stream)   # warm (outside capture)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        run_pass(q, probs, torch.cuda.current_stream().cuda_stream)
-    torch.cuda.synchronize()
-    return g
-
-
-def time_graph(torch, g, steps, warmup, min_warm_s=0.03):
-    """Secondary timings: the requested warm-up replays, continued until at
-    least min_warm_s of replays have run (sustained matrix-core load takes
-    tens of milliseconds to reach steady clocks), then `steps` timed ones."""
-    t0 = time.perf_counter()
+def _cpu_rate(items, target_s):
+    """Run items [(fn, work)] in turn until target_s of time is spent (at
+    least one); returns (work per second, items run, seconds)."""
+    done, used, ran = 0.0, 0.0, 0
     i = 0
-    while i < warmup or time.perf_counter() - t0 < min_warm_s:
-        g.replay()
-        i += 1
-        if i % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        g.replay()
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
-
-
-def time_eager(torch, q, probs, steps, warmup):
-    stream = torch.cuda.current_stream().cuda_stream
-    for _ in range(warmup):
-        run_pass(q, probs, stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        run_pass(q, probs, stream)
-    torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
-
-
-def cpu_baseline(cfg_probs_host, target_s):
-    """The oracle (plain C, fp64, OpenMP over rows) on a bounded sample of the
-    same workload: whole layers of the decode stream, taken in order (and
-    again from the first layer once all are done) until about target_s
-    seconds of CPU time are spent."""
-    import oracle
-    nthreads = oracle.max_threads()
-    done_bytes, t_used, layers = 0, 0.0, 0
-    per_layer = 7
-    nl = len(cfg_probs_host) // per_layer
-    while t_used < target_s or layers == 0:
-        i = (layers % nl) * per_layer
-        chunk = cfg_probs_host[i:i + per_layer]
+    while used < target_s or ran == 0:
+        fn, work = items[i % len(items)]
         t0 = time.perf_counter()
-        for (t, n, k, w, x) in chunk:
-            oracle.gemv(t, w, n, k, x)
-        t_used += time.perf_counter() - t0
-        done_bytes += sum(n * G.row_bytes(t, k) + 4 * k + 4 * n for (t, n, k, w, x) in chunk)
-        layers += 1
-    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": nthreads, "kind": "oracle",
-            "sample": "%d layers (%d GEMVs, %.1f MB of weights; the 22-layer Q4_0 stream repeated %.1f times), %.1f s"
-                      % (layers, layers * per_layer, done_bytes / 1e6, layers / nl, t_used)}
+        fn()
+        used += time.perf_counter() - t0
+        done += work
+        ran += 1
+        i += 1
+    return done / used, ran, used
 
 
-# ------------------------------------------------------------- secondaries --
+def cpu_baselines(target_s, mix_host=None):
+    """The oracle (plain C, exact fp32 dequant then fp64 dot products, OpenMP
+    over rows) on the host, on 1 thread and on every core, over bounded
+    samples of each workload: the same matrices (same seeds) as the GPU runs,
+    taken in chunks of rows (every matrix of a layer in turn, then the next
+    chunk) until about target_s seconds are spent; for the prefill GEMM,
+    rows of one 512-token chunk, one at a time."""
+    import oracle
+    allc = oracle.max_threads()
 
-def sec_cfg1(torch, q, steps, warmup, dev):
+    def gemv_items(mats, chunk=256):
+        """[(fn, bytes)]: row chunks of each matrix, interleaved."""
+        per = []
+        for (t, n, k, w, x) in mats:
+            rb = G.row_bytes(t, k)
+            w2 = w.reshape(n, rb)
+            per.append([((lambda t=t, k=k, x=x, ww=np.ascontiguousarray(w2[r:r + chunk]), nr=min(chunk, n - r):
+                          oracle.gemv(t, ww, nr, k, x)), min(chunk, n - r) * rb + 4 * k + 4 * min(chunk, n - r))
+                        for r in range(0, n, chunk)])
+        items = []
+        for i in range(max(len(p) for p in per)):
+            items += [p[i] for p in per if i < len(p)]
+        return items
+
+    def layer0(cfg):
+        mats = []
+        for i, (name, t, n, k, seed) in enumerate(G.workload(cfg)):
+            if "." in name and not name.startswith("l0."):
+                continue
+            mats.append((t, n, k, G.gen_weights(t, n, k, seed), G.gen_x(k, 1, G.x_seed(cfg, i))))
+        return mats
+
+    work = {
+        "q8_0_2048": ("the 2048 x 2048 Q8_0 GEMV", layer0(1)),
+        "tinyllama_q4_0": ("the Q4_0 stream's first layer (7 GEMVs)", layer0(2)),
+        "llama3_8b_q4_k": ("the Q4_K set's first layer (7 GEMVs)", layer0(3)),
+    }
+    if mix_host is not None:
+        work["q4_k_m_mix_b1"] = ("the mix's first layer (7 GEMVs) and the LM head", mix_host)
+    rates = {}
+    for name, (what, mats) in work.items():
+        items = gemv_items(mats)
+        for nt in (1, allc):
+            oracle.set_threads(nt)
+            rate, ran, used = _cpu_rate(items if nt > 1 else items[:max(1, len(items) // 4)], target_s)
+            rates.setdefault(name, {})["1_thread" if nt == 1 else "all_cores"] = {
+                "value": round(rate / 1e9, 4), "unit": "GB/s", "threads": nt,
+                "sample": "row chunks of 256 of %s, in turn: %d chunks, %.1f s" % (what, ran, used)}
+    m = G.PREFILL_M
+    for name, t, n, k, seed in G.workload(4):
+        w = G.gen_weights(t, n, k, seed)
+        X = G.gen_x_f16(m, k, G.x_seed(4, 0))
+        items = [((lambda r=r: oracle.gemm(t, w, n, k, X, rows=[r])), 2.0 * n * k) for r in range(0, m, 37)]
+        for nt in (1, allc):
+            oracle.set_threads(nt)
+            rate, ran, used = _cpu_rate(items, target_s)
+            rates.setdefault("prefill_" + name, {})["1_thread" if nt == 1 else "all_cores"] = {
+                "value": round(rate / 1e9, 3), "unit": "GFLOP/s", "threads": nt,
+                "sample": "%d rows of one 512 x %d x %d chunk, one at a time, %.1f s" % (ran, n, k, used)}
+    oracle.set_threads(allc)
+    return {"cpu_model": cpu_model(), "cores": allc, "configs": rates}
+
+
+# -------------------------------------------------------------- secondaries --
+
+def sec_q8_0(torch, q, steps, warmup, dev):
     """Q8_0 2048x2048: rotate over 256 copies (1.14 GB) so caches cannot serve
     it; also the cache-resident single-call time."""
     n = k = 2048
@@ -289,40 +379,35 @@ def sec_cfg1(torch, q, steps, warmup, dev):
     copies = [w0.clone() for _ in range(256)]
     y = torch.empty((1, n), dtype=torch.float32, device=dev)
     probs = [Problem(torch, "w%d" % i, G.Q8_0, n, k, c, x, y) for i, c in enumerate(copies)]
-    g = capture(torch, q, probs)
-    t = time_graph(torch, g, max(2, steps // 4), 2) / len(probs)
+    t = time_graph(torch, capture(torch, q, probs), max(2, steps // 4), 2) / len(probs)
     hot = [Problem(torch, "hot", G.Q8_0, n, k, w0, x, y)] * 256
-    gh = capture(torch, q, hot)
-    th = time_graph(torch, gh, max(2, steps // 4), 2) / 256
+    th = time_graph(torch, capture(torch, q, hot), max(2, steps // 4), 2) / 256
     b = probs[0].bytes
-    del copies, probs, g, gh
-    return {"workload": "Q8_0 2048x2048 GEMV, batch 1, over 256 rotating copies",
-            "us_per_gemv": t * 1e6, "GB_s": b / t / 1e9, "pct_hbm_peak": 100 * b / t / 1e9 / HBM_PEAK_GBS,
-            "hot_us_per_gemv_cache_resident": th * 1e6}
+    del copies, probs
+    return {"workload": "Q8_0 2048x2048 GEMV, batch 1, over 256 rotating copies (1.14 GB)",
+            "us_per_gemv": round(t * 1e6, 3), "GB_s": round(b / t / 1e9, 1),
+            "hot_us_per_gemv_cache_resident": round(th * 1e6, 3),
+            "roofline": roofline(b / t / 1e9, HBM_PEAK_GBS, "GB/s", "hbm", kernel="gemv3_kernel<Q8_0>",
+                                 bytes_per_launch=b, avg_launch_us=round(t * 1e6, 3))}
 
 
-def sec_stream(torch, q, cfg, weights, batch, steps, warmup, dev, label, with_gemm=False):
-    probs = make_gemvs(torch, cfg, weights, batch, dev)
-    wbytes = sum(p.wbytes for p in probs)
-    tbytes = sum(p.bytes for p in probs)
-    g = capture(torch, q, probs)
-    tg = time_graph(torch, g, steps, warmup)
-    out = {"workload": label, "gemvs": len(probs), "batch": batch, "weight_bytes": wbytes,
-           "ms_per_pass": tg * 1e3, "GB_s": tbytes / tg / 1e9, "pct_hbm_peak": 100 * tbytes / tg / 1e9 / HBM_PEAK_GBS,
-           "decode_tok_s": batch / tg}
-    del g
-    if with_gemm:
-        # the same pass as a skinny GEMM (fp16 activations, M = batch)
-        gp = []
-        for p in probs:
-            X = torch.from_numpy(G.gen_x_f16(batch, p.k, 77)).to(dev)
-            gp.append(Problem(torch, p.name, p.t, p.n, p.k, p.w, X, p.y, kind="gemm"))
-        gg = capture(torch, q, gp)
-        tgg = time_graph(torch, gg, steps, warmup)
-        out["skinny_gemm_ms_per_pass"] = tgg * 1e3
-        out["skinny_gemm_tok_s"] = batch / tgg
-        del gg, gp
-    del probs
+def sec_pass(torch, q, cfg, steps, warmup, dev, label, weights=None, single_launch_graph=False):
+    wts = weights if weights is not None else build_weights(torch, cfg, dev)
+    P = Pass(torch, q, cfg, wts, dev)
+    tp = time_graph(torch, capture(torch, q, P), steps, warmup)
+    out = {"workload": label, "gemvs": len(P.probs), "stages": P.stages, "batch": 1,
+           "weight_bytes": P.wbytes, "algorithmic_bytes": P.bytes, "ms_per_pass": round(tp * 1e3, 4),
+           "GB_s": round(P.bytes / tp / 1e9, 1), "decode_tok_s": round(1.0 / tp, 1),
+           "roofline": roofline(P.bytes / tp / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                                kernel="whole pass (qmm_gemv_pass, one launch per stage and x)")}
+    if single_launch_graph:
+        # the same GEMVs as one qmm_gemv launch each (one graph), for comparison
+        ts = time_graph(torch, capture(torch, q, P.probs), steps, warmup)
+        out["single_launches_ms_per_pass"] = round(ts * 1e3, 4)
+        out["single_launches_GB_s"] = round(P.bytes / ts / 1e9, 1)
+    del P
+    if weights is None:
+        del wts
     torch.cuda.empty_cache()
     return out
 
@@ -337,13 +422,47 @@ def sec_prefill(torch, q, steps, warmup, dev, cfg=4):
             X = torch.from_numpy(G.gen_x_f16(m, k, G.x_seed(cfg, 10 * c + len(res)))).to(dev)
             Y = torch.empty((m, n), dtype=torch.float32, device=dev)
             probs.append(Problem(torch, "%s.c%d" % (name, c), t, n, k, w, X, Y, kind="gemm"))
-        g = capture(torch, q, probs)
-        tg = time_graph(torch, g, steps, warmup)
+        tg = time_graph(torch, capture(torch, q, probs), steps, warmup)
         flops = sum(p.flops for p in probs)
-        res[name] = {"shape": "4 x (%d x %d x %d)" % (m, n, k), "ms_4_chunks": tg * 1e3,
-                     "TFLOP_s": flops / tg / 1e12, "pct_fp16_peak": 100 * flops / tg / 1e12 / FP16_PEAK_TFLOPS}
-        del g, probs, w
+        tf = flops / tg / 1e12
+        res[name] = {"shape": "4 x (%d x %d x %d)" % (m, n, k), "ms_4_chunks": round(tg * 1e3, 4),
+                     "us_per_chunk": round(tg * 1e6 / len(probs), 2), "TFLOP_s": round(tf, 1),
+                     "roofline": roofline(tf, FP16_PEAK_TFLOPS, "TFLOP/s", "mfma", kernel="gemm_kernel",
+                                          flops_per_launch=flops // len(probs),
+                                          avg_launch_us=round(tg * 1e6 / len(probs), 2))}
+        del probs, w
     torch.cuda.empty_cache()
+    return res
+
+
+def sec_mix_batch(torch, q, steps, warmup, dev, weights):
+    """The Q4_K_M-style mix at batch 4 and 8 (qmm_gemv per matrix, x fp32
+    [B, k]), and the same pass as a skinny GEMM (fp16 X, M = B)."""
+    res = {}
+    for batch in (4, 8):
+        probs = make_gemvs(torch, 5, weights, batch, dev)
+        tot = sum(p.bytes for p in probs)
+        tg = time_graph(torch, capture(torch, q, probs), max(3, steps // 2), 2)
+        gp = [Problem(torch, p.name, p.t, p.n, p.k, p.w, torch.from_numpy(G.gen_x_f16(batch, p.k, 77)).to(dev),
+                      p.y, kind="gemm") for p in probs]
+        tgg = time_graph(torch, capture(torch, q, gp), max(3, steps // 2), 2)
+        res["b%d" % batch] = {
+            "workload": "Q4_K_M-style mix, 225 GEMVs, batch %d" % batch, "ms_per_pass": round(tg * 1e3, 4),
+            "GB_s": round(tot / tg / 1e9, 1), "decode_tok_s": round(batch / tg, 1),
+            "skinny_gemm_ms_per_pass": round(tgg * 1e3, 4), "skinny_gemm_tok_s": round(batch / tgg, 1),
+            "roofline": roofline(tot / tg / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
+                                 kernel="whole pass (batch GEMV, one launch per matrix)")}
+        del probs, gp
+        torch.cuda.empty_cache()
+    return res
+
+
+def sec_q5(torch, q, steps, warmup, dev):
+    res = {"llama3_8b_q5_k": sec_pass(torch, q, 6, steps, warmup, dev,
+                                      "Llama-3-8B-shaped Q5_K decode pass, 224 GEMVs, batch 1"),
+           "tinyllama_q5_0": sec_pass(torch, q, 7, steps, warmup, dev,
+                                      "TinyLlama-shaped Q5_0 decode pass, 154 GEMVs, batch 1"),
+           "prefill_512_q5": sec_prefill(torch, q, steps, warmup, dev, cfg=8)}
     return res
 
 
@@ -464,6 +583,8 @@ def reference_bw(torch, dev):
     return res
 
 
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -491,26 +612,30 @@ def main():
     import dequant_matmul_amd as q
     log("device:", torch.cuda.get_device_name(0), "| lib:", q.version())
 
-    # primary: TinyLlama-shaped Q4_0 decode stream, batch 1
-    log("generating the Q4_0 decode stream (154 GEMVs)")
-    host = []
-    probs = []
-    for i, (name, t, n, k, seed) in enumerate(G.workload(2)):
-        w = G.gen_weights(t, n, k, seed)
-        x = G.gen_x(k, 1, G.x_seed(2, i))
-        host.append((t, n, k, w, x))
-        probs.append(Problem(torch, name, t, n, k, torch.from_numpy(w).to(dev), torch.from_numpy(x).to(dev),
-                             torch.empty((1, n), dtype=torch.float32, device=dev)))
-    torch.cuda.synchronize()
-    tot_bytes = sum(p.bytes for p in probs)
-    w_bytes = sum(p.wbytes for p in probs)
-    g = capture(torch, q, probs)
+    # primary: the Q4_K_M-style mix decode pass, batch 1
+    log("generating the Q4_K_M-style mix (225 GEMVs, 4.88 GB)")
+    weights, host = build_weights(torch, 5, dev, keep_host=True)
+    mix_host = [(t, n, k, host[i], G.gen_x(k, 1, G.x_seed(5, i)))
+                for i, (name, t, n, k, _) in enumerate(weights) if name.startswith("l0.") or name == "lm_head"]
+    del host
+    P = Pass(torch, q, 5, weights, dev)
+    # the dominant kernel: the mixed-type stage GEMV of the q|k|v and gate|up
+    # stages (64 launches per pass), timed alone as a graph of its launches
+    D = Pass(torch, q, 5, weights, dev, only=lambda nm: nm.split(".")[-1] in ("q", "k", "v", "gate", "up"))
+    if args.dominant_only:
+        g = capture(torch, q, D)
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        print(json.dumps({"dominant_only": True, "launches_per_replay": D.stages, "replays": args.steps}))
+        return
+    g = capture(torch, q, P)
     log("timing %d graph replays after %d warmup" % (args.steps, args.warmup))
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
-    # HIP events on the stream the graph (and so every GEMV kernel) runs on
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
@@ -519,7 +644,6 @@ def main():
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / args.steps
     ev_step_s = ev0.elapsed_time(ev1) * 1e-3 / args.steps
-    # spread of single passes: 20 replays, each between its own pair of events
     singles = []
     for _ in range(20):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -529,107 +653,85 @@ def main():
         b.synchronize()
         singles.append(a.elapsed_time(b))
     singles.sort()
-    value = tot_bytes / step_s / 1e9
-    # dominant kernel: every launch of the pass is the Q4_0 GEMV; its average
-    # launch duration is the event time of the pass divided by the launches
-    avg_launch_s = ev_step_s / len(probs)
-    achieved = (tot_bytes / len(probs)) / avg_launch_s / 1e9
-    eager_s = time_eager(torch, q, probs, max(3, args.steps // 2), 2)
-    # the same 154 GEMVs with fewer launches per token: gate|up as one launch
-    # (the dispatch count shimmy's pipeline page gives: 6 per layer) and
-    # q|k|v + gate|up (4 per layer)
-    grouped = {}
-    # (and the 4-launch grouping once more with one activation per group, as
-    # in a decoder layer: q / k / v read one x, gate / up another)
-    for label, fuse, share in (("6_launches_per_layer", (("gate", "up"),), False),
-                               ("4_launches_per_layer", (("q", "k", "v"), ("gate", "up")), False),
-                               ("4_launches_per_layer_shared_x", (("q", "k", "v"), ("gate", "up")), True)):
-        gp = group_layers(probs, fuse, share)
-        gg = capture(torch, q, gp)
-        tg = time_graph(torch, gg, args.steps, args.warmup)
-        grouped[label] = {"launches": len(gp), "ms_per_pass": round(tg * 1e3, 4),
-                          "GB_s": round(tot_bytes / tg / 1e9, 1), "decode_tok_s": round(1.0 / tg, 1)}
-        del gg
-
+    del g
+    gd = capture(torch, q, D)
+    td = time_graph(torch, gd, args.steps, args.warmup)
+    del gd
+    avg_launch = td / D.stages
+    achieved = (D.bytes / D.stages) / avg_launch / 1e9
+    sha = sources_sha16()
+    traffic = TRAFFIC["bytes_per_launch"] if TRAFFIC["sources_sha16"] == sha else None
+    value = P.bytes / step_s / 1e9
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "TinyLlama-shaped Q4_0 decode weight stream: 22 layers x "
-                               "(q 2048x2048, k/v 256x2048, o 2048x2048, gate/up 5632x2048, down 2048x5632) "
-                               "= 154 GEMVs, batch 1, one HIP graph per pass",
-                   "gemvs": len(probs), "batch": 1, "weight_bytes": w_bytes, "algorithmic_bytes": tot_bytes},
+        "config": {"workload": "Q4_K_M-style mix decode pass, Llama-3-8B shapes: 32 layers x (q 4096x4096, "
+                               "k/v 1024x4096, o 4096x4096, gate/up 14336x4096, down 4096x14336; v and down "
+                               "Q6_K, the rest Q4_K) + LM head 128256x4096 Q6_K = 225 GEMVs at batch 1, "
+                               "stage by stage (q|k|v, o, gate|up, down; then the head), one HIP graph per pass",
+                   "gemvs": len(P.probs), "stages": P.stages, "batch": 1, "weight_bytes": P.wbytes,
+                   "algorithmic_bytes": P.bytes},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "decode_tok_s": round(1.0 / step_s, 1),
-        "eager_ms_per_step": round(eager_s * 1e3, 4),
         "event_ms_per_step": round(ev_step_s * 1e3, 4),
         "single_pass_ms": {"median": round(0.5 * (singles[9] + singles[10]), 4), "min": round(singles[0], 4),
                            "max": round(singles[-1], 4), "passes": len(singles)},
-        "grouped_launches": grouped,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": TRAFFIC,
-                     "kernel": "Q4_0 batch-1 GEMV (gemv3_kernel for q/k/v/o and gate/up, gemv1_kernel for down, "
-                               "k=5632)",
-                     "avg_launch_us": round(avg_launch_s * 1e6, 3),
-                     "bytes_per_launch": tot_bytes / len(probs)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "gemv3s_kernel<64, 8>: the mixed-type stage GEMV of the q|k|v and gate|up stages "
+                               "(64 launches per pass)",
+                     "avg_launch_us": round(avg_launch * 1e6, 3),
+                     "bytes_per_launch": round(D.bytes / D.stages), "kernel_sources_sha16": sha},
     }
-    del g
+    del D
 
     if not args.no_cpu_baseline:
-        log("CPU oracle baseline (~%.0f s)" % args.cpu_seconds)
-        line["cpu_baseline"] = cpu_baseline(host, args.cpu_seconds)
-    del host
+        log("CPU oracle baselines (~%.0f s per sample)" % args.cpu_seconds)
+        cb = cpu_baselines(args.cpu_seconds, mix_host)
+        head = cb["configs"]["q4_k_m_mix_b1"]["all_cores"]
+        line["cpu_baseline"] = {"value": head["value"], "unit": "GB/s", "cores": head["threads"], "kind": "oracle",
+                                "sample": head["sample"], "cpu_model": cb["cpu_model"],
+                                "one_thread": cb["configs"]["q4_k_m_mix_b1"]["1_thread"],
+                                "per_workload": cb["configs"]}
+    del mix_host
 
-    if args.secondary != "none":
-        want = (lambda s: args.secondary in ("all", s))
-        sec = {}
-        del probs
-        torch.cuda.empty_cache()
-        if want("q8_0"):
-            log("secondary: Q8_0 single matrix")
-            sec["q8_0_2048"] = sec_cfg1(torch, q, args.steps, args.warmup, dev)
-        if want("q4_k"):
-            log("secondary: Llama-3-8B Q4_K set")
-            wts = build_weights(torch, 3, dev)
-            sec["llama3_8b_q4_k"] = sec_stream(torch, q, 3, wts, 1, args.steps, args.warmup, dev,
-                                               "Llama-3-8B-shaped Q4_K, 224 GEMVs, batch 1")
-            del wts
-            torch.cuda.empty_cache()
-        if want("prefill"):
-            log("secondary: prefill GEMMs")
-            sec["prefill_512"] = sec_prefill(torch, q, args.steps, args.warmup, dev)
-        if want("mix"):
-            log("secondary: Q4_K_M-style mix weights")
-            wts = build_weights(torch, 5, dev)
-            for b in (1, 4, 8):
-                log("secondary: Q4_K_M-style mix, batch", b)
-                sec["q4_k_m_mix_b%d" % b] = sec_stream(
-                    torch, q, 5, wts, b, max(3, args.steps // 2), 2, dev,
-                    "Q4_K_M-style mix (v, down, LM head 128256x4096 in Q6_K), 225 GEMVs, batch %d" % b,
-                    with_gemm=True)
-            del wts
-        if want("q5"):
-            log("secondary: 5-bit types")
-            wts = build_weights(torch, 6, dev)
-            sec["llama3_8b_q5_k"] = sec_stream(torch, q, 6, wts, 1, args.steps, args.warmup, dev,
-                                               "Llama-3-8B-shaped Q5_K, 224 GEMVs, batch 1")
-            del wts
-            torch.cuda.empty_cache()
-            wts = build_weights(torch, 7, dev)
-            sec["tinyllama_q5_0"] = sec_stream(torch, q, 7, wts, 1, args.steps, args.warmup, dev,
-                                               "TinyLlama-shaped Q5_0 stream, 154 GEMVs, batch 1")
-            del wts
-            torch.cuda.empty_cache()
-            sec["prefill_512_q5"] = sec_prefill(torch, q, args.steps, args.warmup, dev, cfg=8)
-        if want("embed"):
-            log("secondary: embedding gathers")
-            sec["embed"] = sec_embed(torch, q, args.steps, args.warmup, dev)
-        if want("dequant"):
-            log("secondary: dequant-only")
-            sec["dequant"] = sec_dequant(torch, q, args.steps, args.warmup, dev)
-        if want("kv"):
-            log("secondary: KV-cache codec")
-            sec["kv_codec"] = sec_kv(torch, q, args.steps, args.warmup, dev)
+    sec = {}
+    want = set(args.secondary)
+    if "mix_batch" in want:
+        log("secondary: the mix at batch 4 and 8")
+        sec["q4_k_m_mix"] = sec_mix_batch(torch, q, args.steps, args.warmup, dev, weights)
+    del P, weights
+    torch.cuda.empty_cache()
+    if "q8_0" in want:
+        log("secondary: Q8_0 single matrix")
+        sec["q8_0_2048"] = sec_q8_0(torch, q, args.steps, args.warmup, dev)
+    if "tinyllama" in want:
+        log("secondary: TinyLlama Q4_0 pass")
+        sec["tinyllama_q4_0"] = sec_pass(torch, q, 2, args.steps, args.warmup, dev,
+                                         "TinyLlama-shaped Q4_0 decode pass, 154 GEMVs, batch 1",
+                                         single_launch_graph=True)
+    if "q4_k" in want:
+        log("secondary: Llama-3-8B Q4_K pass")
+        sec["llama3_8b_q4_k"] = sec_pass(torch, q, 3, args.steps, args.warmup, dev,
+                                         "Llama-3-8B-shaped Q4_K decode pass, 224 GEMVs, batch 1",
+                                         single_launch_graph=True)
+    if "prefill" in want:
+        log("secondary: prefill GEMMs")
+        sec["prefill_512"] = sec_prefill(torch, q, args.steps, args.warmup, dev)
+    if "q5" in want:
+        log("secondary: 5-bit types")
+        sec["q5"] = sec_q5(torch, q, args.steps, args.warmup, dev)
+    if "embed" in want:
+        log("secondary: embedding gathers")
+        sec["embed"] = sec_embed(torch, q, args.steps, args.warmup, dev)
+    if "dequant" in want:
+        log("secondary: dequant-only")
+        sec["dequant"] = sec_dequant(torch, q, args.steps, args.warmup, dev)
+    if "kv" in want:
+        log("secondary: KV-cache codec")
+        sec["kv_codec"] = sec_kv(torch, q, args.steps, args.warmup, dev)
+    if sec:
         line["secondary"] = sec
     print(json.dumps(line), flush=True)
 

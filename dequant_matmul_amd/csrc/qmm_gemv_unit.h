@@ -220,6 +220,17 @@ __device__ __forceinline__ f32x4 wts4(uint32_t q, float dsc, float ndm)
                  __builtin_fmaf(ub2(q), dsc, ndm), __builtin_fmaf(ub3(q), dsc, ndm)};
 }
 
+// The same from four code bytes q_c <= 15 converted as OCP fp8 e4m3 (two per
+// v_cvt_pk_f32_fp8): byte q is q 2^-9 exactly (subnormals and the first
+// normal binade are evenly spaced), so dsc must carry the factor 2^9.
+__device__ __forceinline__ f32x4 wts4_fp8(uint32_t q, float dsc, float ndm)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, true);
+    return f32x4{__builtin_fmaf(a.x, dsc, ndm), __builtin_fmaf(a.y, dsc, ndm), __builtin_fmaf(b.x, dsc, ndm),
+                 __builtin_fmaf(b.y, dsc, ndm)};
+}
+
 __device__ __forceinline__ float dot4_f(const f32x4 &w, const f32x4 &x, float acc)
 {
     acc = __builtin_fmaf(w.x, x.x, acc);
@@ -320,10 +331,62 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
 #pragma unroll
             for (int b = 0; b < B; ++b) acc[r][b] = __builtin_fmaf(d, fin(slo[r][b]) + fin(shi[r][b]), acc[r][b]);
         }
-    } else if constexpr (T == T_Q4_K || T == T_Q5_K) {
+    } else if constexpr (T == T_Q4_K) {
         // unit = (super-block, code group p = u % 4): sub-block 2p in the low
-        // nibbles, 2p+1 in the high nibbles (Q5_K: bit 4 at bit 2p / 2p+1 of
-        // the qh byte of its element)
+        // nibbles, 2p+1 in the high nibbles.  The nibbles are converted two at
+        // a time as OCP fp8 e4m3 bytes (v_cvt_pk_f32_fp8): a byte q <= 15 is
+        // q 2^-9 exactly, so the scale carries the factor 2^9.
+        const int p = u & 3;
+        float dsc0[R], dsc1[R], ndm0[R], ndm1[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            // bytes 2 (p % 2) and 2 (p % 2) + 1 of the three scale dwords
+            const uint32_t sh = 16u * (uint32_t)(p & 1);
+            const uint32_t a = raw[r].hd.y >> sh, b = raw[r].hd.z >> sh, c = raw[r].hd.w >> sh;
+            // (sc_2p, sc_2p+1) and (m_2p, m_2p+1) in bytes 0 and 1: sub-blocks
+            // 0..3 are the low 6 bits of bytes j and j + 4; 4..7 the nibbles of
+            // byte j + 4 with the top 2 bits of bytes j - 4 and j
+            const uint32_t scp = p < 2 ? (a & 0x3f3fu) : ((c & 0x0f0fu) | ((a >> 2) & 0x3030u));
+            const uint32_t mp = p < 2 ? (b & 0x3f3fu) : (((c >> 4) & 0x0f0fu) | ((b >> 2) & 0x3030u));
+            const float d = h2f(raw[r].hd.x & 0xffffu) * 512.f, dmin = h2f(raw[r].hd.x >> 16);
+            dsc0[r] = d * ub0(scp);
+            dsc1[r] = d * ub1(scp);
+            ndm0[r] = -(dmin * ub0(mp));
+            ndm1[r] = -(dmin * ub1(mp));
+        }
+        AccT s0[R][B], s1[R][B];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int r = 0; r < R; ++r) s0[r][b] = s1[r][b] = zero_acc<AccT>();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            f32x4 xl[B], xh[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                xl[b] = xg(i, b);
+                xh[b] = xg(8 + i, b);
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const uint32_t lo = opaque(raw[r].c[i] & 0x0f0f0f0fu);
+                const uint32_t hi = opaque((raw[r].c[i] >> 4) & 0x0f0f0f0fu);
+                const f32x4 wl = wts4_fp8(lo, dsc0[r], ndm0[r]), wh = wts4_fp8(hi, dsc1[r], ndm1[r]);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    s0[r][b] = dot4_f(wl, xl[b], s0[r][b]);
+                    s1[r][b] = dot4_f(wh, xh[b], s1[r][b]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < B; ++b) acc[r][b] += fin(s0[r][b]) + fin(s1[r][b]);
+    } else if constexpr (T == T_Q5_K) {
+        // unit = (super-block, code group p = u % 4): sub-block 2p in the low
+        // nibbles, 2p+1 in the high nibbles; bit 4 at bit 2p / 2p+1 of the
+        // qh byte of its element
         const int p = u & 3;
         float dsc0[R], dsc1[R], ndm0[R], ndm1[R];
 #pragma unroll
@@ -333,8 +396,7 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             q4k_scale_min(raw[r].hd.y, raw[r].hd.z, raw[r].hd.w, 2 * p + 1, sc1, m1);
             const float d = h2f(raw[r].hd.x & 0xffffu), dmin = h2f(raw[r].hd.x >> 16);
             dsc0[r] = d * (float)sc0;
-            // Q4_K high nibbles convert as 16 q
-            dsc1[r] = T == T_Q4_K ? d * (float)sc1 * 0.0625f : d * (float)sc1;
+            dsc1[r] = d * (float)sc1;
             ndm0[r] = -(dmin * (float)m0);
             ndm1[r] = -(dmin * (float)m1);
         }
@@ -354,15 +416,9 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                uint32_t lo, hi;
-                if constexpr (T == T_Q4_K) {
-                    lo = opaque(raw[r].c[i] & 0x0f0f0f0fu);
-                    hi = opaque(raw[r].c[i] & 0xf0f0f0f0u);
-                } else {
-                    const uint32_t c = raw[r].c[i], hb = raw[r].h[i];
-                    lo = opaque((c & 0x0f0f0f0fu) | (((hb >> sh0) & 0x01010101u) << 4));
-                    hi = opaque(((c >> 4) & 0x0f0f0f0fu) | (((hb >> (sh0 + 1u)) & 0x01010101u) << 4));
-                }
+                const uint32_t c = raw[r].c[i], hb = raw[r].h[i];
+                const uint32_t lo = opaque((c & 0x0f0f0f0fu) | (((hb >> sh0) & 0x01010101u) << 4));
+                const uint32_t hi = opaque(((c >> 4) & 0x0f0f0f0fu) | (((hb >> (sh0 + 1u)) & 0x01010101u) << 4));
                 const f32x4 wl = wts4(lo, dsc0[r], ndm0[r]), wh = wts4(hi, dsc1[r], ndm1[r]);
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
