@@ -130,8 +130,14 @@ struct TableProbs {
 // WSTRIDE: dwords of the LDS segment area per wave (0: this type's own size;
 // a launch mixing block types passes the largest, so that the waves' areas
 // do not overlap).
-template <int T, int R, class PS, int NW = 4, bool X_LDS = false, int WSTRIDE = 0>
-__device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint32_t *ws, float *xl, int gw, int tw)
+//
+// X_LDS staging: by default the problem's x (k floats, one segment at most);
+// a caller whose waves work on different column ranges of one row passes the
+// whole x (xsrc, xn floats, at most XMAX) and this wave's offset xoff into
+// the padded LDS copy.
+template <int T, int R, class PS, int NW = 4, bool X_LDS = false, int WSTRIDE = 0, int XMAX = 0>
+__device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint32_t *ws, float *xl, int gw, int tw,
+                                           const float *xsrc = nullptr, int xn = 0, int xoff = 0)
 {
     constexpr int UE = GemvUnit<T>::UE, NRUN = GemvUnit<T>::NRUN;
     using S = SegStage<T, R>;
@@ -141,16 +147,17 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // X_LDS: this thread's share of x is loaded into registers first, so
     // that it is in flight together with the first weight loads (issued
-    // next), and written to LDS after them (stage_x).  Positions past k
-    // read x[0..3] and are not stored.
-    constexpr int XV = X_LDS ? (64 * UE + 4 * 64 * NW - 1) / (4 * 64 * NW) : 1;
+    // next), and written to LDS after them (stage_x).  Positions past the
+    // end read x[0..3] and are not stored.
+    constexpr int XV = X_LDS ? ((XMAX ? XMAX : 64 * UE) + 4 * 64 * NW - 1) / (4 * 64 * NW) : 1;
+    const int xcount = xsrc ? xn : k;
     f32x4 xst[XV];
     if constexpr (X_LDS) {
-        const float *x = P.X(0);
+        const float *x = xsrc ? xsrc : P.X(0);
 #pragma unroll
         for (int j = 0; j < XV; ++j) {
             const int e = 4 * ((int)threadIdx.x + 64 * NW * j);
-            xst[j] = *(const f32x4 *)(x + (e < k ? e : 0));
+            xst[j] = *(const f32x4 *)(x + (e < xcount ? e : 0));
         }
         // keep these loads ahead of the weight loads: the wait for them
         // before the LDS writes then leaves the weight loads in flight
@@ -165,7 +172,7 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
 #pragma unroll
             for (int j = 0; j < XV; ++j) {
                 const int e = 4 * ((int)threadIdx.x + 64 * NW * j);
-                if (e < k)
+                if (e < xcount)
                     *(f32x4 *)(xl + xpad<UE>(e)) = xst[j];
             }
             lds_barrier();
@@ -195,7 +202,7 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
 #pragma unroll
         for (int j = 0; j < NRUN; ++j) {
             const int e = active ? run_elem<T>(lane, j) : 0;
-            xr[j] = X_LDS ? *(const f32x4 *)(xl + xpad<UE>(e)) : *(const f32x4 *)(P.X(pp) + e);
+            xr[j] = X_LDS ? *(const f32x4 *)(xl + xoff + xpad<UE>(e)) : *(const f32x4 *)(P.X(pp) + e);
         }
     };
     const XFromRegs<T> xg{xr};
@@ -406,6 +413,48 @@ __global__ void __launch_bounds__(64 * NW) gemv3s_kernel(const StageGroups G, in
         case T_Q8_0: gemv2_body<T_Q8_0, 1, TableProbs, NW, true, WSDW>(P, k, G.rb[g], ws, xl, gw, tw); break;
         default: gemv2_body<T_Q5_0, 1, TableProbs, NW, true, WSDW>(P, k, G.rb[g], ws, xl, gw, tw); break;
         }
+    }
+}
+
+// --------------------------------------------------------------- gemv4 --
+// Batch 1, k spanning several segments: the workgroup owns rwg consecutive
+// rows and its waves split k by segment -- wave w takes segment w % nseg,
+// the waves of one segment split the rows, and each runs the one-segment
+// loop (gemv2_body) on its segment's columns with that slice of x in its
+// registers (the row pitch stays the full row).  Per-(segment, row) partial
+// sums meet in LDS and are added in segment order, so the result does not
+// depend on timing.
+constexpr int GEMV4_XMAX = 16384;  // the longest x the kernel stages in LDS
+constexpr int GEMV4_PART = 4096;   // LDS floats for the partial sums (nseg * rwg)
+
+template <int T, int NW>
+__global__ void __launch_bounds__(64 * NW)
+gemv4_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
+             float *__restrict__ y, int rwg, int nseg)
+{
+    using S = SegStage<T, 1>;
+    constexpr int UE = GemvUnit<T>::UE;
+    constexpr int XMAX = GEMV4_XMAX;
+    __shared__ __attribute__((aligned(16))) float xl[XMAX + XMAX / UE * 4];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : NW * S::LDS_DW];
+    __shared__ float part[GEMV4_PART];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (int)blockIdx.x * rwg;
+    const int nr = min(rwg, n - row0);
+    const int wps = NW / nseg;                 // waves per segment
+    const int seg = wave % nseg, sub = wave / nseg;
+    // every wave stages its share of the whole x once (waves past wps * nseg
+    // too) and takes its segment's slice from LDS
+    const int kseg = min(S::SEGE, k - seg * S::SEGE);
+    const OneProb P{w + (int64_t)row0 * rb + (int64_t)seg * S::SEGB, x, part + seg * rwg, sub < wps ? nr : 0};
+    gemv2_body<T, 1, OneProb, NW, true, 0, XMAX>(P, kseg, rb, ws, xl, sub < wps ? sub : 0, wps, x, k,
+                                                 xpad<UE>(seg * S::SEGE));
+    __syncthreads();
+    for (int t = threadIdx.x; t < nr; t += 64 * NW) {
+        float v = part[t];
+        for (int g = 1; g < nseg; ++g)
+            v += part[g * rwg + t];
+        y[row0 + t] = v;
     }
 }
 
@@ -755,6 +804,22 @@ static hipError_t launch_b1_lds(const uint8_t *w, int64_t n, int64_t k, size_t r
     return hipGetLastError();
 }
 
+template <int T, int NW>
+static hipError_t launch_b1_split(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
+                                  int nseg, hipStream_t s)
+{
+    const int cus = device_cu_count();
+    if (cus == 0)
+        return hipErrorInvalidValue;
+    int64_t rwg = (n + cus - 1) / cus;
+    const int64_t cap = GEMV4_PART / nseg;
+    rwg = rwg < cap ? rwg : cap;
+    const int64_t grid = (n + rwg - 1) / rwg;
+    hipLaunchKernelGGL((gemv4_kernel<T, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, w, (int)n, (int)k,
+                       (int64_t)rb, x, y, (int)rwg, nseg);
+    return hipGetLastError();
+}
+
 template <int T, int B, int R>
 static hipError_t launch_tbr(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
                              hipStream_t s)
@@ -788,6 +853,18 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
                 return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
             }
             return launch_b1_xlds<T, 1, 8>(w, n, k, rb, x, y, s);
+        }
+        const int nseg = (int)((k + 64 * GemvUnit<T>::UE - 1) / (64 * GemvUnit<T>::UE));
+        if (nseg <= 8 && k <= GEMV4_XMAX) {
+            // the segments split over the waves of a workgroup, the whole x
+            // staged in LDS once (gemv4): as many waves per segment as fit in 8
+            switch (nseg) {
+            case 2: case 4: case 8: return launch_b1_split<T, 8>(w, n, k, rb, x, y, nseg, s);
+            case 3: return launch_b1_split<T, 6>(w, n, k, rb, x, y, nseg, s);
+            case 5: return launch_b1_split<T, 5>(w, n, k, rb, x, y, nseg, s);
+            case 6: return launch_b1_split<T, 6>(w, n, k, rb, x, y, nseg, s);
+            default: return launch_b1_split<T, 7>(w, n, k, rb, x, y, nseg, s);
+            }
         }
         if (k <= 16384) {
             // two rows per item, unless that leaves compute units without a

@@ -510,3 +510,24 @@ def test_gemv_k_quant_scale_ratio(t, batch):
         ref, absum = oracle.gemv(t, w, n, k, x)
         got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
         check_tol(got, ref, absum, GEMV_TOL, "scale ratio %s %s" % (G.NAMES[t], mode))
+
+
+@pytest.mark.parametrize("t", TYPES)
+@pytest.mark.parametrize("nseg", [2, 3, 4, 5, 6, 7, 8])
+def test_gemv_split_segments(t, nseg):
+    """Batch 1 with k spanning 2..8 segments of 64 lane-units (the waves of a
+    workgroup split k by segment, the partial sums meet in LDS), a partial
+    last segment and a ragged row count over several workgroups; then the
+    same call again gives the same bits."""
+    be = G.BLOCK_ELEMS[t]
+    sege = 64 * (64 if be == 256 else 32)
+    k = nseg * sege - 3 * be
+    n = 700
+    say("gemv split segments", G.NAMES[t], n, k, nseg)
+    w = G.gen_weights(t, n, k, seed=1100 + nseg)
+    x = G.gen_x(k, 1, seed=1200 + nseg)
+    ref, absum = oracle.gemv(t, w, n, k, x)
+    wd, xd = upload(w), upload(x)
+    got = q.gemv(wd, t, n, k, xd).cpu().numpy()
+    check_tol(got, ref, absum, GEMV_TOL, "split segments %s k=%d" % (G.NAMES[t], k))
+    assert np.array_equal(q.gemv(wd, t, n, k, xd).cpu().numpy(), got)
