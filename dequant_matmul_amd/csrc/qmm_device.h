@@ -26,6 +26,7 @@ enum : int { T_Q4_0 = 0, T_Q8_0 = 1, T_Q4_K = 2, T_Q6_K = 3, T_Q5_0 = 4, T_Q5_K 
 // lower to memcpy, which can keep arrays of them in scratch memory.)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 
 template <int T> struct Fmt;
 template <> struct Fmt<T_Q4_0> { static constexpr int BE = 32, BB = 18; };

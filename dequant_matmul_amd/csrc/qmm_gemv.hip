@@ -9,22 +9,24 @@
 //   - Work is split into lane-units: one Q8_0 / Q4_0 block (32 elements) or a
 //     64-element quarter of a Q4_K / Q6_K super-block.  A segment is 64
 //     consecutive units of a row, i.e. one unit per lane of a wavefront.
-//   - Weights are read with 16-byte loads.  Q4_K blocks (144 B) keep 16-byte
-//     alignment, so each lane loads its unit straight into registers.  Blocks
-//     of 34, 18, 22 and 210 bytes are only 2-byte aligned (and the 176-byte
-//     Q5_K blocks take the same path): the wavefront copies the
-//     row segment into LDS with fully coalesced loads (64 lanes x 16 B
-//     contiguous) and each lane reads its unit back with aligned dword reads,
-//     realigned in registers with v_alignbyte_b32.
+//   - Weights are read with fully coalesced 16-byte loads: the wavefront
+//     copies each row segment (64 lanes x 16 B contiguous per load) into its
+//     LDS area and each lane reads its unit back (aligned dword reads,
+//     realigned in registers with v_alignbyte_b32 where blocks are only
+//     2-byte aligned).  Measured on MI355X this beats per-lane loads of the
+//     16-byte-aligned Q4_K units (three 16-byte loads per lane at a 144-byte
+//     stride): 14336 x 4096 Q4_K 10.3 -> 8.9 us, 4096 x 4096 5.3 -> 4.3 us.
 //   - Codes are converted with a few bit operations per dword plus the byte
-//     converts (v_cvt_f32_ubyteN, or the sign-extending SDWA convert), and
+//     converts (v_cvt_f32_ubyteN, or the sign-extending SDWA convert), or for
+//     Q4_K straight inside the weight-forming fma (a nibble alone in a
+//     16-bit half is an exact fp16 subnormal, read by v_fma_mix_f32), and
 //     every product uses the element's own weight: integer code offsets
 //     (-8, -16, -32) become signed bytes before the convert, the K-quant
 //     weights d sc q - dmin m are formed per element with one fma.  Sums are
 //     fp32 per block or sub-block; integer-code scales are applied once per
 //     (sub-)block.
-//   - Per-lane partial sums are reduced across the wavefront with cross-lane
-//     shuffles; lane 0 writes y.
+//   - Per-lane partial sums of 8 rows at a time are reduced together
+//     through LDS (8 lanes per row), one store per 8 rows.
 //   - Loads are issued without branches (out-of-range lanes read a valid
 //     address and discard it): the compiler otherwise sinks a predicated load
 //     into its branch and waits for it at once, serializing the memory
@@ -44,10 +46,15 @@
 //                 each wave from L2: one launch instead of one per matrix.
 //   gemv3m_kernel the table with one x shared by every problem (q / k / v,
 //                 gate / up): x staged in LDS as in gemv3.
-//   gemv1_kernel  batch 1, k spanning several segments: x is staged in LDS
-//                 once per workgroup; otherwise as gemv3 (two rows per item,
-//                 one when there are too few rows to give every CU a
-//                 workgroup).
+//   gemv3s_kernel the stage launch of the decode pass: up to three groups of
+//                 problems of different block types (same lane-unit size)
+//                 sharing one x, wave slots split by weight bytes.
+//   gemv4_kernel  batch 1, k of two to eight segments (up to 16384): a
+//                 workgroup owns a block of rows, its waves split the
+//                 segments, x is staged whole in LDS once, and the partial
+//                 sums meet in LDS.
+//   gemv1_kernel  batch 1, longer k: x is staged in LDS per segment,
+//                 otherwise as gemv3.
 //   gemv_kernel   batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K (and unaligned
 //                 batch-1 rows): x
 //                 segment and weight segments staged in LDS per workgroup.
@@ -97,6 +104,7 @@ struct OneProb {
     __device__ __forceinline__ int total_rg(int R) const { return (n + R - 1) / R; }
     __device__ __forceinline__ int find(int) const { return 0; }
     __device__ __forceinline__ int rg_begin(int) const { return 0; }
+    __device__ __forceinline__ int rg_end(int, int R) const { return (n + R - 1) / R; }
     __device__ __forceinline__ const uint8_t *W(int) const { return w; }
     __device__ __forceinline__ const float *X(int) const { return x; }
     __device__ __forceinline__ float *Y(int) const { return y; }
@@ -113,6 +121,7 @@ struct TableProbs {
         return pp;
     }
     __device__ __forceinline__ int rg_begin(int pp) const { return P.rg0[pp]; }
+    __device__ __forceinline__ int rg_end(int pp, int) const { return P.rg0[pp + 1]; }
     __device__ __forceinline__ const uint8_t *W(int pp) const { return P.w[pp]; }
     __device__ __forceinline__ const float *X(int pp) const { return P.x[pp]; }
     __device__ __forceinline__ float *Y(int pp) const { return P.y[pp]; }
@@ -141,7 +150,6 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
 {
     constexpr int UE = GemvUnit<T>::UE, NRUN = GemvUnit<T>::NRUN;
     using S = SegStage<T, R>;
-    constexpr bool DIRECT = (T == T_Q4_K);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -179,8 +187,7 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
         }
     };
     // each wave takes a contiguous run of row groups (run lengths differ by
-    // at most one, so every wave has work when there are enough), so that
-    // its results form contiguous runs of y (stored 64 at a time, below)
+    // at most one, so every wave has work when there are enough)
     const int nrg = P.total_rg(R);
     const int q = nrg / tw, rem = nrg - q * tw;    // one 32-bit division
     const int rgs = gw * q + min(gw, rem);
@@ -188,13 +195,40 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     const bool active = lane < k / UE;
     const int cpr = k / Fmt<T>::BE * Fmt<T>::BB / 16;
 
-    // problem and first row of item it (past the end: the last item)
-    auto locate = [&](int it, int &pp, int &row0) __attribute__((always_inline)) {
-        it = min(it, max(nit - 1, 0));
-        const int rg = min(rgs + it, nrg - 1);   // a wave with no item: the last row group
-        pp = P.find(rg);
-        row0 = (rg - P.rg_begin(pp)) * R;
+    // Problem of an item: a cursor walks the problems as the items advance
+    // (items are visited in increasing order), so that the problem's
+    // pointers and sizes are read from the table only when it changes, not
+    // per item (each such scalar read is a wait in the item loop).
+    struct Cur {
+        int pp, beg, end, n;
+        const uint8_t *w;
     };
+    auto cur_set = [&](Cur &c, int pp) __attribute__((always_inline)) {
+        c.pp = pp;
+        c.beg = P.rg_begin(pp);
+        c.end = P.rg_end(pp, R);
+        c.n = P.N(pp);
+        c.w = P.W(pp);
+    };
+    // first row group of item it (past the end: the last item; a wave with
+    // no item: the last row group)
+    auto item_rg = [&](int it) __attribute__((always_inline)) {
+        it = min(it, max(nit - 1, 0));
+        return min(rgs + it, nrg - 1);
+    };
+    auto locate = [&](Cur &c, int it) __attribute__((always_inline)) {
+        const int rg = item_rg(it);
+        if (rg >= c.end) {
+            int pp = c.pp + 1;
+            while (rg >= P.rg_end(pp, R))
+                ++pp;
+            cur_set(c, pp);
+        }
+        return (rg - c.beg) * R;   // first row of the item in its problem
+    };
+    Cur cl, cs;                    // the load and the compute cursors
+    cur_set(cl, P.find(item_rg(0)));
+    cs = cl;
 
     // this lane's slice of x for the current problem
     f32x4 xr[NRUN];
@@ -211,135 +245,94 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r][0] = 0.f;
 
-    int p0, r0;
-    locate(0, p0, r0);
-    int xp = p0;
+    int xp = cs.pp;
     if constexpr (!X_LDS)
         load_x(xp);
 
-    // Two items of weight bytes in flight while an item computes: three
-    // prefetch register sets, the loop unrolled by three so that each has a
-    // fixed place.  An item computes in place and its set is reloaded (for
-    // item it + 3) only after its last use, with a scheduling barrier in
-    // between: a reload scheduled above the use would need other registers
-    // and a copy back at the loop edge, which waits for the load.  Prefetches
-    // past the wave's last item read offset 0 in every lane (one cache line,
-    // no branch: a load under a branch is waited for at once).  Lanes past k
-    // compute on offset-0 bytes and contribute 0 (select, not branch).
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    // Row results collect in lane (row - blk_row) of res and leave as one
-    // coalesced store per 64 rows (or at a problem change / the end); a
-    // one-lane store per row costs a divergent branch and a store each.
-    float res = 0.f;
-    int blk_row = 0, blk_cnt = 0, blk_pp = 0;
+    // Row results: each lane's partial sum of a row goes to LDS (one slot of
+    // 64 floats per row, RG rows per group); a full group (or a problem
+    // change, or the end) is reduced across lanes at once, 8 lanes per row
+    // (two 128-bit reads, 7 adds and 3 DPP steps per 8 rows instead of a
+    // full 64-lane reduction per row), and leaves as one store per 8 rows.
+    constexpr int RG = 8;
+    static_assert(R <= RG, "rows per item above the reduction group");
+    __shared__ __attribute__((aligned(16))) float redbuf[NW * RG * 64];
+    float *const red = redbuf + wave * (RG * 64);
+    int blk_row = 0, blk_cnt = 0, blk_pp = -1, blk_n = 0;
+    float *blk_y = nullptr;
     auto flush = [&]() __attribute__((always_inline)) {
         if (blk_cnt > 0) {
-            const int row = blk_row + lane;
-            if (lane < blk_cnt && row < P.N(blk_pp))
-                P.Y(blk_pp)[row] = res;
+            wave_lds_sync();
+            const int rr = lane >> 3, q8 = lane & 7;
+            const f32x4 a = *(const f32x4 *)(red + 8 * lane), b = *(const f32x4 *)(red + 8 * lane + 4);
+            float v = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+            v += dpp_f(v, 0xB1);    // lanes 1,0,3,2 of each quad
+            v += dpp_f(v, 0x4E);    // lanes 2,3,0,1 of each quad
+            v += dpp_f(v, 0x141);   // the other quad of each 8 lanes
+            const int row = blk_row + rr;
+            if (q8 == 0 && rr < blk_cnt && row < blk_n)
+                blk_y[row] = v;
+            wave_lds_sync();
         }
         blk_cnt = 0;
     };
-    auto finish = [&](int pp, int row0) __attribute__((always_inline)) {
-        if (blk_cnt + R > 64 || (blk_cnt > 0 && pp != blk_pp))
+    auto finish = [&](int row0) __attribute__((always_inline)) {
+        if (blk_cnt + R > RG || (blk_cnt > 0 && cs.pp != blk_pp))
             flush();
         if (blk_cnt == 0) {
             blk_row = row0;
-            blk_pp = pp;
+            if (cs.pp != blk_pp) {
+                blk_pp = cs.pp;
+                blk_n = cs.n;
+                blk_y = P.Y(blk_pp);
+            }
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float v = wave_sum_hi(active ? acc[r][0] : 0.f);
-            const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-            res = lane == blk_cnt + r ? tot : res;
+            red[(blk_cnt + r) * 64 + lane] = active ? acc[r][0] : 0.f;
             acc[r][0] = 0.f;
         }
         blk_cnt += R;
     };
-    if constexpr (DIRECT) {
-        URaw<T> pr[3][R];
-        auto load = [&](int it, URaw<T> (&dst)[R]) __attribute__((always_inline)) {
-            int pp, row0;
-            locate(it, pp, row0);
-            const uint8_t *w = P.W(pp);
-            const int n = P.N(pp);
-            const bool live = it < nit;   // past the wave's last item: a dummy load of offset 0
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const bool ok = live && active && row0 + r < n;
-                raw_from_global_q4k(w + (ok ? (int64_t)(row0 + r) * rb : 0), ok ? lane : 0, dst[r]);
-            }
-        };
-        load(0, pr[0]);
-        load(1, pr[1]);
-        load(2, pr[2]);
-        if constexpr (X_LDS) {
-            stage_x();
-            load_x(xp);
-        }
-        auto step = [&](auto bc, int it) __attribute__((always_inline)) {
-            constexpr int B = decltype(bc)::value;
-            int pp, row0;
-            locate(it, pp, row0);
-            if (pp != xp) {   // wave-uniform: the next problem's x
-                xp = pp;
-                load_x(xp);
-            }
-            unit_dot<T, 1, R>(pr[B], lane, xg, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            load(it + 3, pr[B]);
-            finish(pp, row0);
-        };
-        int it = 0;
-        for (; it + 2 < nit; it += 3) {
-            step(I0{}, it);
-            step(I1{}, it + 1);
-            step(I2{}, it + 2);
-        }
-        if (it < nit)
-            step(I0{}, it);
-        if (it + 1 < nit)
-            step(I1{}, it + 1);
-        flush();
-    } else {
-        // LDS-staged rows: one prefetch register set suffices, since it is
-        // emptied into LDS before being refilled (no copy of an in-flight
-        // load); measured faster than three sets for these types
-        static_assert(WSTRIDE == 0 || WSTRIDE >= S::LDS_DW, "LDS segment area too small");
-        uint32_t *mw = ws + wave * (WSTRIDE ? WSTRIDE : S::LDS_DW);
-        S st;
-        auto load = [&](int it) __attribute__((always_inline)) {
-            int pp, row0;
-            locate(it, pp, row0);
-            // past the wave's last item: no row is in range, every chunk reads offset 0
-            st.load(P.W(pp), rb, it < nit ? P.N(pp) : 0, row0, 0, cpr, lane);
-        };
-        load(0);
-        if constexpr (X_LDS) {
-            stage_x();
-            load_x(xp);
-        }
-        for (int it = 0; it < nit; ++it) {
-            int pp, row0;
-            locate(it, pp, row0);
-            if (pp != xp) {
-                xp = pp;
-                load_x(xp);
-            }
-            st.store(mw, lane);
-            wave_lds_sync();
-            load(it + 1);
-            URaw<T> cur[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
-            unit_dot<T, 1, R>(cur, lane, xg, acc);
-            finish(pp, row0);
-            wave_lds_sync();
-        }
-        flush();
+
+    // Rows are staged through LDS: the wave loads an item's row segments
+    // with fully coalesced 16-byte loads (64 lanes, contiguous), stores them
+    // to its LDS area and each lane reads its unit back.  One prefetch
+    // register set: it is emptied into LDS before being refilled (no copy of
+    // an in-flight load).  Prefetches past the wave's last item read offset
+    // 0 in every lane (one cache line, no branch: a load under a branch is
+    // waited for at once).  Lanes past k compute on offset-0 bytes and
+    // contribute 0 (select, not branch).
+    static_assert(WSTRIDE == 0 || WSTRIDE >= S::LDS_DW, "LDS segment area too small");
+    uint32_t *mw = ws + wave * (WSTRIDE ? WSTRIDE : S::LDS_DW);
+    S st;
+    auto load = [&](int it) __attribute__((always_inline)) {
+        const int row0 = locate(cl, it);
+        // past the wave's last item: no row is in range, every chunk reads offset 0
+        st.load(cl.w, rb, it < nit ? cl.n : 0, row0, 0, cpr, lane);
+    };
+    load(0);
+    if constexpr (X_LDS) {
+        stage_x();
+        load_x(xp);
     }
+    for (int it = 0; it < nit; ++it) {
+        const int row0 = locate(cs, it);
+        if (cs.pp != xp) {   // wave-uniform: the next problem's x
+            xp = cs.pp;
+            load_x(xp);
+        }
+        st.store(mw, lane);
+        wave_lds_sync();
+        load(it + 1);
+        URaw<T> cur[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) raw_from_lds<T>(mw + r * S::RS, lane, cur[r]);
+        unit_dot<T, 1, R>(cur, lane, xg, acc);
+        finish(row0);
+        wave_lds_sync();
+    }
+    flush();
 }
 
 // Batch 1, one problem, x staged in LDS, NW wavefronts per workgroup (one
@@ -350,7 +343,7 @@ gemv3_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
              float *__restrict__ y)
 {
     __shared__ __attribute__((aligned(16))) float xl[64 * (GemvUnit<T>::UE + 4)];
-    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : NW * SegStage<T, R>::LDS_DW];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[NW * SegStage<T, R>::LDS_DW];
     const OneProb P{w, x, y, n};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     gemv2_body<T, R, OneProb, NW, true>(P, k, rb, ws, xl, blockIdx.x * NW + wave, gridDim.x * NW);
@@ -360,7 +353,7 @@ template <int T, int R>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4)))
 gemv2m_kernel(const GemvProbs Pt, int k, int64_t rb)
 {
-    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : 4 * SegStage<T, R>::LDS_DW];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[4 * SegStage<T, R>::LDS_DW];
     const TableProbs P{Pt};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     gemv2_body<T, R>(P, k, rb, ws, nullptr, blockIdx.x * 4 + wave, gridDim.x * 4);
@@ -374,7 +367,7 @@ __global__ void __launch_bounds__(64 * NW)
 gemv3m_kernel(const GemvProbs Pt, int k, int64_t rb)
 {
     __shared__ __attribute__((aligned(16))) float xl[64 * (GemvUnit<T>::UE + 4)];
-    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : NW * SegStage<T, R>::LDS_DW];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[NW * SegStage<T, R>::LDS_DW];
     const TableProbs P{Pt};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     gemv2_body<T, R, TableProbs, NW, true>(P, k, rb, ws, xl, blockIdx.x * NW + wave, gridDim.x * NW);
@@ -436,7 +429,7 @@ gemv4_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
     constexpr int UE = GemvUnit<T>::UE;
     constexpr int XMAX = GEMV4_XMAX;
     __shared__ __attribute__((aligned(16))) float xl[XMAX + XMAX / UE * 4];
-    __shared__ __attribute__((aligned(16))) uint32_t ws[T == T_Q4_K ? 4 : NW * S::LDS_DW];
+    __shared__ __attribute__((aligned(16))) uint32_t ws[NW * S::LDS_DW];
     __shared__ float part[GEMV4_PART];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row0 = (int)blockIdx.x * rwg;
@@ -448,7 +441,7 @@ gemv4_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
     const int kseg = min(S::SEGE, k - seg * S::SEGE);
     const OneProb P{w + (int64_t)row0 * rb + (int64_t)seg * S::SEGB, x, part + seg * rwg, sub < wps ? nr : 0};
     gemv2_body<T, 1, OneProb, NW, true, 0, XMAX>(P, kseg, rb, ws, xl, sub < wps ? sub : 0, wps, x, k,
-                                                 xpad<UE>(seg * S::SEGE));
+                                                    xpad<UE>(seg * S::SEGE));
     __syncthreads();
     for (int t = threadIdx.x; t < nr; t += 64 * NW) {
         float v = part[t];

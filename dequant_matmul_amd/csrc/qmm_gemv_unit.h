@@ -130,18 +130,6 @@ __device__ __forceinline__ void raw_from_lds(const uint32_t *seg, int u, URaw<T>
     }
 }
 
-// Q4_K unit u straight from global memory (super-blocks are 16-byte aligned).
-__device__ __forceinline__ void raw_from_global_q4k(const uint8_t *seg, int u, URaw<T_Q4_K> &r)
-{
-    const uint8_t *blk = seg + 144 * (u >> 2);
-    const int p = u & 3;
-    r.hd = *(const u32x4 *)blk;
-    const u32x4 c0 = *(const u32x4 *)(blk + 16 + 32 * p);
-    const u32x4 c1 = *(const u32x4 *)(blk + 32 + 32 * p);
-    r.c[0] = c0.x; r.c[1] = c0.y; r.c[2] = c0.z; r.c[3] = c0.w;
-    r.c[4] = c1.x; r.c[5] = c1.y; r.c[6] = c1.z; r.c[7] = c1.w;
-}
-
 // ------------------------------------------------------------- unit dot --
 
 __device__ __forceinline__ float dot4_u(uint32_t q, const f32x4 &x, float acc)
@@ -218,17 +206,6 @@ __device__ __forceinline__ f32x4 wts4(uint32_t q, float dsc, float ndm)
 {
     return f32x4{__builtin_fmaf(ub0(q), dsc, ndm), __builtin_fmaf(ub1(q), dsc, ndm),
                  __builtin_fmaf(ub2(q), dsc, ndm), __builtin_fmaf(ub3(q), dsc, ndm)};
-}
-
-// The same from four code bytes q_c <= 15 converted as OCP fp8 e4m3 (two per
-// v_cvt_pk_f32_fp8): byte q is q 2^-9 exactly (subnormals and the first
-// normal binade are evenly spaced), so dsc must carry the factor 2^9.
-__device__ __forceinline__ f32x4 wts4_fp8(uint32_t q, float dsc, float ndm)
-{
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, false), b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, true);
-    return f32x4{__builtin_fmaf(a.x, dsc, ndm), __builtin_fmaf(a.y, dsc, ndm), __builtin_fmaf(b.x, dsc, ndm),
-                 __builtin_fmaf(b.y, dsc, ndm)};
 }
 
 __device__ __forceinline__ float dot4_f(const f32x4 &w, const f32x4 &x, float acc)
@@ -333,9 +310,11 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
         }
     } else if constexpr (T == T_Q4_K) {
         // unit = (super-block, code group p = u % 4): sub-block 2p in the low
-        // nibbles, 2p+1 in the high nibbles.  The nibbles are converted two at
-        // a time as OCP fp8 e4m3 bytes (v_cvt_pk_f32_fp8): a byte q <= 15 is
-        // q 2^-9 exactly, so the scale carries the factor 2^9.
+        // nibbles, 2p+1 in the high nibbles.  A nibble q alone in bits 0..3
+        // (or 4..7) of a 16-bit half is the fp16 subnormal q 2^-24 (q 2^-20),
+        // exactly; the fma that forms the weight takes the half as it is
+        // (v_fma_mix_f32) with the scale times 2^24 (2^20): one masking per
+        // two weights and no separate convert.
         const int p = u & 3;
         float dsc0[R], dsc1[R], ndm0[R], ndm1[R];
 #pragma unroll
@@ -348,17 +327,19 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             // byte j + 4 with the top 2 bits of bytes j - 4 and j
             const uint32_t scp = p < 2 ? (a & 0x3f3fu) : ((c & 0x0f0fu) | ((a >> 2) & 0x3030u));
             const uint32_t mp = p < 2 ? (b & 0x3f3fu) : (((c >> 4) & 0x0f0fu) | ((b >> 2) & 0x3030u));
-            const float d = h2f(raw[r].hd.x & 0xffffu) * 512.f, dmin = h2f(raw[r].hd.x >> 16);
+            const float d = h2f(raw[r].hd.x & 0xffffu) * 16777216.f, dmin = h2f(raw[r].hd.x >> 16);
             dsc0[r] = d * ub0(scp);
-            dsc1[r] = d * ub1(scp);
+            dsc1[r] = d * 0.0625f * ub1(scp);
             ndm0[r] = -(dmin * ub0(mp));
             ndm1[r] = -(dmin * ub1(mp));
         }
-        AccT s0[R][B], s1[R][B];
+        // one chain per sub-block: the fma latency is covered by the other
+        // chain and the weight forming between them
+        float s0[R][B], s1[R][B];
 #pragma unroll
         for (int b = 0; b < B; ++b)
 #pragma unroll
-            for (int r = 0; r < R; ++r) s0[r][b] = s1[r][b] = zero_acc<AccT>();
+            for (int r = 0; r < R; ++r) s0[r][b] = s1[r][b] = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             f32x4 xl[B], xh[B];
@@ -369,9 +350,19 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             }
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const uint32_t lo = opaque(raw[r].c[i] & 0x0f0f0f0fu);
-                const uint32_t hi = opaque((raw[r].c[i] >> 4) & 0x0f0f0f0fu);
-                const f32x4 wl = wts4_fp8(lo, dsc0[r], ndm0[r]), wh = wts4_fp8(hi, dsc1[r], ndm1[r]);
+                // bytes 0..3 of the code dword are elements 4i..4i+3 (low
+                // nibbles) and 32+4i..32+4i+3 (high nibbles): halves of
+                // (c & 0x000f000f) are elements 0 and 2, of (c & 0x00f000f0)
+                // 32 and 34, and the same of c >> 8 elements 1, 3, 33, 35
+                const uint32_t c = raw[r].c[i], c8 = c >> 8;
+                const h16x2 e02 = __builtin_bit_cast(h16x2, opaque(c & 0x000f000fu));
+                const h16x2 e13 = __builtin_bit_cast(h16x2, opaque(c8 & 0x000f000fu));
+                const h16x2 f02 = __builtin_bit_cast(h16x2, opaque(c & 0x00f000f0u));
+                const h16x2 f13 = __builtin_bit_cast(h16x2, opaque(c8 & 0x00f000f0u));
+                const f32x4 wl{__builtin_fmaf((float)e02.x, dsc0[r], ndm0[r]), __builtin_fmaf((float)e13.x, dsc0[r], ndm0[r]),
+                               __builtin_fmaf((float)e02.y, dsc0[r], ndm0[r]), __builtin_fmaf((float)e13.y, dsc0[r], ndm0[r])};
+                const f32x4 wh{__builtin_fmaf((float)f02.x, dsc1[r], ndm1[r]), __builtin_fmaf((float)f13.x, dsc1[r], ndm1[r]),
+                               __builtin_fmaf((float)f02.y, dsc1[r], ndm1[r]), __builtin_fmaf((float)f13.y, dsc1[r], ndm1[r])};
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     s0[r][b] = dot4_f(wl, xl[b], s0[r][b]);
@@ -382,7 +373,7 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] += fin(s0[r][b]) + fin(s1[r][b]);
+            for (int b = 0; b < B; ++b) acc[r][b] += s0[r][b] + s1[r][b];
     } else if constexpr (T == T_Q5_K) {
         // unit = (super-block, code group p = u % 4): sub-block 2p in the low
         // nibbles, 2p+1 in the high nibbles; bit 4 at bit 2p / 2p+1 of the
