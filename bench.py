@@ -308,13 +308,14 @@ def _cpu_rate(items, target_s):
     return done / used, ran, used
 
 
-def cpu_baselines(target_s, mix_host=None):
+def cpu_baselines(target_s, mix_host=None, head_s=10.0):
     """The oracle (plain C, exact fp32 dequant then fp64 dot products, OpenMP
     over rows) on the host, on 1 thread and on every core, over bounded
     samples of each workload: the same matrices (same seeds) as the GPU runs,
     taken in chunks of rows (every matrix of a layer in turn, then the next
-    chunk) until about target_s seconds are spent; for the prefill GEMM,
-    rows of one 512-token chunk, one at a time."""
+    chunk) until about target_s seconds are spent (head_s for the headline
+    workload, the mix at batch 1); for the prefill GEMM, rows of one
+    512-token chunk, one at a time."""
     import oracle
     allc = oracle.max_threads()
 
@@ -352,7 +353,8 @@ def cpu_baselines(target_s, mix_host=None):
         items = gemv_items(mats)
         for nt in (1, allc):
             oracle.set_threads(nt)
-            rate, ran, used = _cpu_rate(items if nt > 1 else items[:max(1, len(items) // 4)], target_s)
+            rate, ran, used = _cpu_rate(items if nt > 1 else items[:max(1, len(items) // 4)],
+                                        head_s if name == "q4_k_m_mix_b1" else target_s)
             rates.setdefault(name, {})["1_thread" if nt == 1 else "all_cores"] = {
                 "value": round(rate / 1e9, 4), "unit": "GB/s", "threads": nt,
                 "sample": "row chunks of 256 of %s, in turn: %d chunks, %.1f s" % (what, ran, used)}
