@@ -708,8 +708,8 @@ static hipError_t launch_stage_t(StageGroups &G, const int64_t *bytes, int64_t r
         return hipErrorInvalidValue;
     const int64_t want = (rows + NW - 1) / NW;
     const int grid = (int)(want < cus ? want : cus);
-    // wave slots in proportion to the groups' weight bytes, at least one and
-    // at most one per row for each group
+    // wave slots in proportion to the groups' weighted bytes, at least one
+    // and at most one per row for each group
     const int tot = grid * NW;
     int64_t btot = 0;
     for (int g = 0; g < G.ng; ++g)
@@ -771,7 +771,11 @@ hipError_t launch_gemv_stage(int ng, const int *type, const int *np, const void 
             P.y[j] = y[i];
             P.n[j] = (int)n[i];
             P.rg0[j + 1] = P.rg0[j] + (int)n[i];
-            bytes[g] += n[i] * G.rb[g];
+            // Q6_K rows take longer per byte than Q4_K rows (2-byte-aligned
+            // blocks read back from LDS with realignment): they get 1.4x
+            // their byte share of the waves (q|k|v of the Q4_K_M-style mix:
+            // 8.2 -> 7.9 us; 0.6x / 2x / 3x: 9.0 / 8.2 / 8.5 us)
+            bytes[g] += n[i] * G.rb[g] * (t == T_Q6_K ? 14 : 10) / 10;
         }
         rows += P.rg0[P.np];
     }
