@@ -13,19 +13,22 @@
 //     the fp32 input.  sh is a power of two per (row b, super-block) that puts
 //     the block's largest |x| in [2^14, 2^15): no fp16 overflow, and both
 //     parts stay normal for every element down to 2^-29 of the largest.
-//   B (256 x 16, fp16): 16 weight rows.  Q6_K: (q - 32) * scale, an integer
-//     of magnitude at most 2048 that fp16 holds exactly, formed by one fused
-//     fp16 multiply-add from a biased code; the super-block scale d is applied
-//     to the fp32 sums.  Q4_K: the weight d sc q - dmin m itself, formed per
-//     element in fp32 exactly as the dequantizer forms it (after a power of
-//     two 2^s per super-block that keeps it below 2^15), and split into
-//     hi = fp16(w) and lo = fp16((w - hi) 2^11): two B operands, whose sum
-//     holds every weight of the block to 22 bits (exactly when d and dmin lie
-//     within 2^8 of each other).  No cancellation happens after a rounding:
-//     a row of zero weights gives exactly 0.
-//   C (16 x 16, fp32): the sum over the super-block; then, per row j and
-//     batch b, y[b][j] += 2^-sh (C_hi + 2^-11 C_lo) (Q6_K: times d; Q4_K:
-//     both weight parts, times 2^-s) in fp32.
+//   B (256 x 16, fp16): 16 weight rows, two operands whose sum is the
+//     weight, so that every product is taken with the element's own weight.
+//     Q6_K: (q - 32)(sc - b) and (q - 32) b, b = sc & 1: an even integer of
+//     magnitude at most 4096 and one of at most 32, both exact in fp16, each
+//     formed by one fused fp16 multiply-add from a biased code (256 + q); the
+//     super-block scale d is applied to the fp32 sums.  Q4_K: the weight
+//     d sc q - dmin m itself, formed per element in fp32 exactly as the
+//     dequantizer forms it (after a power of two 2^s per super-block that
+//     keeps it below 2^15), and split into hi = fp16(w) and the remainder
+//     fp16(w - hi), which holds it to 22 bits (a subnormal, 2^-25 absolute,
+//     only for weights below 2^-18 of the block's scale).  No cancellation
+//     happens after a rounding: a row of zero weights gives exactly 0.
+//   C (16 x 16, fp32): the sum over the super-block of both weight parts;
+//     then, per row j and batch b, y[b][j] += 2^-sh (C_hi + 2^-11 C_lo)
+//     (Q6_K: times d; Q4_K: times 2^-s) in fp32, C_hi and C_lo being the
+//     rows of x's two fp16 parts.
 //
 // Block layouts: Q4_K fp16 d, fp16 dmin, 12 bytes of packed 6-bit scales and
 // mins, 128 code bytes (sub-block j of 32: nibble j%2 of bytes 32(j/2)..+31);
@@ -223,6 +226,23 @@ __device__ __forceinline__ void keep(const WRawB<T> &r)
 
 __device__ __forceinline__ h2 h2c(float v) { return (h2){(_Float16)v, (_Float16)v}; }
 
+// A value hidden from the optimizer without a scheduling barrier (no
+// volatile): keeps the two halves of a packed fp16 pair in one register, so
+// that each half is formed by v_fma_mixlo_f16 / v_fma_mixhi_f16 and read in
+// place (op_sel) by the next v_fma_mix.  No instruction is written in asm:
+// the hazard recognizer sees every VALU write that an MFMA reads.
+__device__ __forceinline__ uint32_t hide(uint32_t v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
+
+__device__ __forceinline__ _Float16 hide_h(_Float16 v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
+
 // One super-block of one 16-row tile: 8 (+1) MFMAs and the fp32 scaling into
 // acc0 / acc1 (batch rows 2g, 2g+1 of weight row n of the tile).
 template <int T>
@@ -245,23 +265,38 @@ __device__ __forceinline__ void sb_dot<T_Q4_K>(const WRawB<T_Q4_K> &r, const XFr
     const float d = h2f(r.hd.x & 0xffffu), dmin = h2f(r.hd.x >> 16);
     const int s = 5 - __builtin_amdgcn_frexp_expf(fmaxf(fabsf(d), fabsf(dmin)));
     const float ds = __builtin_amdgcn_ldexpf(d, s), dms = __builtin_amdgcn_ldexpf(dmin, s);
-    // d sc and dmin m (times 2^s) are exact products
-    const float dsc0 = ds * ub0(sc), dsc1 = ds * ub1(sc);
-    const float ndm0 = -(dms * ub0(mm)), ndm1 = -(dms * ub1(mm));
+    // A code masked in place is an fp16 subnormal: q 2^-24 for a low nibble,
+    // q 2^-20 for a high one.  The scales carry the inverse power of two and
+    // 2^11: W = 2^11 2^s w, one rounding of the exact q d sc - dmin m.
+    const float dsc0 = ds * ub0(sc) * 0x1p35f, dsc1 = ds * ub1(sc) * 0x1p31f;
+    const float ndm0 = -(dms * ub0(mm)) * 0x1p11f, ndm1 = -(dms * ub1(mm)) * 0x1p11f;
     const uint32_t D[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+    uint32_t D8[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+        D8[t] = D[t] >> 8;
+    // a zero the optimizer cannot see: W 2^-11 + z stays a fused convert
+    // (v_fma_mixlo_f16) instead of a multiply and a separate convert
+    const float z = __builtin_bit_cast(float, hide(0u));
     fl4 ch = {0.f, 0.f, 0.f, 0.f}, cl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int t0 = 2 * (i & 3), ns = i < 4 ? 0 : 4;
-        const float dsc = i < 4 ? dsc0 : dsc1, ndm = i < 4 ? ndm0 : ndm1;
+        const int t0 = 2 * (i & 3);
+        const bool hn = i >= 4;
+        const uint32_t msk = hn ? 0x00f000f0u : 0x000f000fu;      // codes of bytes 0, 2
+        const float dsc = hn ? dsc1 : dsc0, ndm = hn ? ndm1 : ndm0;
         uint32_t oh[4], ol[4];
 #pragma unroll
         for (int pr = 0; pr < 4; ++pr) {
-            const uint32_t q = (D[t0 + (pr >> 1)] >> (ns + 8 * (pr & 1))) & 0x000f000fu;   // codes in bytes 0, 2
-            const float w0 = fmaf(ub0(q), dsc, ndm), w1 = fmaf(ub2(q), dsc, ndm);           // 2^s w, one rounding
-            oh[pr] = pk_rne(w0, w1);
+            const uint32_t v = (pr & 1) ? D8[t0 + (pr >> 1)] : D[t0 + (pr >> 1)];
+            const h2 e = as_h2(opaque(v & msk));
+            // W (v_fma_mix_f32 reads the fp16 code), hi = fp16(2^s w) and
+            // lo = fp16(W - 2^11 hi), the remainder times 2^11
+            const float W0 = fmaf((float)e[0], dsc, ndm), W1 = fmaf((float)e[1], dsc, ndm);
+            oh[pr] = hide(as_u((h2){(_Float16)fmaf(W0, 0x1p-11f, z), (_Float16)fmaf(W1, 0x1p-11f, z)}));
             const h2 h = as_h2(oh[pr]);
-            ol[pr] = pk_rne((w0 - (float)h[0]) * 2048.f, (w1 - (float)h[1]) * 2048.f);     // exact remainders
+            const _Float16 l0 = hide_h((_Float16)fmaf((float)h[0], -2048.f, W0));
+            ol[pr] = as_u((h2){l0, (_Float16)fmaf((float)h[1], -2048.f, W1)});
         }
         ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){oh[0], oh[1], oh[2], oh[3]}),
                                                     ch, 0, 0, 0);
@@ -285,38 +320,46 @@ __device__ __forceinline__ void sb_dot<T_Q6_K>(const WRawB<T_Q6_K> &r, const XFr
                             align_bytes(r.q1.w, r.q1.z, sh), align_bytes(r.q1t, r.q1.w, sh)};
     const uint32_t H[4] = {align_bytes(r.qh.y, r.qh.x, sh), align_bytes(r.qh.z, r.qh.y, sh),
                            align_bytes(r.qh.w, r.qh.z, sh), align_bytes(r.qht, r.qh.w, sh)};
-    // int8 scales 8h + l + 2g' (g' = 0..3): bytes l, l+2 of the two dwords
+    // int8 scales 8h + l + 2g' (g' = 0..3): bytes l, l+2 of the two dwords,
+    // biased to sc + 128 and split into the even part sc - b and the low bit b
     const uint32_t S0 = align_bytes(r.s1, r.s0, sh) ^ 0x80808080u, S1 = align_bytes(r.st, r.s1, sh) ^ 0x80808080u;
     const uint32_t l = (uint32_t)(g & 1);
     const uint32_t sel0 = 0x04000400u + l * 0x00010001u, sel1 = sel0 + 0x00020002u;
-    const h2 k1152 = h2c(1152.f), kn544 = h2c(-544.f);
-    h2 s2[4], n2[4];
+    const h2 k1152 = h2c(1152.f), k1024 = h2c(1024.f), kn288 = h2c(-288.f);
+    h2 se[4], ne[4], sb[4], nb[4];
 #pragma unroll
     for (int gp = 0; gp < 4; ++gp) {
-        s2[gp] = as_h2(byte_pair(0x64646464u, gp < 2 ? S0 : S1, (gp & 1) ? sel1 : sel0)) - k1152;   // scale
-        n2[gp] = s2[gp] * kn544;
+        const uint32_t S = gp < 2 ? S0 : S1, sel = (gp & 1) ? sel1 : sel0;
+        se[gp] = as_h2(byte_pair(0x64646464u, S & 0xfefefefeu, sel)) - k1152;   // sc - b, even
+        sb[gp] = as_h2(byte_pair(0x64646464u, S & 0x01010101u, sel)) - k1024;   // b = sc & 1
+        ne[gp] = se[gp] * kn288;
+        nb[gp] = sb[gp] * kn288;
     }
     fl4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int gp = i >> 1, t0 = 2 * (i & 1);
-        uint32_t o[4];
+        uint32_t oe[4], ob[4];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             const uint32_t ql = (gp & 1) ? Q1[t0 + tt] : Q0[t0 + tt];
-            // 2q per byte: low 4 bits from ql (nibble gp/2), bits 4-5 from qh (bits 2gp..2gp+1)
-            const uint32_t lo4 = gp < 2 ? (ql << 1) & 0x1e1e1e1eu : (ql >> 3) & 0x1e1e1e1eu;
-            const int hs = 2 * gp;
-            const uint32_t hi2 = hs <= 5 ? (H[t0 + tt] << (5 - hs)) & 0x60606060u : (H[t0 + tt] >> (hs - 5)) & 0x60606060u;
-            const uint32_t q2 = lo4 | hi2;
+            // 4q per byte: low 4 bits from ql (nibble gp/2) to bits 2-5, bits
+            // 4-5 of q from qh (bits 2gp..2gp+1) to bits 6-7
+            const uint32_t lo4 = gp < 2 ? (ql << 2) & 0x3c3c3c3cu : (ql >> 2) & 0x3c3c3c3cu;
+            const uint32_t q4 = lo4 | ((H[t0 + tt] << (6 - 2 * gp)) & 0xc0c0c0c0u);
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
-                // bytes (pp, pp+2) -> fp16 512 + q
-                const h2 code = as_h2(byte_pair(0x60606060u, q2, pp ? 0x04030401u : 0x04020400u));
-                o[2 * tt + pp] = as_u(__builtin_elementwise_fma(code, s2[gp], n2[gp]));   // (q-32)*scale, exact
+                // bytes (pp, pp+2) -> fp16 256 + q
+                const h2 code = as_h2(byte_pair(0x5c5c5c5cu, q4, pp ? 0x04030401u : 0x04020400u));
+                // (q - 32)(sc - b): even, at most 4096 in magnitude; (q - 32) b:
+                // both exact in fp16, each from one fused multiply-add
+                oe[2 * tt + pp] = as_u(__builtin_elementwise_fma(code, se[gp], ne[gp]));
+                ob[2 * tt + pp] = as_u(__builtin_elementwise_fma(code, sb[gp], nb[gp]));
             }
         }
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){o[0], o[1], o[2], o[3]}),
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){oe[0], oe[1], oe[2], oe[3]}),
+                                                   c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){ob[0], ob[1], ob[2], ob[3]}),
                                                    c, 0, 0, 0);
     }
     const float d = h2f(r.d);
@@ -446,11 +489,11 @@ gemvb_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
 // ----------------------------------------------------- single-run kernel --
 // K of at most 16 super-blocks (every wave owns at most two): the A fragments
 // are converted once per workgroup and the weight stream runs through a ring
-// of GB_D tiles per wave (GB_D - 1 tiles of bytes in flight while one is
-// decoded).  The activations reach LDS by direct global->LDS loads, issued
-// before the first weight loads: waiting for them (the memory counter
-// completes in order) leaves those weight loads in flight, and they take no
-// registers while the fragments are built.
+// of D tiles per wave (D - 1 tiles of bytes in flight while one is decoded;
+// a workgroup with t tiles takes D = min(t + 1, the type's depth)).  The
+// activations reach LDS by direct global->LDS loads, issued before the first
+// weight loads: waiting for them (the memory counter completes in order)
+// leaves those weight loads in flight while the fragments are built.
 template <int T> struct RingDepth { static constexpr int D = 3; };
 template <> struct RingDepth<T_Q4_K> { static constexpr int D = 4; };
 
@@ -500,6 +543,7 @@ __device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n,
         load_tile(ring[d], d);
     __builtin_amdgcn_sched_barrier(0);
     // the activation loads were issued before the ring: wait for them only
+    // (the first D - 1 tiles stay in flight while the fragments are built)
     QMM_WAIT_VMCNT((D - 1) * NC * RawLoads<T>::N);
     __builtin_amdgcn_sched_barrier(0);
     XFrag xf[NC];
@@ -515,7 +559,10 @@ __device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n,
     for (int t = 0; t < t_count; t += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            load_tile(ring[(j + D - 1) % D], t + j + D - 1);   // past the end: a harmless re-read
+            // past the workgroup's last tile: a re-read of that tile
+            // (unconditional: a branch around the loads makes the compiler
+            // wait for every load in flight)
+            load_tile(ring[(j + D - 1) % D], t + j + D - 1);
             if (t + j < t_count) {
                 float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -572,18 +619,25 @@ gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const flo
     using std_true = std::integral_constant<bool, true>;
     using std_false = std::integral_constant<bool, false>;
     if (ns > 0) {
-        const int dsel = min(t_count, DM);
-        if (ns == 2) {
-            if (dsel >= DM) run(std_true{}, std::integral_constant<int, DM>{});
-            else if (dsel == 3) run(std_true{}, std::integral_constant<int, 3>{});
-            else if (dsel == 2) run(std_true{}, std::integral_constant<int, 2>{});
-            else run(std_true{}, std::integral_constant<int, 1>{});
-        } else {
-            if (dsel >= DM) run(std_false{}, std::integral_constant<int, DM>{});
-            else if (dsel == 3) run(std_false{}, std::integral_constant<int, 3>{});
-            else if (dsel == 2) run(std_false{}, std::integral_constant<int, 2>{});
-            else run(std_false{}, std::integral_constant<int, 1>{});
-        }
+        // D - 1 tiles in flight, at most one past the workgroup's last
+        const int dsel = min(t_count + 1, DM);
+        auto by_depth = [&](auto two_c) {
+            if (dsel >= DM) run(two_c, std::integral_constant<int, DM>{});
+            else if constexpr (DM > 3) {
+                if (dsel == 3) run(two_c, std::integral_constant<int, 3>{});
+                else if (dsel == 2) run(two_c, std::integral_constant<int, 2>{});
+                else run(two_c, std::integral_constant<int, 1>{});
+            } else if constexpr (DM > 2) {
+                if (dsel == 2) run(two_c, std::integral_constant<int, 2>{});
+                else run(two_c, std::integral_constant<int, 1>{});
+            } else {
+                run(two_c, std::integral_constant<int, 1>{});
+            }
+        };
+        if (ns == 2)
+            by_depth(std_true{});
+        else
+            by_depth(std_false{});
     }
     else {
         // no super-block: zero partials, same barriers as the others

@@ -186,8 +186,9 @@ QMM_API int qmm_quantize_f16(int type, const uint16_t *x, int64_t n, int64_t k, 
  * products and sums.  Batch 2..8 of Q4_K / Q6_K run on the fp16 matrix
  * cores: per 256-element block and activation row, x is scaled by a power
  * of two and split into two fp16 parts (about 22 significant bits); Q6_K
- * weights enter as exact fp16 integers (code x sub-block scale), Q4_K
- * weights as two fp16 parts of the fp32 weight; sums are fp32.  On that
+ * weights enter as two exact fp16 integers ((q - 32) times the even part of
+ * the int8 scale, and times its low bit), Q4_K weights as two fp16 parts of
+ * the fp32 weight; sums are fp32.  On that
  * path an element of x smaller than about 2^-34 of the largest |x| of its
  * 256-element block keeps an absolute error of about 2^-50 of that largest
  * value (not a relative one): the bound above can fail only for rows whose

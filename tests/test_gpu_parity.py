@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
+import packing as PK
 import qmm_inputs as G
 
 pytestmark = pytest.mark.gpu
@@ -224,6 +225,56 @@ def test_gemv_batch_dynamic_range(t):
     ref, absum = oracle.gemv(t, w, n, k, x)
     got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
     say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "dynamic range %s" % G.NAMES[t]))
+
+
+def _edge_field_rows(t, n, nb, seed):
+    """K-quant rows whose fields sit at the edges of their ranges.  Q6_K: int8
+    scales -128, 127 and odd values past 64 (where (q - 32) * scale needs 12
+    bits), codes 0, 63 and 32, d from fp16 subnormal to 6e4.  Q4_K: 6-bit
+    scales and mins 0, 1, 62, 63, codes 0 and 15, and d, dmin equal, 2^29
+    apart either way round, of opposite signs, or fp16 subnormal."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for r in range(n):
+        blks = []
+        for _ in range(nb):
+            if t == G.Q6_K:
+                sc = rng.choice([-128, 127, -127, 125, 65, -65, 99, -1, 0, 1], size=16)
+                q6 = rng.integers(0, 64, size=256) if r % 3 == 0 else rng.choice([0, 63, 1, 62, 32, 31, 33], size=256)
+                d = [3e-4, -7e-4, 6e4, 1e-7][r % 4]
+                blks.append(PK.pack_q6_k(int(PK.f16(d)), sc, q6))
+            else:
+                sc = rng.choice([0, 1, 62, 63, 33], size=8)
+                m = rng.choice([0, 1, 62, 63, 17], size=8)
+                q4 = rng.choice([0, 15, 1, 14], size=256)
+                d, dmin = [(1e-3, 1e-3), (6e4, 1e-4), (1e-4, 6e4), (-5e3, 2e-2), (3e-6, -2e-5)][r % 5]
+                blks.append(PK.pack_q4_k(int(PK.f16(d)), int(PK.f16(dmin)), sc, m, q4))
+        rows.append(b"".join(blks))
+    return np.frombuffer(b"".join(rows), np.uint8).reshape(n, -1).copy()
+
+
+@pytest.mark.parametrize("t", [G.Q4_K, G.Q6_K])
+@pytest.mark.parametrize("nb", [5, 18])
+def test_kquant_edge_fields(t, nb):
+    """Dequant bit-exact, every GEMV path within 2e-5, and the GEMM within
+    1e-3 on the rows whose weights fit fp16, for blocks at the edges of the
+    format (full-range Q6_K scales are what real Q6_K files hold)."""
+    n, k = 40, 256 * nb
+    w = _edge_field_rows(t, n, nb, seed=77 + t + nb)
+    say("edge fields", G.NAMES[t], n, k)
+    W = oracle.dequant(t, w, n, k)
+    assert np.array_equal(q.dequant(upload(w), t, n, k).cpu().numpy(), W)
+    for batch in (1, 2, 5, 8):
+        x = G.gen_x(k, batch, seed=78 + batch)
+        ref, absum = oracle.gemv(t, w, n, k, x)
+        got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+        say("  B", batch, "worst relative error",
+            check_tol(got, ref, absum, GEMV_TOL, "edge fields %s B=%d" % (G.NAMES[t], batch)))
+    fits = np.abs(W).max(axis=1) < 6e4
+    X = G.gen_x_f16(33, k, seed=79)
+    ref, absum = oracle.gemm(t, w, n, k, X)
+    got = q.gemm_prefill(upload(w), t, n, k, upload(X)).cpu().numpy()
+    check_tol(got[:, fits], ref[:, fits], absum[:, fits], GEMM_TOL, "edge fields gemm %s" % G.NAMES[t])
 
 
 @pytest.mark.parametrize("t,n,k,batch", [(G.Q4_K, 33000, 4608, 5), (G.Q6_K, 40000, 1024, 8),
