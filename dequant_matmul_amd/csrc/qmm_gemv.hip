@@ -55,10 +55,11 @@
 //                 sums meet in LDS.
 //   gemv1_kernel  batch 1, longer k: x is staged in LDS per segment,
 //                 otherwise as gemv3.
-//   gemv_kernel   batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K (and unaligned
-//                 batch-1 rows): x
+//   gemv_kernel   batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K, batch 2 of Q4_K /
+//                 Q6_K below 65536 rows (and unaligned batch-1 rows): x
 //                 segment and weight segments staged in LDS per workgroup.
-//   Batch 2..8 of Q4_K / Q6_K runs on the matrix cores (qmm_gemv_mfma.hip).
+//   The other batches 2..8 of Q4_K / Q6_K run on the matrix cores
+//   (qmm_gemv_mfma.hip).
 #include "qmm_device.h"
 #include "qmm_gemv_unit.h"
 #include "qmm_launch.h"
@@ -875,7 +876,15 @@ static hipError_t launch_t(const uint8_t *w, int64_t n, int64_t k, size_t rb, co
             return launch_b1_lds<T, 2, 8, 16384, 1>(w, n, k, rb, x, y, s);
         }
     }
-    if (gemv_mfma_supported(T, batch))
+    // Batch 2 of the K-quants takes the fp32 vector kernel below (1 + 2
+    // operations per weight, two rows per item) except on very tall matrices:
+    // measured on MI355X at B = 2 against the matrix-core kernel, 14336 x
+    // 4096 Q4_K 21.3 -> 17.7 us, 4096 x 14336 Q6_K 28.2 -> 21.3, 4096 x 4096
+    // Q4_K 8.9 -> 6.7, 1024 x 4096 Q4_K 8.9 -> 4.8; the 128256 x 4096 Q6_K
+    // head (128 -> 151 us) stays on the matrix cores, and so does every
+    // batch from 3 on (the vector kernel's x staging then leaves one
+    // workgroup per compute unit: 34 us for the 14336 x 4096 Q4_K at B = 3).
+    if (gemv_mfma_supported(T, batch) && !(batch == 2 && n < 65536))
         return launch_gemv_mfma(T, w, n, k, rb, x, batch, y, s);
     switch (batch) {
     case 1: return launch_tbr<T, 1, 2>(w, n, k, rb, x, y, s);

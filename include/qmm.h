@@ -182,9 +182,9 @@ QMM_API int qmm_quantize_f16(int type, const uint16_t *x, int64_t n, int64_t k, 
  * are formed per element), so there is no cancellation after a rounding:
  * |y - exact| <= 2e-5 * sum_i |w[j][i] x[b][i]| for every output, and a row
  * of zero weights gives exactly 0.
- * Batch 1 (all types) and batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K: fp32
- * products and sums.  Batch 2..8 of Q4_K / Q6_K run on the fp16 matrix
- * cores: per 256-element block and activation row, x is scaled by a power
+ * Batch 1 (all types), batch 2..8 of Q8_0 / Q4_0 / Q5_0 / Q5_K and batch 2
+ * of Q4_K / Q6_K with n < 65536: fp32 products and sums.  The other batches
+ * 2..8 of Q4_K / Q6_K run on the fp16 matrix cores: per 256-element block and activation row, x is scaled by a power
  * of two and split into two fp16 parts (about 22 significant bits); Q6_K
  * weights enter as two exact fp16 integers ((q - 32) times the even part of
  * the int8 scale, and times its low bit), Q4_K weights as two fp16 parts of

@@ -153,7 +153,7 @@ def test_gemv_and_gemm_wide_k(t):
     check_tol(got, ref, absum, GEMM_TOL, "gemm wide k %s" % G.NAMES[t])
 
 
-@pytest.mark.parametrize("batch", [1, 4, 8])
+@pytest.mark.parametrize("batch", [1, 2, 4, 8])
 def test_gemv_lm_head(batch):
     """The largest matrix of the workloads: the 128256 x 4096 Q6_K LM head of
     the Q4_K_M-style mix (431 MB), every output against the oracle."""
@@ -278,12 +278,14 @@ def test_kquant_edge_fields(t, nb):
 
 
 @pytest.mark.parametrize("t,n,k,batch", [(G.Q4_K, 33000, 4608, 5), (G.Q6_K, 40000, 1024, 8),
-                                         (G.Q6_K, 2100, 4864, 3)])
+                                         (G.Q6_K, 2100, 4864, 3), (G.Q4_K, 66000, 512, 2),
+                                         (G.Q6_K, 70001, 4608, 2)])
 def test_gemv_batch_many_tiles(t, n, k, batch):
     """More 16-row tiles than 8 per compute unit (several reduction rounds
     per workgroup), K runs longer than two blocks per wave, waves with no
-    block (k = 1024), and an odd super-block count per row (Q6_K rows then
-    alternate their 4-byte alignment)."""
+    block (k = 1024), an odd super-block count per row (Q6_K rows then
+    alternate their 4-byte alignment), and batch 2 past 65536 rows (the
+    matrix-core kernel; shorter matrices take the vector kernel at B = 2)."""
     say("gemv many tiles", G.NAMES[t], n, k, batch)
     w = G.gen_weights(t, n, k, seed=31)
     x = G.gen_x(k, batch, seed=32)
