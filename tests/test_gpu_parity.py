@@ -254,7 +254,7 @@ def _edge_field_rows(t, n, nb, seed):
 
 
 @pytest.mark.parametrize("t", [G.Q4_K, G.Q6_K])
-@pytest.mark.parametrize("nb", [5, 18])
+@pytest.mark.parametrize("nb", [5, 16, 18])
 def test_kquant_edge_fields(t, nb):
     """Dequant bit-exact, every GEMV path within 2e-5, and the GEMM within
     1e-3 on the rows whose weights fit fp16, for blocks at the edges of the
@@ -292,6 +292,26 @@ def test_gemv_batch_many_tiles(t, n, k, batch):
     ref, absum = oracle.gemv(t, w, n, k, x)
     got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
     say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "gemv %s %dx%d B%d" % (G.NAMES[t], n, k, batch)))
+
+
+@pytest.mark.parametrize("batch", [3, 8])
+def test_gemv_q6k_staged_tiles(batch):
+    """Q6_K at k = 4096 with at least four 16-row tiles per workgroup: the
+    batch kernel stages whole tiles through LDS.  Rows of random blocks, and
+    rows of edge-field blocks (full-range int8 scales), over a ragged last
+    tile (16390 rows)."""
+    t, n, k = G.Q6_K, 16390, 4096
+    say("gemv q6k staged", n, k, batch)
+    x = G.gen_x(k, batch, seed=41 + batch)
+    w = G.gen_weights(t, n, k, seed=40)
+    ref, absum = oracle.gemv(t, w, n, k, x)
+    got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+    say("  random, worst relative error", check_tol(got, ref, absum, GEMV_TOL, "staged random B=%d" % batch))
+    base = _edge_field_rows(t, 40, 16, seed=42)
+    we = np.ascontiguousarray(np.tile(base, ((n + 39) // 40, 1))[:n])
+    ref, absum = oracle.gemv(t, we, n, k, x)
+    got = q.gemv(upload(we), t, n, k, upload(x)).cpu().numpy()
+    say("  edge fields, worst relative error", check_tol(got, ref, absum, GEMV_TOL, "staged edge B=%d" % batch))
 
 
 def test_gemv_unaligned_rows():
