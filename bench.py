@@ -128,6 +128,50 @@ class Problem:
             raise RuntimeError("%s %s: %s" % (self.kind, self.name, q.status_str(st)))
 
 
+class BatchPass:
+    """A decode pass at batch B > 1 in the decoder's stage order, the
+    problems of a stage reading one x [B, k] (q / k / v, gate / up), as in
+    Pass: each stage's problems of one block type go to one qmm_gemv_multi
+    call (at batch 3..8 of the K-quants one matrix-core launch over all
+    their tiles), a lone problem to qmm_gemv."""
+
+    def __init__(self, torch, q, cfg, weights, batch, dev):
+        import ctypes
+        self.units, self.probs = [], []
+        xs, groups = {}, {}
+        for i, (name, t, n, k, w) in enumerate(weights):
+            st = G.decode_stage(name)
+            if st not in xs:
+                xs[st] = torch.from_numpy(G.gen_x(k, batch, G.x_seed(cfg, i))).to(dev)
+            y = torch.empty((batch, n), dtype=torch.float32, device=dev)
+            p = Problem(torch, name, t, n, k, w, xs[st], y)
+            self.probs.append(p)
+            groups.setdefault((st, t), []).append(p)
+        for (st, t), ps in sorted(groups.items(), key=lambda e: e[0][0]):
+            if len(ps) == 1:
+                self.units.append(ps[0])
+                continue
+            m = len(ps)
+            self.units.append(("multi", t, m, ps[0].k, batch,
+                               (ctypes.c_void_p * m)(*[p.w.data_ptr() for p in ps]),
+                               (ctypes.c_int64 * m)(*[p.n for p in ps]),
+                               (ctypes.c_void_p * m)(*[p.x.data_ptr() for p in ps]),
+                               (ctypes.c_void_p * m)(*[p.y.data_ptr() for p in ps])))
+        self.wbytes = sum(p.wbytes for p in self.probs)
+        self.bytes = self.wbytes + sum(4 * x.numel() for x in xs.values()) + sum(4 * batch * p.n for p in self.probs)
+        self.launches = len(self.units)
+
+    def launch(self, q, stream):
+        for u in self.units:
+            if isinstance(u, Problem):
+                u.launch(q, stream)
+                continue
+            _, t, m, k, batch, wp, nn, xp, yp = u
+            st = q.lib.qmm_gemv_multi(t, m, wp, nn, k, xp, batch, yp, stream)
+            if st != 0:
+                raise RuntimeError("qmm_gemv_multi: %s" % q.status_str(st))
+
+
 class Embed:
     """One embedding gather (qmm_embed / qmm_embed_f16) with its buffers."""
 
@@ -441,13 +485,15 @@ def sec_prefill(torch, q, steps, warmup, dev, cfg=4):
 
 
 def sec_mix_batch(torch, q, steps, warmup, dev, weights):
-    """The Q4_K_M-style mix at batch 4 and 8 (qmm_gemv per matrix, x fp32
-    [B, k]), and the same pass as a skinny GEMM (fp16 X, M = B)."""
+    """The Q4_K_M-style mix at batch 4 and 8 (x fp32 [B, k], one x per stage
+    as in the batch-1 pass: qmm_gemv_multi per stage and block type), and the
+    same pass as a skinny GEMM (fp16 X, M = B, one call per matrix)."""
     res = {}
     for batch in (4, 8):
-        probs = make_gemvs(torch, 5, weights, batch, dev)
-        tot = sum(p.bytes for p in probs)
-        tg = time_graph(torch, capture(torch, q, probs), max(3, steps // 2), 2)
+        bp = BatchPass(torch, q, 5, weights, batch, dev)
+        probs = bp.probs
+        tot = bp.bytes
+        tg = time_graph(torch, capture(torch, q, bp), max(3, steps // 2), 2)
         gp = [Problem(torch, p.name, p.t, p.n, p.k, p.w, torch.from_numpy(G.gen_x_f16(batch, p.k, 77)).to(dev),
                       p.y, kind="gemm") for p in probs]
         tgg = time_graph(torch, capture(torch, q, gp), max(3, steps // 2), 2)
@@ -455,9 +501,10 @@ def sec_mix_batch(torch, q, steps, warmup, dev, weights):
             "workload": "Q4_K_M-style mix, 225 GEMVs, batch %d" % batch, "ms_per_pass": round(tg * 1e3, 4),
             "GB_s": round(tot / tg / 1e9, 1), "decode_tok_s": round(batch / tg, 1),
             "skinny_gemm_ms_per_pass": round(tgg * 1e3, 4), "skinny_gemm_tok_s": round(batch / tgg, 1),
+            "launches_per_pass": bp.launches,
             "roofline": roofline(tot / tg / 1e9, HBM_PEAK_GBS, "GB/s", "hbm",
-                                 kernel="whole pass (batch GEMV, one launch per matrix)")}
-        del probs, gp
+                                 kernel="whole pass (batch GEMV, qmm_gemv_multi per stage and type)")}
+        del probs, gp, bp
         torch.cuda.empty_cache()
     return res
 

@@ -961,6 +961,16 @@ static hipError_t launch_multi_t(int np, const void *const *w, const int64_t *n,
         }
         return hipSuccess;
     }
+    // batch 3..8 of the K-quants, one x for every problem: one matrix-core
+    // launch over all their tiles (x converted once per workgroup for more
+    // tiles, one launch instead of one per matrix)
+    if (batch >= 3 && gemv_mfma_multi_supported(T, batch, k)) {
+        bool shared = true;
+        for (int i = 1; i < np; ++i)
+            shared = shared && x[i] == x[0];
+        if (shared)
+            return launch_gemv_mfma_multi(T, np, w, n, k, rb, x[0], batch, y, s);
+    }
     // other shapes: one launch per problem
     for (int i = 0; i < np; ++i) {
         if (n[i] == 0)

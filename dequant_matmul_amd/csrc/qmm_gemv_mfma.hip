@@ -507,10 +507,54 @@ template <> struct RawLoads<T_Q6_K> { static constexpr int N = 9; };
 // vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 #define QMM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
 
+// Up to MP_MAX problems of one type and k sharing x (q / k, gate / up of a
+// layer): their 16-row tiles are numbered one after another (tile0), and a
+// workgroup's run of tiles may cross from one problem into the next.
+constexpr int MP_MAX = 8;
+struct MProbs {
+    const uint8_t *w[MP_MAX];
+    float *y[MP_MAX];
+    int n[MP_MAX];
+    int tile0[MP_MAX + 1];   // first tile of each problem; tile0[np] = all tiles
+    int np;
+};
+
+struct TileRef {
+    const uint8_t *w;
+    float *y;
+    int n, row0;             // the problem's rows, the tile's first row in it
+};
+
+// Tile ti's problem (wave-uniform: a short scalar scan of the table).
+__device__ __forceinline__ TileRef tile_ref(const MProbs &P, int ti)
+{
+    int p = 0;
+    while (p + 1 < P.np && ti >= P.tile0[p + 1])
+        ++p;
+    return TileRef{P.w[p], P.y[p], P.n[p], (ti - P.tile0[p]) * 16};
+}
+
+// Cross-wave sum of tile j (red[j]) stored to its problem's y: one
+// (row, batch pair) per thread of the first 64 j + 64.
+__device__ __forceinline__ void store_tile(const MProbs &P, int ti, const fl2 (*redj)[64], int ln, int batch)
+{
+    fl2 s = redj[0][ln];
+#pragma unroll
+    for (int ww = 1; ww < GB_W; ++ww)
+        s += redj[ww][ln];
+    const TileRef R = tile_ref(P, ti);
+    const int row = R.row0 + (ln & 15), b0 = 2 * (ln >> 4);
+    if (row < R.n) {
+        if (b0 < batch)
+            R.y[(int64_t)b0 * R.n + row] = s[0];
+        if (b0 + 1 < batch)
+            R.y[(int64_t)(b0 + 1) * R.n + row] = s[1];
+    }
+}
+
 template <int T, bool TWO, int D>
-__device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n, int k, int64_t rb,
-                                           const float *__restrict__ x, int batch, float *__restrict__ y,
-                                           int t_begin, int t_count, int sa, float (*xs)[8][XROW],
+__device__ __forceinline__ void single_run(const MProbs &P, int k, int64_t rb, const float *__restrict__ x,
+                                           int batch, int t_begin, int t_count, int sa, float (*xs)[8][XROW],
                                            fl2 (*red)[GB_W][64])
 {
     using F = Fmt<T>;
@@ -531,12 +575,12 @@ __device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n,
     };
     Slot ring[D];
     auto load_tile = [&](Slot &sl, int t) {
-        t = min(t, t_count - 1);
-        const int row = min((t_begin + t) * 16 + nl, n - 1);
+        const TileRef R = tile_ref(P, t_begin + min(t, t_count - 1));
+        const int row = min(R.row0 + nl, R.n - 1);
         const int64_t base = (int64_t)row * rb + (int64_t)sa * F::BB;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            load_b<T>(w, base + c * F::BB, g, sl.r[c]);
+            load_b<T>(R.w, base + c * F::BB, g, sl.r[c]);
     };
 #pragma unroll
     for (int d = 0; d < D - 1; ++d)
@@ -575,20 +619,8 @@ __device__ __forceinline__ void single_run(const uint8_t *__restrict__ w, int n,
         // weight loads in flight)
         lds_barrier();
         const int nt = min(D, t_count - t);
-        if ((int)threadIdx.x < nt * 64) {
-            const int j = threadIdx.x >> 6, ln = threadIdx.x & 63;
-            fl2 s = red[j][0][ln];
-#pragma unroll
-            for (int ww = 1; ww < GB_W; ++ww)
-                s += red[j][ww][ln];
-            const int row = (t_begin + t + j) * 16 + (ln & 15), b0 = 2 * (ln >> 4);
-            if (row < n) {
-                if (b0 < batch)
-                    y[(int64_t)b0 * n + row] = s[0];
-                if (b0 + 1 < batch)
-                    y[(int64_t)(b0 + 1) * n + row] = s[1];
-            }
-        }
+        if ((int)threadIdx.x < nt * 64)
+            store_tile(P, t_begin + t + (threadIdx.x >> 6), red[threadIdx.x >> 6], threadIdx.x & 63, batch);
         lds_barrier();
     }
 }
@@ -635,9 +667,9 @@ __device__ __forceinline__ void lds_load_b_q6k(const uint32_t *tb, int nl, int s
 }
 
 template <int D>
-__device__ __forceinline__ void staged_run_q6k(const uint8_t *__restrict__ w, int n, const float *__restrict__ x,
-                                               int batch, float *__restrict__ y, int t_begin, int t_count, int sa,
-                                               float (*xs)[8][XROW], uint32_t *tbuf, fl2 (*red)[GB_W][64])
+__device__ __forceinline__ void staged_run_q6k(const MProbs &P, const float *__restrict__ x, int batch, int t_begin,
+                                               int t_count, int sa, float (*xs)[8][XROW], uint32_t *tbuf,
+                                               fl2 (*red)[GB_W][64])
 {
     constexpr int T = T_Q6_K, NC = 2, k = 4096;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nl = lane & 15, g = lane >> 4;
@@ -653,16 +685,15 @@ __device__ __forceinline__ void staged_run_q6k(const uint8_t *__restrict__ w, in
         u32x4 v[ST_CPT];
     };
     Slot ring[D];
-    // chunk c of tile t: bytes 16 c of its 16 rows; past the matrix the
-    // last chunk of the matrix (rows past n are never stored)
-    const int64_t last = (int64_t)n * ST_RB - 16;
+    // chunk c of tile t: bytes 16 c of its 16 rows; past its problem's
+    // matrix the last chunk of that matrix (rows past n are never stored)
     auto load_tile = [&](Slot &sl, int t) {
-        t = min(t, t_count - 1);
-        const int64_t base = (int64_t)(t_begin + t) * 16 * ST_RB;
+        const TileRef R = tile_ref(P, t_begin + min(t, t_count - 1));
+        const int64_t base = (int64_t)R.row0 * ST_RB, last = (int64_t)R.n * ST_RB - 16;
 #pragma unroll
         for (int i = 0; i < ST_CPT; ++i) {
             const int c = min(tid + 64 * GB_W * i, ST_CH - 1);
-            sl.v[i] = *(const u32x4 *)(w + min(base + 16 * c, last));
+            sl.v[i] = *(const u32x4 *)(R.w + min(base + 16 * c, last));
         }
     };
 #pragma unroll
@@ -712,28 +743,15 @@ __device__ __forceinline__ void staged_run_q6k(const uint8_t *__restrict__ w, in
         }
         lds_barrier();
         const int nt = min(D, t_count - t);
-        if ((int)threadIdx.x < nt * 64) {
-            const int j = threadIdx.x >> 6, ln = threadIdx.x & 63;
-            fl2 s = red[j][0][ln];
-#pragma unroll
-            for (int ww = 1; ww < GB_W; ++ww)
-                s += red[j][ww][ln];
-            const int row = (t_begin + t + j) * 16 + (ln & 15), b0 = 2 * (ln >> 4);
-            if (row < n) {
-                if (b0 < batch)
-                    y[(int64_t)b0 * n + row] = s[0];
-                if (b0 + 1 < batch)
-                    y[(int64_t)(b0 + 1) * n + row] = s[1];
-            }
-        }
+        if ((int)threadIdx.x < nt * 64)
+            store_tile(P, t_begin + t + (threadIdx.x >> 6), red[threadIdx.x >> 6], threadIdx.x & 63, batch);
         lds_barrier();
     }
 }
 
 template <int T>
 __global__ void __launch_bounds__(64 * GB_W)
-gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x, int batch,
-              float *__restrict__ y)
+gemvb1_kernel(const MProbs P, int k, int64_t rb, const float *__restrict__ x, int batch)
 {
     constexpr int DM = RingDepth<T>::D;
     // activation staging; for staged Q6_K tiles also the two tile buffers
@@ -746,7 +764,7 @@ gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const flo
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int S = k / 256;
     const int sa = wave * S / GB_W, ns = (wave + 1) * S / GB_W - sa;   // 0, 1 or 2 super-blocks
-    const int ntiles = (n + 15) >> 4;
+    const int ntiles = P.tile0[P.np];
     const int per = ntiles / (int)gridDim.x, rem = ntiles - per * (int)gridDim.x;
     const int t_begin = (int)blockIdx.x * per + min((int)blockIdx.x, rem);
     const int t_count = per + ((int)blockIdx.x < rem ? 1 : 0);
@@ -754,7 +772,7 @@ gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const flo
     // ring depth: one tile per lane group of loads in flight per tile the
     // workgroup still has (no prefetch of tiles that do not exist)
     auto run = [&](auto two_c, auto d_c) {
-        single_run<T, decltype(two_c)::value, decltype(d_c)::value>(w, n, k, rb, x, batch, y, t_begin, t_count, sa,
+        single_run<T, decltype(two_c)::value, decltype(d_c)::value>(P, k, rb, x, batch, t_begin, t_count, sa,
                                                                       xs[wave], red);
     };
     using std_true = std::integral_constant<bool, true>;
@@ -764,12 +782,7 @@ gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const flo
         // (with fewer, the per-tile barriers cost more than the scattered
         // loads: 1024 x 4096 at batch 8, 8.1 -> 9.8 us)
         if (k == 4096 && rb == ST_RB && t_count >= 4) {
-            if (t_count + 1 >= DM)
-                staged_run_q6k<DM>(w, n, x, batch, y, t_begin, t_count, sa, xs[wave], lds_x, red);
-            else if (t_count + 1 == 2)
-                staged_run_q6k<2>(w, n, x, batch, y, t_begin, t_count, sa, xs[wave], lds_x, red);
-            else
-                staged_run_q6k<1>(w, n, x, batch, y, t_begin, t_count, sa, xs[wave], lds_x, red);
+            staged_run_q6k<DM>(P, x, batch, t_begin, t_count, sa, xs[wave], lds_x, red);
             return;
         }
     }
@@ -802,19 +815,8 @@ gemvb1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const flo
                 red[j][wave][lane] = (fl2){0.f, 0.f};
             lds_barrier();
             const int nt = min(D, t_count - t);
-            if ((int)threadIdx.x < nt * 64) {
-                const int j = threadIdx.x >> 6, ln = threadIdx.x & 63;
-                fl2 s = red[j][0][ln];
-                for (int ww = 1; ww < GB_W; ++ww)
-                    s += red[j][ww][ln];
-                const int row = (t_begin + t + j) * 16 + (ln & 15), b0 = 2 * (ln >> 4);
-                if (row < n) {
-                    if (b0 < batch)
-                        y[(int64_t)b0 * n + row] = s[0];
-                    if (b0 + 1 < batch)
-                        y[(int64_t)(b0 + 1) * n + row] = s[1];
-                }
-            }
+            if ((int)threadIdx.x < nt * 64)
+                store_tile(P, t_begin + t + (threadIdx.x >> 6), red[threadIdx.x >> 6], threadIdx.x & 63, batch);
             lds_barrier();
         }
     }
@@ -833,13 +835,49 @@ hipError_t launch_b(const uint8_t *w, int64_t n, int64_t k, size_t rb, const flo
     const int64_t ntiles = (n + 15) / 16;
     const int grid = (int)(ntiles < cu_count_cached() ? ntiles : cu_count_cached());
     if (k <= 256 * 2 * GB_W) {
-        hipLaunchKernelGGL(gemvb1_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, w, (int)n, (int)k, (int64_t)rb, x,
-                           batch, y);
+        MProbs P{};
+        P.w[0] = w;
+        P.y[0] = y;
+        P.n[0] = (int)n;
+        P.tile0[1] = (int)ntiles;
+        P.np = 1;
+        hipLaunchKernelGGL(gemvb1_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, P, (int)k, (int64_t)rb, x, batch);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(gemvb_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, w, (int)n, (int)k, (int64_t)rb, x,
                        batch, y);
     return hipGetLastError();
+}
+
+// Problems of one type and k <= 4096 reading one x: one launch over all their
+// tiles (empty problems left out of the table).
+template <int T>
+hipError_t launch_b_multi(int np, const void *const *w, const int64_t *n, int64_t k, size_t rb, const float *x,
+                          int batch, float *const *y, hipStream_t s)
+{
+    for (int i0 = 0; i0 < np;) {
+        MProbs P{};
+        int c = 0;
+        for (; i0 < np && c < MP_MAX; ++i0) {
+            if (n[i0] == 0)
+                continue;
+            P.w[c] = (const uint8_t *)w[i0];
+            P.y[c] = y[i0];
+            P.n[c] = (int)n[i0];
+            P.tile0[c + 1] = P.tile0[c] + (int)((n[i0] + 15) / 16);
+            ++c;
+        }
+        if (c == 0)
+            break;
+        P.np = c;
+        const int ntiles = P.tile0[c];
+        const int grid = ntiles < cu_count_cached() ? ntiles : cu_count_cached();
+        hipLaunchKernelGGL(gemvb1_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, P, (int)k, (int64_t)rb, x, batch);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -856,6 +894,21 @@ hipError_t launch_gemv_mfma(int type, const void *w, int64_t n, int64_t k, size_
     switch (type) {
     case T_Q4_K: return launch_b<T_Q4_K>(wb, n, k, rb, x, batch, y, s);
     case T_Q6_K: return launch_b<T_Q6_K>(wb, n, k, rb, x, batch, y, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool gemv_mfma_multi_supported(int type, int batch, int64_t k)
+{
+    return gemv_mfma_supported(type, batch) && k <= 256 * 2 * GB_W;
+}
+
+hipError_t launch_gemv_mfma_multi(int type, int np, const void *const *w, const int64_t *n, int64_t k, size_t rb,
+                                  const float *x, int batch, float *const *y, hipStream_t s)
+{
+    switch (type) {
+    case T_Q4_K: return launch_b_multi<T_Q4_K>(np, w, n, k, rb, x, batch, y, s);
+    case T_Q6_K: return launch_b_multi<T_Q6_K>(np, w, n, k, rb, x, batch, y, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -71,6 +71,11 @@ hipError_t launch_gemv_multi(int type, int np, const void *const *w, const int64
 // Batch 2..8 GEMV on the matrix cores (Q4_K, Q6_K); launch_gemv uses it for
 // the batches and types that gemv_mfma_supported accepts.
 bool gemv_mfma_supported(int type, int batch);
+// np problems of one type and k sharing x [batch, k] on the matrix cores, one
+// launch for up to eight of them (k <= 4096; gemv_mfma_multi_supported).
+bool gemv_mfma_multi_supported(int type, int batch, int64_t k);
+hipError_t launch_gemv_mfma_multi(int type, int np, const void *const *w, const int64_t *n, int64_t k, size_t rb,
+                                  const float *x, int batch, float *const *y, hipStream_t s);
 hipError_t launch_gemv_mfma(int type, const void *w, int64_t n, int64_t k, size_t rb, const float *x, int batch,
                             float *y, hipStream_t s);
 

@@ -483,14 +483,18 @@ def test_gemv_multi_matches_single_calls(t, k, ns, batch):
                                     (G.Q4_K, 4096, [4096, 1024, 1024]), (G.Q4_K, 4096, [14336, 14336]),
                                     (G.Q6_K, 4096, [1024, 3, 0, 700]), (G.Q8_0, 1984, [37] * 9),
                                     (G.Q5_0, 2048, [4100, 7]), (G.Q5_K, 3840, [0, 515, 1]),
-                                    (G.Q4_K, 4096, [700, 0]), (G.Q4_0, 2048, [37] * 7 + [0])])
-def test_gemv_multi_shared_x_matches_single_calls(t, k, ns):
+                                    (G.Q4_K, 4096, [700, 0]), (G.Q4_0, 2048, [37] * 7 + [0]),
+                                    (G.Q6_K, 4096, [16384, 16390])])
+@pytest.mark.parametrize("batch", [1, 3, 8])
+def test_gemv_multi_shared_x_matches_single_calls(t, k, ns, batch):
     """A grouped call whose problems all read one x (q / k / v, gate / up)
-    stages x once per workgroup; results stay bit-identical to one qmm_gemv
-    call per problem, and each matches the oracle."""
-    say("gemv_multi shared x", G.NAMES[t], k, ns)
+    stages x once per workgroup (at batch 3..8 of the K-quants: one
+    matrix-core launch over the tiles of every problem, a workgroup's tiles
+    crossing from one problem into the next); results stay bit-identical to
+    one qmm_gemv call per problem, and each matches the oracle."""
+    say("gemv_multi shared x", G.NAMES[t], k, ns, batch)
     ws = [G.gen_weights(t, n, k, seed=800 + i) for i, n in enumerate(ns)]
-    x = G.gen_x(k, 1, seed=900)
+    x = G.gen_x(k, batch, seed=900)
     wd = [upload(w) for w in ws]
     xd = upload(x)
     ys = q.gemv_multi(wd, t, ns, k, [xd] * len(ns))
