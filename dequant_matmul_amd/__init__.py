@@ -59,6 +59,10 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError("libqmm.so not built: run `python dequant_matmul_amd/build.py` "
                           "(expected at %s)" % LIB_PATH)
+    # torch first: it loads its own copy of the HIP runtime by path, and this
+    # library must bind to that copy (loaded first, the library would pull in
+    # a second runtime whose streams and graphs are not torch's)
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         f = getattr(L, name)
