@@ -547,7 +547,7 @@ gemv_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float
 {
     using F = Fmt<T>;
     constexpr int UE = GemvUnit<T>::UE;
-    using S = SegStage<T, R>;
+    using S = SegStage<T, R, false>;
     constexpr int SEGE = S::SEGE, SEGB = S::SEGB;
     constexpr int XS = SEGE + (SEGE / UE) * 4;    // padded floats per batch
     __shared__ __attribute__((aligned(16))) float xs[B * XS];
