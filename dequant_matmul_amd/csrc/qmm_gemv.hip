@@ -145,12 +145,12 @@ struct TableProbs {
 // a caller whose waves work on different column ranges of one row passes the
 // whole x (xsrc, xn floats, at most XMAX) and this wave's offset xoff into
 // the padded LDS copy.
-template <int T, int R, class PS, int NW = 4, bool X_LDS = false, int WSTRIDE = 0, int XMAX = 0>
+template <int T, int R, class PS, int NW = 4, bool X_LDS = false, int WSTRIDE = 0, int XMAX = 0, bool NT = true>
 __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint32_t *ws, float *xl, int gw, int tw,
                                            const float *xsrc = nullptr, int xn = 0, int xoff = 0)
 {
     constexpr int UE = GemvUnit<T>::UE, NRUN = GemvUnit<T>::NRUN;
-    using S = SegStage<T, R>;
+    using S = SegStage<T, R, NT>;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -338,7 +338,7 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
 
 // Batch 1, one problem, x staged in LDS, NW wavefronts per workgroup (one
 // workgroup per CU: 16 waves, 4 per SIMD, hide the weight latency).
-template <int T, int R, int NW>
+template <int T, int R, int NW, bool NT>
 __global__ void __launch_bounds__(64 * NW)
 gemv3_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
              float *__restrict__ y)
@@ -347,7 +347,7 @@ gemv3_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
     __shared__ __attribute__((aligned(16))) uint32_t ws[NW * SegStage<T, R>::LDS_DW];
     const OneProb P{w, x, y, n};
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    gemv2_body<T, R, OneProb, NW, true>(P, k, rb, ws, xl, blockIdx.x * NW + wave, gridDim.x * NW);
+    gemv2_body<T, R, OneProb, NW, true, 0, 0, NT>(P, k, rb, ws, xl, blockIdx.x * NW + wave, gridDim.x * NW);
 }
 
 template <int T, int R>
@@ -421,7 +421,7 @@ __global__ void __launch_bounds__(64 * NW) gemv3s_kernel(const StageGroups G, in
 constexpr int GEMV4_XMAX = 16384;  // the longest x the kernel stages in LDS
 constexpr int GEMV4_PART = 4096;   // LDS floats for the partial sums (nseg * rwg)
 
-template <int T, int NW>
+template <int T, int NW, bool NT>
 __global__ void __launch_bounds__(64 * NW)
 gemv4_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
              float *__restrict__ y, int rwg, int nseg)
@@ -441,7 +441,7 @@ gemv4_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
     // too) and takes its segment's slice from LDS
     const int kseg = min(S::SEGE, k - seg * S::SEGE);
     const OneProb P{w + (int64_t)row0 * rb + (int64_t)seg * S::SEGB, x, part + seg * rwg, sub < wps ? nr : 0};
-    gemv2_body<T, 1, OneProb, NW, true, 0, XMAX>(P, kseg, rb, ws, xl, sub < wps ? sub : 0, wps, x, k,
+    gemv2_body<T, 1, OneProb, NW, true, 0, XMAX, NT>(P, kseg, rb, ws, xl, sub < wps ? sub : 0, wps, x, k,
                                                     xpad<UE>(seg * S::SEGE));
     __syncthreads();
     for (int t = threadIdx.x; t < nr; t += 64 * NW) {
@@ -457,14 +457,14 @@ gemv4_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const floa
 // each wave walks items (R rows x one segment) with the weight bytes of the
 // next D items in flight (a ring of D register stages, so a row's segments
 // are fetched together rather than one round trip after another).
-template <int T, int R, int NW, int XK, int D>
+template <int T, int R, int NW, int XK, int D, bool NT>
 __global__ void __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 4)))
 gemv1_kernel(const uint8_t *__restrict__ w, int n, int k, int64_t rb, const float *__restrict__ x,
              float *__restrict__ y)
 {
     using F = Fmt<T>;
     constexpr int UE = GemvUnit<T>::UE;
-    using S = SegStage<T, R>;
+    using S = SegStage<T, R, NT>;
     constexpr int SEGE = S::SEGE;
     constexpr int XS = XK + (XK / UE) * 4;
     constexpr int XV = XK / (4 * 64 * NW);          // 4-float vectors per thread for x
@@ -656,6 +656,13 @@ static int gemv2_cap(K kernel)
     return res < 2 * cus ? res : 2 * cus;
 }
 
+// Matrices of at least this many bytes stream their weights with
+// non-temporal loads; smaller single launches are faster with plain ones
+// (Q8_0 2048 x 2048, 4.5 MB, over rotating copies: 2.92 us plain, 3.35 us
+// non-temporal), and the decode passes faster with non-temporal loads from
+// the 4096 x 4096 Q4_K projection (9.4 MB) up.
+constexpr int64_t NT_MIN_BYTES = 8 << 20;
+
 // Batch 1 through gemv3 (x staged in LDS, 8 waves per workgroup): at most
 // one workgroup per CU, each wave a contiguous run of rows.
 template <int T, int R, int NW>
@@ -667,7 +674,10 @@ static hipError_t launch_b1_xlds(const uint8_t *w, int64_t n, int64_t k, size_t 
         return hipErrorInvalidValue;
     const int64_t want = ((n + R - 1) / R + NW - 1) / NW;
     const dim3 grid((unsigned)(want < cus ? want : cus)), block(64 * NW);
-    hipLaunchKernelGGL((gemv3_kernel<T, R, NW>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
+    if (n * (int64_t)rb >= NT_MIN_BYTES)
+        hipLaunchKernelGGL((gemv3_kernel<T, R, NW, true>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
+    else
+        hipLaunchKernelGGL((gemv3_kernel<T, R, NW, false>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
     return hipGetLastError();
 }
 
@@ -788,18 +798,27 @@ hipError_t launch_gemv_stage(int ng, const int *type, const int *np, const void 
     return rows >= 4096 ? launch_stage_t<32, 16>(G, bytes, rows, k, s) : launch_stage_t<32, 8>(G, bytes, rows, k, s);
 }
 
-template <int T, int R, int NW, int XK, int D>
-static hipError_t launch_b1_lds(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
-                                hipStream_t s)
+template <int T, int R, int NW, int XK, int D, bool NT>
+static hipError_t launch_b1_lds_nt(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
+                                   hipStream_t s)
 {
     static std::atomic<int> slot[64];
-    const int cap = per_device_cached(slot, [] { return resident_wgs(gemv1_kernel<T, R, NW, XK, D>, 64 * NW); });
+    const int cap = per_device_cached(slot, [] { return resident_wgs(gemv1_kernel<T, R, NW, XK, D, NT>, 64 * NW); });
     if (cap == 0)
         return hipErrorInvalidValue;
     const int64_t want = ((n + R - 1) / R + NW - 1) / NW;
     const dim3 grid((unsigned)(want < cap ? want : cap)), block(64 * NW);
-    hipLaunchKernelGGL((gemv1_kernel<T, R, NW, XK, D>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
+    hipLaunchKernelGGL((gemv1_kernel<T, R, NW, XK, D, NT>), grid, block, 0, s, w, (int)n, (int)k, (int64_t)rb, x, y);
     return hipGetLastError();
+}
+
+template <int T, int R, int NW, int XK, int D>
+static hipError_t launch_b1_lds(const uint8_t *w, int64_t n, int64_t k, size_t rb, const float *x, float *y,
+                                hipStream_t s)
+{
+    if (n * (int64_t)rb >= NT_MIN_BYTES)
+        return launch_b1_lds_nt<T, R, NW, XK, D, true>(w, n, k, rb, x, y, s);
+    return launch_b1_lds_nt<T, R, NW, XK, D, false>(w, n, k, rb, x, y, s);
 }
 
 template <int T, int NW>
@@ -813,8 +832,12 @@ static hipError_t launch_b1_split(const uint8_t *w, int64_t n, int64_t k, size_t
     const int64_t cap = GEMV4_PART / nseg;
     rwg = rwg < cap ? rwg : cap;
     const int64_t grid = (n + rwg - 1) / rwg;
-    hipLaunchKernelGGL((gemv4_kernel<T, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, w, (int)n, (int)k,
-                       (int64_t)rb, x, y, (int)rwg, nseg);
+    if (n * (int64_t)rb >= NT_MIN_BYTES)
+        hipLaunchKernelGGL((gemv4_kernel<T, NW, true>), dim3((unsigned)grid), dim3(64 * NW), 0, s, w, (int)n,
+                           (int)k, (int64_t)rb, x, y, (int)rwg, nseg);
+    else
+        hipLaunchKernelGGL((gemv4_kernel<T, NW, false>), dim3((unsigned)grid), dim3(64 * NW), 0, s, w, (int)n,
+                           (int)k, (int64_t)rb, x, y, (int)rwg, nseg);
     return hipGetLastError();
 }
 
