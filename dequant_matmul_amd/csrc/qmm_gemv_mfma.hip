@@ -226,23 +226,6 @@ __device__ __forceinline__ void keep(const WRawB<T> &r)
 
 __device__ __forceinline__ h2 h2c(float v) { return (h2){(_Float16)v, (_Float16)v}; }
 
-// A value hidden from the optimizer without a scheduling barrier (no
-// volatile): keeps the two halves of a packed fp16 pair in one register, so
-// that each half is formed by v_fma_mixlo_f16 / v_fma_mixhi_f16 and read in
-// place (op_sel) by the next v_fma_mix.  No instruction is written in asm:
-// the hazard recognizer sees every VALU write that an MFMA reads.
-__device__ __forceinline__ uint32_t hide(uint32_t v)
-{
-    asm("" : "+v"(v));
-    return v;
-}
-
-__device__ __forceinline__ _Float16 hide_h(_Float16 v)
-{
-    asm("" : "+v"(v));
-    return v;
-}
-
 // One super-block of one 16-row tile: 8 (+1) MFMAs and the fp32 scaling into
 // acc0 / acc1 (batch rows 2g, 2g+1 of weight row n of the tile).
 template <int T>
@@ -275,9 +258,6 @@ __device__ __forceinline__ void sb_dot<T_Q4_K>(const WRawB<T_Q4_K> &r, const XFr
 #pragma unroll
     for (int t = 0; t < 8; ++t)
         D8[t] = D[t] >> 8;
-    // a zero the optimizer cannot see: W 2^-11 + z stays a fused convert
-    // (v_fma_mixlo_f16) instead of a multiply and a separate convert
-    const float z = __builtin_bit_cast(float, hide(0u));
     fl4 ch = {0.f, 0.f, 0.f, 0.f}, cl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -291,12 +271,14 @@ __device__ __forceinline__ void sb_dot<T_Q4_K>(const WRawB<T_Q4_K> &r, const XFr
             const uint32_t v = (pr & 1) ? D8[t0 + (pr >> 1)] : D[t0 + (pr >> 1)];
             const h2 e = as_h2(opaque(v & msk));
             // W (v_fma_mix_f32 reads the fp16 code), hi = fp16(2^s w) and
-            // lo = fp16(W - 2^11 hi), the remainder times 2^11
+            // lo = fp16(W - 2^11 hi), the remainder times 2^11 (exact in
+            // fp32, one rounding).  Full-rate operations only: the fused
+            // converts v_fma_mixlo/mixhi_f16 issue at about half the rate of
+            // an fma on this chip, v_cvt_pk_f16_f32 at the full rate.
             const float W0 = fmaf((float)e[0], dsc, ndm), W1 = fmaf((float)e[1], dsc, ndm);
-            oh[pr] = hide(as_u((h2){(_Float16)fmaf(W0, 0x1p-11f, z), (_Float16)fmaf(W1, 0x1p-11f, z)}));
+            oh[pr] = pk_rne(W0 * 0x1p-11f, W1 * 0x1p-11f);
             const h2 h = as_h2(oh[pr]);
-            const _Float16 l0 = hide_h((_Float16)fmaf((float)h[0], -2048.f, W0));
-            ol[pr] = as_u((h2){l0, (_Float16)fmaf((float)h[1], -2048.f, W1)});
+            ol[pr] = pk_rne(fmaf((float)h[0], -2048.f, W0), fmaf((float)h[1], -2048.f, W1));
         }
         ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(f.a[i], __builtin_bit_cast(h8, (u32x4){oh[0], oh[1], oh[2], oh[3]}),
                                                     ch, 0, 0, 0);
@@ -686,14 +668,18 @@ __device__ __forceinline__ void staged_run_q6k(const MProbs &P, const float *__r
     };
     Slot ring[D];
     // chunk c of tile t: bytes 16 c of its 16 rows; past its problem's
-    // matrix the last chunk of that matrix (rows past n are never stored)
+    // matrix the last chunk of that matrix (rows past n are never stored).
+    // Whole lines, each read once: non-temporal loads (128256 x 4096 at
+    // batch 4 / 8: 114 / 116 -> 111 / 113 us; the per-lane field loads of
+    // the other paths share lines between instructions and are 15% slower
+    // with them)
     auto load_tile = [&](Slot &sl, int t) {
         const TileRef R = tile_ref(P, t_begin + min(t, t_count - 1));
         const int64_t base = (int64_t)R.row0 * ST_RB, last = (int64_t)R.n * ST_RB - 16;
 #pragma unroll
         for (int i = 0; i < ST_CPT; ++i) {
             const int c = min(tid + 64 * GB_W * i, ST_CH - 1);
-            sl.v[i] = *(const u32x4 *)(R.w + min(base + 16 * c, last));
+            sl.v[i] = __builtin_nontemporal_load((const u32x4 *)(R.w + min(base + 16 * c, last)));
         }
     };
 #pragma unroll
