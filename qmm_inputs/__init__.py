@@ -112,7 +112,9 @@ def gen_weights(qtype: int, n: int, k: int, seed: int, d_range=None) -> np.ndarr
         blk[:, :, 0:2] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
         blk[:, :, 2:4] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
     elif qtype == Q6_K:
-        # ql, qh uniform (q ~ U{0..63}); scale bytes uniform: int8 ~ U{-128..127}
+        # ql, qh uniform (q ~ U{0..63}); scale = (uniform byte & 127) - 64 ~ U{-64..63}
+        sc = (blk[:, :, 192:208] & 0x7F).astype(np.int16) - 64
+        blk[:, :, 192:208] = sc.astype(np.int8).view(np.uint8)
         blk[:, :, 208:210] = _f16_bytes(rng.uniform(lo, hi, size=(n, nb)))
     else:
         raise ValueError("unknown type %r" % (qtype,))

@@ -46,7 +46,7 @@ def test_field_ranges(t, lo, hi):
     else:
         assert q.min() == 0 and q.max() == 63
         sc = np.concatenate([f["sc"] for f in fs])
-        assert sc.min() == -128 and sc.max() == 127
+        assert sc.min() == -64 and sc.max() == 63
     if t in (G.Q4_K, G.Q5_K):
         dmin = np.array([_h(f["dmin"]) for f in fs])
         assert dmin.min() >= np.float16(lo) * (1 - 2 ** -10) and dmin.max() <= np.float16(hi) * (1 + 2 ** -10)
