@@ -367,18 +367,18 @@ __device__ __forceinline__ void run_piece(const uint8_t *__restrict__ w, int64_t
     };
     WRawB<T> A0, A1, B0, B1;
     if (convert) {
-        // activations first: the wait for them then leaves the weight loads
-        // below in flight (loads complete in order)
-        fl4 v[16];
+        // activations of both super-blocks first: the waits for them then
+        // leave the weight loads below in flight (loads complete in order)
+        fl4 v[16], v2[16];
         load_x<T>(xrow + 256 * sa, g, v);
+        if (TWO)
+            load_x<T>(xrow + 256 * (sa + 1), g, v2);
         load_b<T>(w, off(0, sa), g, A0);
         if (TWO)
             load_b<T>(w, off(0, sa + 1), g, A1);
         convert_x<T>(v, xf[0]);
-        if (TWO) {
-            load_x<T>(xrow + 256 * (sa + 1), g, v);
-            convert_x<T>(v, xf[1]);
-        }
+        if (TWO)
+            convert_x<T>(v2, xf[1]);
     } else {
         load_b<T>(w, off(0, sa), g, A0);
         if (TWO)
