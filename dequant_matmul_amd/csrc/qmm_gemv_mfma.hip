@@ -99,58 +99,69 @@ struct XFrag {
     float xs1;
 };
 
+// Element offset of the q-th group of 4 activations of lane group G in a
+// 256-element block (the k order above).
 template <int T>
-__device__ __forceinline__ void load_x(const float *__restrict__ xb, int G, fl4 v[16])
+__device__ __forceinline__ int xgroup_off(int G, int q)
 {
-    if (T == T_Q4_K) {
-        const fl4 *p = (const fl4 *)(xb + 64 * G);
-#pragma unroll
-        for (int q = 0; q < 16; ++q)
-            v[q] = p[q];
-    } else {
-        const float *p = xb + 128 * (G >> 1) + 16 * (G & 1);
-#pragma unroll
-        for (int gp = 0; gp < 4; ++gp)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                v[4 * gp + q] = *(const fl4 *)(p + 32 * gp + 4 * q);
-    }
+    return T == T_Q4_K ? 64 * G + 4 * q : 128 * (G >> 1) + 16 * (G & 1) + 32 * (q >> 2) + 4 * (q & 3);
 }
 
-__device__ __forceinline__ float vget(const fl4 v[16], int j) { return v[j >> 2][j & 3]; }
-
+// The two lanes of a batch row (rows 2b and 2b+1 of A, lanes l and l ^ 1)
+// split its 64 activations of a block: fragment i takes groups 2i and 2i+1,
+// and the lane of parity p loads group 2i + p.
 template <int T>
-__device__ __forceinline__ void convert_x(fl4 v[16], XFrag &f)
+__device__ __forceinline__ void load_x(const float *__restrict__ xb, int G, fl4 v[8])
 {
-    const int lane = threadIdx.x & 63, r = lane & 15, G = lane >> 4;
+    const int p = threadIdx.x & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = *(const fl4 *)(xb + xgroup_off<T>(G, 2 * i + p));
+}
+
+// The partner lane's value of v (lanes l and l ^ 1 swap, DPP quad_perm 1,0,3,2).
+__device__ __forceinline__ uint32_t swap_pair(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
+}
+
+// A fragments of one block from this lane's half of its row's activations.
+// Row 2b keeps hi = fp16(x 2^sh), row 2b+1 the fp16 of the remainder times
+// 2^11 (exact in fp32, at most 16 in magnitude).  Each lane forms hi and lo
+// of its own groups and takes the other half of its fragment from the
+// partner lane: 22 instead of 32 operations per fragment.
+template <int T>
+__device__ __forceinline__ void convert_x(fl4 v[8], XFrag &f)
+{
+    const int lane = threadIdx.x & 63, G = lane >> 4;
+    const bool odd = (lane & 1) != 0;
     float m = 0.f;
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
+    for (int q = 0; q < 8; ++q)
         m = fmaxf(fmaxf(m, fmaxf(fabsf(v[q][0]), fabsf(v[q][1]))), fmaxf(fabsf(v[q][2]), fabsf(v[q][3])));
+    m = fmaxf(m, __builtin_bit_cast(float, swap_pair(__builtin_bit_cast(uint32_t, m))));
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     // m in [2^(e-1), 2^e): scale the block so that it lands in [2^14, 2^15)
     const int e = __builtin_amdgcn_frexp_expf(m);
     const int sh = min(max(15 - e, -128), 126);
-#pragma unroll
-    for (int q = 0; q < 16; ++q)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-            v[q][c] = __builtin_amdgcn_ldexpf(v[q][c], sh);
-    // row 2b keeps the fp16 value, row 2b+1 the fp16 of the remainder times
-    // 2^11 (the remainder is exact in fp32, at most 16 in magnitude)
-    const float pm = (r & 1) ? 1.f : 0.f, ps = (r & 1) ? 2048.f : 1.f;
+    // -1 the optimizer cannot see: a + (-1) hi stays one v_fma_mix_f32 that
+    // reads hi in place (not a convert and a subtract)
+    const float n1 = __builtin_bit_cast(float, opaque(0xbf800000u));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        uint32_t o[4];
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-            const int j0 = 8 * i + (pr & 1) + 4 * (pr >> 1), j1 = j0 + 2;
-            const float a = vget(v, j0), b = vget(v, j1);
-            const h2 h = as_h2(pk_rne(a, b));
-            o[pr] = pk_rne(fmaf(-pm, (float)h[0], a) * ps, fmaf(-pm, (float)h[1], b) * ps);
-        }
-        f.a[i] = __builtin_bit_cast(h8, (u32x4){o[0], o[1], o[2], o[3]});
+        const float a0 = __builtin_amdgcn_ldexpf(v[i][0], sh), a1 = __builtin_amdgcn_ldexpf(v[i][1], sh);
+        const float a2 = __builtin_amdgcn_ldexpf(v[i][2], sh), a3 = __builtin_amdgcn_ldexpf(v[i][3], sh);
+        // element pairs (0, 2) and (1, 3) of the group
+        const uint32_t H0 = pk_rne(a0, a2), H1 = pk_rne(a1, a3);
+        const h2 h0 = as_h2(H0), h1 = as_h2(H1);
+        const uint32_t L0 = pk_rne(fmaf(n1, (float)h0[0], a0) * 2048.f, fmaf(n1, (float)h0[1], a2) * 2048.f);
+        const uint32_t L1 = pk_rne(fmaf(n1, (float)h1[0], a1) * 2048.f, fmaf(n1, (float)h1[1], a3) * 2048.f);
+        // the partner needs lo of an even lane's group, hi of an odd lane's
+        const uint32_t R0 = swap_pair(odd ? H0 : L0), R1 = swap_pair(odd ? H1 : L1);
+        // even lane (hi row): own group first; odd lane (lo row): own second
+        const uint32_t o0 = odd ? R0 : H0, o1 = odd ? R1 : H1, o2 = odd ? L0 : R0, o3 = odd ? L1 : R1;
+        f.a[i] = __builtin_bit_cast(h8, (u32x4){o0, o1, o2, o3});
     }
     const float xs = __builtin_amdgcn_ldexpf(1.f, -sh);
     f.xs0 = __shfl(xs, 4 * G);        // row 4G   = batch 2G
@@ -369,7 +380,7 @@ __device__ __forceinline__ void run_piece(const uint8_t *__restrict__ w, int64_t
     if (convert) {
         // activations of both super-blocks first: the waits for them then
         // leave the weight loads below in flight (loads complete in order)
-        fl4 v[16], v2[16];
+        fl4 v[8], v2[8];
         load_x<T>(xrow + 256 * sa, g, v);
         if (TWO)
             load_x<T>(xrow + 256 * (sa + 1), g, v2);
@@ -577,7 +588,7 @@ __device__ __forceinline__ void single_run(const MProbs &P, int k, int64_t rb, c
         const int r = lane & 15, b = min(r >> 1, batch - 1);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            fl4 v[16];
+            fl4 v[8];
             load_x<T>(xs[c][b], g, v);   // b: this lane's row (min(r/2, batch - 1))
             convert_x<T>(v, xf[c]);
         }
@@ -693,7 +704,7 @@ __device__ __forceinline__ void staged_run_q6k(const MProbs &P, const float *__r
         const int r = lane & 15, b = min(r >> 1, batch - 1);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            fl4 v[16];
+            fl4 v[8];
             load_x<T>(xs[c][b], g, v);
             convert_x<T>(v, xf[c]);
         }
