@@ -457,12 +457,11 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const uint32_t a = raw[r].qa[i], bq = raw[r].qb[i], hx = raw[r].qh[i] ^ 0xaaaaaaaau;
-                    uint32_t q;
-                    if (g == 0) q = ((a << 2) & 0x3c3c3c3cu) | ((hx << 6) & 0xc0c0c0c0u);
-                    else if (g == 1) q = ((bq << 2) & 0x3c3c3c3cu) | ((hx << 4) & 0xc0c0c0c0u);
-                    else if (g == 2) q = ((a >> 2) & 0x3c3c3c3cu) | ((hx << 2) & 0xc0c0c0c0u);
-                    else q = ((bq >> 2) & 0x3c3c3c3cu) | (hx & 0xc0c0c0c0u);
-                    q = opaque(q);
+                    // high bits at 6..7 alone (zeros elsewhere), then one
+                    // v_and_or_b32 with the shifted nibbles
+                    const uint32_t hb = opaque((hx << (6 - 2 * g)) & 0xc0c0c0c0u);
+                    const uint32_t lo = g == 0 ? a << 2 : g == 1 ? bq << 2 : g == 2 ? a >> 2 : bq >> 2;
+                    const uint32_t q = opaque((lo & 0x3c3c3c3cu) | hb);
 #pragma unroll
                     for (int b = 0; b < B; ++b) s[r][b][g] = dot4_s(q, xv[b], s[r][b][g]);
                 }
