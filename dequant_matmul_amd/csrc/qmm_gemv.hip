@@ -309,8 +309,13 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     S st;
     auto load = [&](int it) __attribute__((always_inline)) {
         const int row0 = locate(cl, it);
-        // past the wave's last item: no row is in range, every chunk reads offset 0
-        st.load(cl.w, rb, it < nit ? cl.n : 0, row0, 0, cpr, lane);
+        if constexpr (R == 1 && NT) {
+            // past the wave's last item: an empty range, every chunk reads zero
+            st.load_row(cl.w + (int64_t)row0 * rb, it < nit ? (uint32_t)(16 * cpr) : 0u, lane);
+        } else {
+            // past the wave's last item: no row is in range, every chunk reads offset 0
+            st.load(cl.w, rb, it < nit ? cl.n : 0, row0, 0, cpr, lane);
+        }
     };
     load(0);
     if constexpr (X_LDS) {
