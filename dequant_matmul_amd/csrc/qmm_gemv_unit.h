@@ -440,13 +440,15 @@ __device__ __forceinline__ void unit_dot(const URaw<T> (&raw)[R], int u, const X
             dsc[r][2] = d * (float)(int8_t)(raw[r].sc[1] >> sh);          // scale 8h + 4 + hf
             dsc[r][3] = d * (float)(int8_t)(raw[r].sc[1] >> (16 + sh));   // scale 8h + 6 + hf
         }
-        AccT s[R][B][4];
+        // one scalar chain per (row, batch, group): the four groups already
+        // give four independent chains of 16 fmas per unit
+        float s[R][B][4];
 #pragma unroll
         for (int b = 0; b < B; ++b)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
 #pragma unroll
-                for (int r = 0; r < R; ++r) s[r][b][g] = zero_acc<AccT>();
+                for (int r = 0; r < R; ++r) s[r][b][g] = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
