@@ -130,6 +130,22 @@ def test_gemv_workload_shapes(t, n, k, batch):
     say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "gemv %s %dx%d" % (G.NAMES[t], n, k)))
 
 
+@pytest.mark.parametrize("t,n,k", [(G.Q8_0, 4099, 2048), (G.Q4_0, 7433, 2048), (G.Q5_0, 6007, 2048),
+                                   (G.Q4_K, 3641, 4096), (G.Q5_K, 2981, 4096), (G.Q6_K, 2501, 4096),
+                                   (G.Q6_K, 1001, 10240)])
+def test_gemv_batch1_large_ragged(t, n, k):
+    """Batch 1 just past 8 MiB of weights (the non-temporal loads through a
+    buffer resource per row), odd row counts (waves with one item fewer
+    than others), and a Q6_K row of 40 super-blocks on the split-k kernel."""
+    assert n * G.row_bytes(t, k) >= 8 << 20
+    say("gemv large ragged", G.NAMES[t], n, k)
+    w = G.gen_weights(t, n, k, seed=61)
+    x = G.gen_x(k, 1, seed=62)
+    ref, absum = oracle.gemv(t, w, n, k, x)
+    got = q.gemv(upload(w), t, n, k, upload(x)).cpu().numpy()
+    say("  worst relative error", check_tol(got, ref, absum, GEMV_TOL, "gemv %s %dx%d" % (G.NAMES[t], n, k)))
+
+
 @pytest.mark.parametrize("t", TYPES)
 def test_gemv_and_gemm_wide_k(t):
     """k past the widest x staging of the batch-1 kernels (16384), with a
