@@ -84,14 +84,11 @@ struct GemvProbs {
 };
 
 // A mixed-type launch (gemv3s): up to STAGE_MAXG groups, each a table of
-// problems of one block type; group g owns wave slots [wb[g], wb[g + 1]).
+// problems of one block type.  The groups' block types and wave-slot ranges
+// travel as plain kernel arguments (preloaded into SGPRs), the tables here.
 constexpr int STAGE_MAXG = 3;
 struct StageGroups {
     GemvProbs P[STAGE_MAXG];
-    int64_t rb[STAGE_MAXG];
-    int type[STAGE_MAXG];
-    int wb[STAGE_MAXG + 1];
-    int ng;
 };
 
 // Problem sources: one problem passed as plain kernel arguments (held in
@@ -111,14 +108,37 @@ struct OneProb {
     __device__ __forceinline__ float *Y(int) const { return y; }
     __device__ __forceinline__ int N(int) const { return n; }
 };
+// The table's row-group starts are read at constant indices, so that the
+// reads are one batch of independent scalar loads (a loop bounded by np, or
+// an index read from the table, chains one load round trip after another
+// ahead of the first weight load).  The problem of a row group is the number
+// of starts (past the first) at or below it: the starts never decrease.
 struct TableProbs {
     const GemvProbs &P;
-    __device__ __forceinline__ int total_rg(int) const { return P.rg0[P.np]; }
+    __device__ __forceinline__ int total_rg(int) const
+    {
+        int r[GEMV_MAXP + 1];
+#pragma unroll
+        for (int q = 0; q <= GEMV_MAXP; ++q)
+            r[q] = P.rg0[q];
+        const int np = P.np;
+        int t = 0;
+#pragma unroll
+        for (int q = 1; q <= GEMV_MAXP; ++q)
+            t = q == np ? r[q] : t;
+        return t;
+    }
     __device__ __forceinline__ int find(int rg) const
     {
+        int r[GEMV_MAXP];
+#pragma unroll
+        for (int q = 0; q < GEMV_MAXP; ++q)
+            r[q] = P.rg0[q];
+        const int np = P.np;
         int pp = 0;
-        for (int q = 1; q < P.np; ++q)
-            if (rg >= P.rg0[q]) pp = q;
+#pragma unroll
+        for (int q = 1; q < GEMV_MAXP; ++q)
+            pp += (int)(q < np) & (int)(rg >= r[q]);
         return pp;
     }
     __device__ __forceinline__ int rg_begin(int pp) const { return P.rg0[pp]; }
@@ -127,6 +147,11 @@ struct TableProbs {
     __device__ __forceinline__ const float *X(int pp) const { return P.x[pp]; }
     __device__ __forceinline__ float *Y(int pp) const { return P.y[pp]; }
     __device__ __forceinline__ int N(int pp) const { return P.n[pp]; }
+};
+// A table whose problems all read one x, passed as a kernel argument.
+struct SharedXProbs : TableProbs {
+    const float *xs;
+    __device__ __forceinline__ const float *X(int) const { return xs; }
 };
 
 // NW wavefronts per workgroup.  xl (X_LDS): the workgroup first copies the
@@ -219,12 +244,8 @@ __device__ __forceinline__ void gemv2_body(const PS &P, int k, int64_t rb, uint3
     };
     auto locate = [&](Cur &c, int it) __attribute__((always_inline)) {
         const int rg = item_rg(it);
-        if (rg >= c.end) {
-            int pp = c.pp + 1;
-            while (rg >= P.rg_end(pp, R))
-                ++pp;
-            cur_set(c, pp);
-        }
+        if (rg >= c.end)
+            cur_set(c, P.find(rg));
         return (rg - c.beg) * R;   // first row of the item in its problem
     };
     Cur cl, cs;                    // the load and the compute cursors
@@ -387,30 +408,43 @@ gemv3m_kernel(const GemvProbs Pt, int k, int64_t rb)
 // the groups in proportion to their weight bytes, numbered wave-major
 // (slot = wave * grid + workgroup) so that every workgroup holds waves of
 // every group, and each wave runs its group's table loop.
+// Group g owns the wave slots [wb_g, wb_{g+1}) with wb_0 = 0, wb_1 = wb1,
+// wb_2 = wb2 and wb_3 = all slots (a launch of fewer groups passes all slots
+// for the missing boundaries); its block type is bits 4g..4g+3 of types.
+// grid is gridDim.x, passed as an argument: the argument arrives in an SGPR,
+// while gridDim.x is a read of the dispatch's implicit arguments.
+template <int T, class PS, int NW, int WSDW>
+__device__ __forceinline__ void stage_body(const PS &P, int k, uint32_t *ws, float *xl, int gw, int tw)
+{
+    const int64_t rb = (int64_t)(k / Fmt<T>::BE) * Fmt<T>::BB;
+    gemv2_body<T, 1, PS, NW, true, WSDW>(P, k, rb, ws, xl, gw, tw);
+}
+
 template <int UEK, int NW>
-__global__ void __launch_bounds__(64 * NW) gemv3s_kernel(const StageGroups G, int k)
+__global__ void __launch_bounds__(64 * NW)
+gemv3s_kernel(const float *__restrict__ x, int k, int grid, int wb1, int wb2, int types, const StageGroups G)
 {
     constexpr int WSDW = UEK == 64 ? SegStage<T_Q6_K, 1>::LDS_DW : SegStage<T_Q8_0, 1>::LDS_DW;
     __shared__ __attribute__((aligned(16))) float xl[64 * (UEK + 4)];
     __shared__ __attribute__((aligned(16))) uint32_t ws[NW * WSDW];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slot = wave * (int)gridDim.x + (int)blockIdx.x;
-    int g = 0;
-    while (g + 1 < G.ng && slot >= G.wb[g + 1])
-        ++g;
-    const int gw = slot - G.wb[g], tw = G.wb[g + 1] - G.wb[g];
-    const TableProbs P{G.P[g]};
+    const int slot = wave * grid + (int)blockIdx.x;
+    const int g = (slot >= wb1 ? 1 : 0) + (slot >= wb2 ? 1 : 0);
+    const int lo = g == 0 ? 0 : g == 1 ? wb1 : wb2;
+    const int hi = g == 0 ? wb1 : g == 1 ? wb2 : grid * NW;
+    const int gw = slot - lo, tw = hi - lo;
+    const SharedXProbs P{{G.P[g]}, x};
     if constexpr (UEK == 64) {
-        switch (G.type[g]) {
-        case T_Q4_K: gemv2_body<T_Q4_K, 1, TableProbs, NW, true, WSDW>(P, k, G.rb[g], ws, xl, gw, tw); break;
-        case T_Q6_K: gemv2_body<T_Q6_K, 1, TableProbs, NW, true, WSDW>(P, k, G.rb[g], ws, xl, gw, tw); break;
-        default: gemv2_body<T_Q5_K, 1, TableProbs, NW, true, WSDW>(P, k, G.rb[g], ws, xl, gw, tw); break;
+        switch ((types >> (4 * g)) & 15) {
+        case T_Q4_K: stage_body<T_Q4_K, SharedXProbs, NW, WSDW>(P, k, ws, xl, gw, tw); break;
+        case T_Q6_K: stage_body<T_Q6_K, SharedXProbs, NW, WSDW>(P, k, ws, xl, gw, tw); break;
+        default: stage_body<T_Q5_K, SharedXProbs, NW, WSDW>(P, k, ws, xl, gw, tw); break;
         }
     } else {
-        switch (G.type[g]) {
-        case T_Q4_0: gemv2_body<T_Q4_0, 1, TableProbs, NW, true, WSDW>(P, k, G.rb[g], ws, xl, gw, tw); break;
-        case T_Q8_0: gemv2_body<T_Q8_0, 1, TableProbs, NW, true, WSDW>(P, k, G.rb[g], ws, xl, gw, tw); break;
-        default: gemv2_body<T_Q5_0, 1, TableProbs, NW, true, WSDW>(P, k, G.rb[g], ws, xl, gw, tw); break;
+        switch ((types >> (4 * g)) & 15) {
+        case T_Q4_0: stage_body<T_Q4_0, SharedXProbs, NW, WSDW>(P, k, ws, xl, gw, tw); break;
+        case T_Q8_0: stage_body<T_Q8_0, SharedXProbs, NW, WSDW>(P, k, ws, xl, gw, tw); break;
+        default: stage_body<T_Q5_0, SharedXProbs, NW, WSDW>(P, k, ws, xl, gw, tw); break;
         }
     }
 }
@@ -717,7 +751,8 @@ static hipError_t launch_b1_table_xlds(const GemvProbs &P, int64_t k, size_t rb,
 }
 
 template <int UEK, int NW>
-static hipError_t launch_stage_t(StageGroups &G, const int64_t *bytes, int64_t rows, int64_t k, hipStream_t s)
+static hipError_t launch_stage_t(const StageGroups &G, int ng, const int *type, const int64_t *bytes, int64_t rows,
+                                 int64_t k, const float *x, hipStream_t s)
 {
     const int cus = device_cu_count();
     if (cus == 0)
@@ -728,10 +763,10 @@ static hipError_t launch_stage_t(StageGroups &G, const int64_t *bytes, int64_t r
     // and at most one per row for each group
     const int tot = grid * NW;
     int64_t btot = 0;
-    for (int g = 0; g < G.ng; ++g)
+    for (int g = 0; g < ng; ++g)
         btot += bytes[g];
     int cnt[STAGE_MAXG], used = 0;
-    for (int g = 0; g < G.ng; ++g) {
+    for (int g = 0; g < ng; ++g) {
         const int64_t r = G.P[g].rg0[G.P[g].np];
         int64_t c = btot > 0 ? (tot * bytes[g] + btot / 2) / btot : 1;
         c = c < 1 ? 1 : c > r ? r : c;
@@ -741,7 +776,7 @@ static hipError_t launch_stage_t(StageGroups &G, const int64_t *bytes, int64_t r
     // fix the sum: surplus slots go to (or are taken from) the largest groups
     while (used != tot) {
         int best = -1;
-        for (int g = 0; g < G.ng; ++g) {
+        for (int g = 0; g < ng; ++g) {
             const int64_t r = G.P[g].rg0[G.P[g].np];
             const bool can = used < tot ? cnt[g] < r : cnt[g] > 1;
             if (can && (best < 0 || bytes[g] > bytes[best]))
@@ -752,13 +787,15 @@ static hipError_t launch_stage_t(StageGroups &G, const int64_t *bytes, int64_t r
         cnt[best] += used < tot ? 1 : -1;
         used += used < tot ? 1 : -1;
     }
-    G.wb[0] = 0;
-    for (int g = 0; g < G.ng; ++g)
-        G.wb[g + 1] = G.wb[g] + cnt[g];
-    // slots past the last group (when every group is capped at its rows)
-    // fall into the last group and find no row there
-    G.wb[G.ng] = tot > G.wb[G.ng] ? tot : G.wb[G.ng];
-    hipLaunchKernelGGL((gemv3s_kernel<UEK, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, G, (int)k);
+    // group boundaries; slots past the last group (when every group is
+    // capped at its rows) fall into the last group and find no row there
+    int wb[STAGE_MAXG] = {0, tot, tot}, types = 0;
+    for (int g = 0; g < ng; ++g)
+        types |= type[g] << (4 * g);
+    for (int g = 1; g < ng; ++g)
+        wb[g] = wb[g - 1] + cnt[g - 1];
+    hipLaunchKernelGGL((gemv3s_kernel<UEK, NW>), dim3((unsigned)grid), dim3(64 * NW), 0, s, x, (int)k, grid, wb[1],
+                       wb[2], types, G);
     return hipGetLastError();
 }
 
@@ -766,7 +803,6 @@ hipError_t launch_gemv_stage(int ng, const int *type, const int *np, const void 
                              int64_t k, const float *x, float *const *y, hipStream_t s)
 {
     StageGroups G{};
-    G.ng = ng;
     int64_t bytes[STAGE_MAXG] = {0, 0, 0};
     int64_t rows = 0;
     int i = 0;
@@ -776,8 +812,7 @@ hipError_t launch_gemv_stage(int ng, const int *type, const int *np, const void 
         const int be = (t == T_Q4_K || t == T_Q6_K || t == T_Q5_K) ? 256 : 32;
         const int bb = t == T_Q4_0 ? 18 : t == T_Q8_0 ? 34 : t == T_Q4_K ? 144 : t == T_Q6_K ? 210 : t == T_Q5_0 ? 22 : 176;
         ue = be == 256 ? 64 : 32;
-        G.type[g] = t;
-        G.rb[g] = k / be * bb;
+        const int64_t rb = k / be * bb;
         GemvProbs &P = G.P[g];
         P.np = np[g];
         P.rg0[0] = 0;
@@ -791,16 +826,17 @@ hipError_t launch_gemv_stage(int ng, const int *type, const int *np, const void 
             // blocks read back from LDS with realignment): they get 1.4x
             // their byte share of the waves (q|k|v of the Q4_K_M-style mix:
             // 8.2 -> 7.9 us; 0.6x / 2x / 3x: 9.0 / 8.2 / 8.5 us)
-            bytes[g] += n[i] * G.rb[g] * (t == T_Q6_K ? 14 : 10) / 10;
+            bytes[g] += n[i] * rb * (t == T_Q6_K ? 14 : 10) / 10;
         }
         rows += P.rg0[P.np];
     }
     if (rows == 0)
         return hipSuccess;
     if (ue == 64)
-        return launch_stage_t<64, 8>(G, bytes, rows, k, s);
+        return launch_stage_t<64, 8>(G, ng, type, bytes, rows, k, x, s);
     // 16 waves per compute unit for the 32-element types with many rows (as gemv3)
-    return rows >= 4096 ? launch_stage_t<32, 16>(G, bytes, rows, k, s) : launch_stage_t<32, 8>(G, bytes, rows, k, s);
+    return rows >= 4096 ? launch_stage_t<32, 16>(G, ng, type, bytes, rows, k, x, s)
+                        : launch_stage_t<32, 8>(G, ng, type, bytes, rows, k, x, s);
 }
 
 template <int T, int R, int NW, int XK, int D, bool NT>

@@ -518,12 +518,22 @@ struct TileRef {
     int n, row0;             // the problem's rows, the tile's first row in it
 };
 
-// Tile ti's problem (wave-uniform: a short scalar scan of the table).
+// Tile ti's problem (wave-uniform): the number of problem starts past the
+// first at or below ti (the starts never decrease).  The starts are read at
+// constant indices, so that they are loaded once, ahead of the tile loop, as
+// independent scalar loads; the problem's fields are then one round of loads
+// (a scan bounded by np would chain one load round trip per problem).
 __device__ __forceinline__ TileRef tile_ref(const MProbs &P, int ti)
 {
+    int t0[MP_MAX];
+#pragma unroll
+    for (int q = 0; q < MP_MAX; ++q)
+        t0[q] = P.tile0[q];
+    const int np = P.np;
     int p = 0;
-    while (p + 1 < P.np && ti >= P.tile0[p + 1])
-        ++p;
+#pragma unroll
+    for (int q = 1; q < MP_MAX; ++q)
+        p += (int)(q < np) & (int)(ti >= t0[q]);
     return TileRef{P.w[p], P.y[p], P.n[p], (ti - P.tile0[p]) * 16};
 }
 
@@ -748,7 +758,7 @@ __device__ __forceinline__ void staged_run_q6k(const MProbs &P, const float *__r
 
 template <int T>
 __global__ void __launch_bounds__(64 * GB_W)
-gemvb1_kernel(const MProbs P, int k, int64_t rb, const float *__restrict__ x, int batch)
+gemvb1_kernel(const float *__restrict__ x, int k, int64_t rb, int batch, int ntiles, int grid, const MProbs P)
 {
     constexpr int DM = RingDepth<T>::D;
     // activation staging; for staged Q6_K tiles also the two tile buffers
@@ -761,8 +771,10 @@ gemvb1_kernel(const MProbs P, int k, int64_t rb, const float *__restrict__ x, in
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int S = k / 256;
     const int sa = wave * S / GB_W, ns = (wave + 1) * S / GB_W - sa;   // 0, 1 or 2 super-blocks
-    const int ntiles = P.tile0[P.np];
-    const int per = ntiles / (int)gridDim.x, rem = ntiles - per * (int)gridDim.x;
+    // ntiles (all tiles of the table) and grid (gridDim.x) arrive as plain
+    // arguments, preloaded into SGPRs, not read from the table or the
+    // dispatch's implicit arguments
+    const int per = ntiles / grid, rem = ntiles - per * grid;
     const int t_begin = (int)blockIdx.x * per + min((int)blockIdx.x, rem);
     const int t_count = per + ((int)blockIdx.x < rem ? 1 : 0);
 
@@ -838,7 +850,8 @@ hipError_t launch_b(const uint8_t *w, int64_t n, int64_t k, size_t rb, const flo
         P.n[0] = (int)n;
         P.tile0[1] = (int)ntiles;
         P.np = 1;
-        hipLaunchKernelGGL(gemvb1_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, P, (int)k, (int64_t)rb, x, batch);
+        hipLaunchKernelGGL(gemvb1_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, x, (int)k, (int64_t)rb, batch,
+                           (int)ntiles, grid, P);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(gemvb_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, w, (int)n, (int)k, (int64_t)rb, x,
@@ -869,7 +882,8 @@ hipError_t launch_b_multi(int np, const void *const *w, const int64_t *n, int64_
         P.np = c;
         const int ntiles = P.tile0[c];
         const int grid = ntiles < cu_count_cached() ? ntiles : cu_count_cached();
-        hipLaunchKernelGGL(gemvb1_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, P, (int)k, (int64_t)rb, x, batch);
+        hipLaunchKernelGGL(gemvb1_kernel<T>, dim3(grid), dim3(64 * GB_W), 0, s, x, (int)k, (int64_t)rb, batch,
+                           ntiles, grid, P);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
