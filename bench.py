@@ -55,7 +55,7 @@ FP16_PEAK_TFLOPS = 2500.0
 # Taken with gemv3s_kernel<64, 8> over the 64 launches of one pass (256
 # dispatches): FETCH_SIZE 20001.9 KiB x 2.0 + WRITE_SIZE 114.7 KiB x 1.0 per
 # launch (profiles/gemv3s_stage_decode_pass_q4_k_m_mix.md).
-TRAFFIC = {"sources_sha16": "e052548421fe71b2", "bytes_per_launch": 41081437}
+TRAFFIC = {"sources_sha16": "b2ddcd09ae50d430", "bytes_per_launch": 41128074}
 TRAFFIC_SOURCES = ("dequant_matmul_amd/csrc/qmm_gemv.hip", "dequant_matmul_amd/csrc/qmm_gemv_unit.h",
                    "dequant_matmul_amd/csrc/qmm_device.h")
 SECONDARIES = ("q8_0", "tinyllama", "q4_k", "prefill", "mix_batch", "q5", "embed", "kv", "dequant")
