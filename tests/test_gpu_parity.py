@@ -500,7 +500,10 @@ def test_gemv_multi_matches_single_calls(t, k, ns, batch):
                                     (G.Q6_K, 4096, [1024, 3, 0, 700]), (G.Q8_0, 1984, [37] * 9),
                                     (G.Q5_0, 2048, [4100, 7]), (G.Q5_K, 3840, [0, 515, 1]),
                                     (G.Q4_K, 4096, [700, 0]), (G.Q4_0, 2048, [37] * 7 + [0]),
-                                    (G.Q6_K, 4096, [16384, 16390])])
+                                    (G.Q6_K, 4096, [16384, 16390]),
+                                    # eight problems (a full table), ragged and tiny ones among them
+                                    (G.Q4_K, 4096, [1, 17, 300, 2, 16, 15, 33, 1000]),
+                                    (G.Q6_K, 4096, [5, 40, 1, 16, 700, 2, 31, 64])])
 @pytest.mark.parametrize("batch", [1, 3, 8])
 def test_gemv_multi_shared_x_matches_single_calls(t, k, ns, batch):
     """A grouped call whose problems all read one x (q / k / v, gate / up)

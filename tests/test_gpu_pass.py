@@ -215,3 +215,27 @@ def test_pass_stage_launch_matches_single_calls():
     for (w, t, n, k_, xx, y, st) in probs:
         single = q.gemv(w, t, n, k, x.view(1, -1)).view(-1)
         assert torch.equal(y, single), G.NAMES[t]
+
+
+def test_pass_stage_group_edges():
+    """Stage launches at the edges of their wave-slot split: a group of the
+    full eight problems with one- and three-row problems between large ones,
+    a group of two rows (fewer rows than its byte share of the slots, so it
+    is capped and the slots past the groups fall into the last group), and
+    a one-row problem last; the same for the 32-element types.  Each output
+    is checked against the oracle and against one qmm_gemv call of its own
+    (same decode and summation order, so the same bits)."""
+    spec = []
+    k_groups = [(G.Q4_K, [1, 3, 700, 5, 2048, 17, 1, 900]), (G.Q6_K, [2]), (G.Q5_K, [1000, 1])]
+    e_groups = [(G.Q8_0, [1]), (G.Q4_0, [5000, 3]), (G.Q5_0, [64, 7])]
+    for st, (k, src, groups) in enumerate([(4096, "h4", k_groups), (2048, "h2", e_groups)]):
+        for t, ns in groups:
+            for j, n in enumerate(ns):
+                spec.append(("%s_%d_%d" % (G.NAMES[t], st, j), t, n, k, src, st))
+    net = Net(spec, {"h4": G.gen_x(4096, 1, seed=21)[0], "h2": G.gen_x(2048, 1, seed=22)[0]}, seed=300)
+    say("pass stage group edges", len(spec), "GEMVs")
+    net.run()
+    net.verify("stage edges")
+    for (nm, t, n, k, src, st) in spec:
+        single = q.gemv(net.w[nm], t, n, k, net.x[src].view(1, -1)).view(-1)
+        assert torch.equal(net.y[nm], single), nm
