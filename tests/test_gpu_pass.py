@@ -239,3 +239,17 @@ def test_pass_stage_group_edges():
     for (nm, t, n, k, src, st) in spec:
         single = q.gemv(net.w[nm], t, n, k, net.x[src].view(1, -1)).view(-1)
         assert torch.equal(net.y[nm], single), nm
+
+
+def test_pass_full_layer_llama3_8b_mix():
+    """One decoder layer of the Q4_K_M-style mix at the Llama-3-8B shapes the
+    benchmark pass runs (hidden 4096, ffn 14336, k/v 1024 rows; v and down
+    Q6_K, the rest Q4_K), chained stage to stage through qmm_gemv_pass (so
+    the stage launches have the benchmark's grids and slot splits), plus a
+    ragged 2999-row Q6_K head; every output against the oracle."""
+    types = (G.Q4_K, G.Q4_K, G.Q6_K, G.Q4_K, G.Q4_K, G.Q4_K, G.Q6_K, G.Q6_K)
+    spec = decoder_spec(1, 4096, 14336, 1024, 2999, types)
+    net = Net(spec, {"h": G.gen_x(4096, 1, seed=41)[0]}, seed=400)
+    say("pass full layer", len(spec), "GEMVs")
+    net.run()
+    net.verify("full layer")
